@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the fine-grained block-scaled E4M3 GEMM hot path on one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+1x128 activation quantization, 128x128 weight quantization and the
+block-scaled GEMM (dense, contiguous-grouped or masked-grouped by workload).
+Inputs are generated and moved to HBM before timing starts; outputs are
+preallocated.  Prints ONE JSON line.
+
+Default workload: dense prefill GEMM M=4096, N=7168, K=7168 (N(0,1) inputs,
+0.1% of entries x100).  The other configurations are parity workloads that
+can also be timed with --config.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "TFLOPS (and GB/s) of block-scaled FP8 GEMM; % of MI355X FP8 MFMA/HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    """Hash of the HIP sources: counters taken for other sources are stale."""
+    csrc = os.path.join(ROOT, "fine_grained_block_e4m3_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_counts(wl):
+    """Valid FLOPs and algorithmic bytes (A + sA + B + sB + Y, valid rows only,
+    every weight byte once) of one GEMM launch."""
+    import numpy as np
+    K, N = wl.K, wl.N
+    KB = K // 128
+    if wl.kind == "dense":
+        rows = wl.M
+        w_rows = N
+        n_sb = ((N + 127) // 128) * KB
+    elif wl.kind == "contiguous":
+        counts = np.bincount(wl.m_indices[wl.m_indices >= 0], minlength=wl.E)
+        rows = int(counts.sum())
+        used = int((counts > 0).sum())
+        w_rows = used * N
+        n_sb = used * (N // 128) * KB
+    else:
+        valid = np.clip(wl.masked_m, 0, wl.max_m)
+        rows = int(valid.sum())
+        used = int((valid > 0).sum())
+        w_rows = used * N
+        n_sb = used * (N // 128) * KB
+    flops = 2.0 * rows * N * K
+    nbytes = rows * K + 4 * rows * KB + w_rows * K + 4 * n_sb + 2 * rows * N
+    return flops, float(nbytes), rows
+
+
+def load_traffic(key: str, sha: str):
+    """HBM bytes per GEMM launch from committed rocprofv3 PMC counters, or None
+    when they were taken for other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = data.get(key)
+    if not e or e.get("source_sha") != sha:
+        return None
+    return float(e["hbm_bytes_per_dispatch"])
+
+
+def cpu_baseline(wl, target_s: float):
+    """Time the CPU oracle on a bounded sample of the same workload: the first
+    Ms rows of X and first Ns rows of W, quantized and multiplied."""
+    import numpy as np
+    import oracle
+    K = wl.K
+    flags = oracle.FLAG_UE8M0 if wl.ue8m0 else 0
+
+    def run(ms, ns):
+        x = np.ascontiguousarray(wl.x[:ms])
+        w = np.ascontiguousarray(wl.w[:ns])
+        t0 = time.perf_counter()
+        xq, sa = oracle.quant_1x128(x, flags)
+        wq, sb = oracle.quant_128x128(w, flags)
+        oracle.gemm_nt(xq, sa, wq, sb, flags)
+        return time.perf_counter() - t0
+
+    ms, ns = 16, 128
+    t = run(ms, ns)
+    scale = max(1.0, target_s / max(t, 1e-6))
+    # grow rows first (cheap quantization), then columns in whole 128-blocks
+    ms_max = min(wl.M, 4096)
+    ms2 = int(min(ms_max, max(16, ms * scale)))
+    scale2 = scale * ms / ms2
+    ns2 = int(min(wl.w.shape[0], max(128, (ns * scale2) // 128 * 128)))
+    log(f"cpu baseline: calibration {ms}x{ns} took {t:.2f}s; sample {ms2}x{ns2}x{K}")
+    t2 = run(ms2, ns2)
+    flops = 2.0 * ms2 * ns2 * K
+    return {
+        "value": flops / t2 / 1e12,
+        "unit": "TFLOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{wl.name}: X rows [0,{ms2}) and W rows [0,{ns2}), K={K}: oracle "
+                  f"quant_1x128 + quant_128x128 + gemm_nt ({flops:.3g} FLOP) in {t2:.2f} s",
+        "seconds": t2,
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); the multi-GPU path is not built", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fine_grained_block_e4m3_amd as fp8
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fp8.load_library()
+
+    log(f"generating workload {args.config}: {workloads.CONFIG_NAMES[args.config]}")
+    wl = workloads.config(args.config)
+    ue8m0 = wl.ue8m0
+    x = torch.from_numpy(wl.x).to(dev)
+    w = torch.from_numpy(wl.w).to(dev)
+    M, K = wl.x.shape
+    NW = wl.w.shape[0]
+    xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+    wq = torch.empty((NW, K), dtype=torch.uint8, device=dev)
+    sb = torch.empty(((NW + 127) // 128, K // 128), dtype=torch.float32, device=dev)
+    if wl.kind == "dense":
+        y = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
+
+        def gemm():
+            fp8.gemm_nt(xq, sa, wq, sb, ue8m0=ue8m0, out=y)
+    elif wl.kind == "contiguous":
+        y = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
+        idx = torch.from_numpy(wl.m_indices).to(dev)
+        wq3 = wq.view(wl.E, wl.N, K)
+        sb3 = sb.view(wl.E, wl.N // 128, K // 128)
+
+        def gemm():
+            fp8.grouped_gemm_contiguous(xq, sa, wq3, sb3, idx, ue8m0=ue8m0, out=y)
+    else:
+        y = torch.empty((wl.E, wl.max_m, wl.N), dtype=torch.bfloat16, device=dev)
+        mm = torch.from_numpy(wl.masked_m).to(dev)
+        xq3 = xq.view(wl.E, wl.max_m, K)
+        wq3 = wq.view(wl.E, wl.N, K)
+        sb3 = sb.view(wl.E, wl.N // 128, K // 128)
+
+        def gemm():
+            fp8.grouped_gemm_masked(xq3, sa, wq3, sb3, mm, ue8m0=ue8m0, out=y)
+
+    names = ("quant_1x128", "quant_128x128", "gemm")
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fp8.quant_1x128(x, ue8m0=ue8m0, out=(xq, sa))
+        if ev is not None:
+            ev[1].record(stream)
+        fp8.quant_128x128(w, ue8m0=ue8m0, out=(wq, sb))
+        if ev is not None:
+            ev[2].record(stream)
+        gemm()
+        if ev is not None:
+            ev[3].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_kernel_ms = {n: float(np.mean([events[i][k].elapsed_time(events[i][k + 1])
+                                       for i in range(args.steps)]))
+                     for k, n in enumerate(names)}
+
+    flops, nbytes, rows = algorithmic_counts(wl)
+    gemm_s = per_kernel_ms["gemm"] / 1e3
+    compute_bound = wl.kind == "contiguous" or (wl.kind == "dense" and flops / nbytes > 629)
+    sha = kernel_source_sha()
+    traffic = load_traffic(f"gemm_cfg{args.config}", sha)
+    if compute_bound:
+        achieved = flops / gemm_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS, "traffic": traffic}
+    else:
+        achieved = nbytes / gemm_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
+    roof["kernel"] = "gemm"
+    roof["avg_launch_us"] = per_kernel_ms["gemm"] * 1e3
+    roof["algorithmic_flop"] = flops
+    roof["algorithmic_bytes"] = nbytes
+
+    qx_bytes = 4.0 * M * K + M * K + 4.0 * M * (K // 128)
+    qw_bytes = 4.0 * NW * K + NW * K + 4.0 * sb.numel()
+    kernels = {
+        "quant_1x128": {"avg_us": per_kernel_ms["quant_1x128"] * 1e3,
+                        "GB/s": qx_bytes / (per_kernel_ms["quant_1x128"] / 1e3) / 1e9},
+        "quant_128x128": {"avg_us": per_kernel_ms["quant_128x128"] * 1e3,
+                          "GB/s": qw_bytes / (per_kernel_ms["quant_128x128"] / 1e3) / 1e9},
+        "gemm": {"avg_us": per_kernel_ms["gemm"] * 1e3, "TFLOPS": flops / gemm_s / 1e12,
+                 "GB/s": nbytes / gemm_s / 1e9,
+                 "frac_mfma": flops / gemm_s / 1e12 / PEAK_FP8_TFLOPS,
+                 "frac_hbm": nbytes / gemm_s / 1e9 / PEAK_HBM_GBS},
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    value = flops / (ms_per_step / 1e3) / 1e12
+    cfg = {"workload": wl.name, "kind": wl.kind, "M": int(M), "N": int(wl.N), "K": int(K),
+           "valid_rows": rows, "scales": "ue8m0" if ue8m0 else "fp32",
+           "step": "quant_1x128(X) + quant_128x128(W) + block-scaled GEMM"}
+    if wl.kind != "dense":
+        cfg["experts"] = int(wl.E)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": cfg,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "gpu": torch.cuda.get_device_name(dev),
+        "kernel_source_sha": sha,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+"""Fine-grained block-scaled E4M3 GEMM for AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libfp8gemm.so`` (C ABI in ``include/fp8gemm.h``).
+Every function below only checks tensor shapes/dtypes/devices, allocates the
+outputs through torch and passes raw device pointers plus the current HIP
+stream to the library; all arithmetic runs in the library's HIP kernels.  If
+the library is not built, or no GPU is visible, calls raise -- there is no
+CPU fallback.
+
+Names follow the C ABI: ``quant_1x128``, ``quant_128x128``, ``gemm_nt``,
+``grouped_gemm_contiguous``, ``grouped_gemm_masked``,
+``get_mk_alignment_for_contiguous_layout``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8gemm.so")
+
+FLAG_UE8M0 = 1
+FLAG_PRECISE = 2
+
+STATUS = {
+    0: "FP8_OK",
+    1: "FP8_ERR_INVALID_ARG",
+    2: "FP8_ERR_SHAPE",
+    3: "FP8_ERR_ALIGNMENT",
+    4: "FP8_ERR_UNSUPPORTED",
+    5: "FP8_ERR_NO_DEVICE",
+    6: "FP8_ERR_LAUNCH",
+}
+
+# Exported C symbols (kept in step with include/fp8gemm.h by the tests).
+SYMBOLS = (
+    "fp8_quant_1x128",
+    "fp8_quant_128x128",
+    "fp8_gemm_nt",
+    "fp8_grouped_gemm_contiguous",
+    "fp8_grouped_gemm_masked",
+    "fp8_get_mk_alignment_for_contiguous_layout",
+    "fp8_status_string",
+)
+
+
+class Fp8GemmError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfp8gemm.so (no GPU needed to load it).  Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -m fine_grained_block_e4m3_amd.build` "
+            "(hipcc, gfx950). There is no CPU fallback.")
+    L = ctypes.CDLL(path)
+    P, I64, I32, U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+    L.fp8_quant_1x128.argtypes = [P, I64, I64, P, P, U32, P]
+    L.fp8_quant_128x128.argtypes = [P, I64, I64, P, P, U32, P]
+    L.fp8_gemm_nt.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
+    L.fp8_grouped_gemm_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, U32, P]
+    L.fp8_grouped_gemm_masked.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, U32, P]
+    for fn in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_gemm_nt",
+               "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked"):
+        getattr(L, fn).restype = ctypes.c_int
+    L.fp8_get_mk_alignment_for_contiguous_layout.argtypes = []
+    L.fp8_get_mk_alignment_for_contiguous_layout.restype = I32
+    L.fp8_status_string.argtypes = [ctypes.c_int]
+    L.fp8_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        msg = load_library().fp8_status_string(status).decode()
+        raise Fp8GemmError(fn, status, msg)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _flags(ue8m0: bool, precise: bool = False) -> int:
+    return (FLAG_UE8M0 if ue8m0 else 0) | (FLAG_PRECISE if precise else 0)
+
+
+def get_mk_alignment_for_contiguous_layout() -> int:
+    return int(load_library().fp8_get_mk_alignment_for_contiguous_layout())
+
+
+def quant_1x128(x: torch.Tensor, ue8m0: bool = False, out=None):
+    """x fp32 (M, K) -> (xq uint8 (M, K), sa fp32 (K/128, M))."""
+    L = load_library()
+    _need(x, "x", torch.float32, 2)
+    M, K = x.shape
+    if out is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        sa = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+    else:
+        xq, sa = out
+    _check("fp8_quant_1x128", L.fp8_quant_1x128(_ptr(x), M, K, _ptr(xq), _ptr(sa),
+                                                _flags(ue8m0), _stream(x)))
+    return xq, sa
+
+
+def quant_128x128(w: torch.Tensor, ue8m0: bool = False, out=None):
+    """w fp32 (N, K) -> (wq uint8 (N, K), sb fp32 (ceil(N/128), K/128))."""
+    L = load_library()
+    _need(w, "w", torch.float32, 2)
+    N, K = w.shape
+    if out is None:
+        wq = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+        sb = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=w.device)
+    else:
+        wq, sb = out
+    _check("fp8_quant_128x128", L.fp8_quant_128x128(_ptr(w), N, K, _ptr(wq), _ptr(sb),
+                                                    _flags(ue8m0), _stream(w)))
+    return wq, sb
+
+
+def gemm_nt(xq, sa, wq, sb, ue8m0: bool = False, precise: bool = False, out=None) -> torch.Tensor:
+    """Y (M, N) bf16 = block-scaled X * W^T."""
+    L = load_library()
+    _need(xq, "xq", torch.uint8, 2)
+    _need(wq, "wq", torch.uint8, 2)
+    _need(sa, "sa", torch.float32, 2)
+    _need(sb, "sb", torch.float32, 2)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or sa.shape != (K // 128, M) or sb.shape != ((N + 127) // 128, K // 128):
+        raise ValueError("gemm_nt: inconsistent operand shapes")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _check("fp8_gemm_nt", L.fp8_gemm_nt(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(y),
+                                        M, N, K, _flags(ue8m0, precise), _stream(xq)))
+    return y
+
+
+def grouped_gemm_contiguous(xq, sa, wq, sb, m_indices, ue8m0: bool = False, precise: bool = False,
+                            out=None) -> torch.Tensor:
+    """xq (M, K), sa (K/128, M), wq (E, N, K), sb (E, N/128, K/128), m_indices int32 (M)."""
+    L = load_library()
+    _need(xq, "xq", torch.uint8, 2)
+    _need(wq, "wq", torch.uint8, 3)
+    _need(sa, "sa", torch.float32, 2)
+    _need(sb, "sb", torch.float32, 3)
+    _need(m_indices, "m_indices", torch.int32, 1)
+    M, K = xq.shape
+    E, N, _ = wq.shape
+    if wq.shape[2] != K or sa.shape != (K // 128, M) or sb.shape != (E, N // 128, K // 128) \
+            or m_indices.shape[0] != M:
+        raise ValueError("grouped_gemm_contiguous: inconsistent operand shapes")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _check("fp8_grouped_gemm_contiguous",
+           L.fp8_grouped_gemm_contiguous(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(m_indices),
+                                         _ptr(y), M, N, K, E, _flags(ue8m0, precise), _stream(xq)))
+    return y
+
+
+def grouped_gemm_masked(xq, sa, wq, sb, masked_m, ue8m0: bool = False, precise: bool = False,
+                        out=None) -> torch.Tensor:
+    """xq (E, max_m, K), sa (K/128, E*max_m), wq (E, N, K), sb (E, N/128, K/128),
+    masked_m int32 (E).  Returns y (E, max_m, N) bf16 (rows past masked_m untouched)."""
+    L = load_library()
+    _need(xq, "xq", torch.uint8, 3)
+    _need(wq, "wq", torch.uint8, 3)
+    _need(sa, "sa", torch.float32, 2)
+    _need(sb, "sb", torch.float32, 3)
+    _need(masked_m, "masked_m", torch.int32, 1)
+    E, max_m, K = xq.shape
+    N = wq.shape[1]
+    if wq.shape != (E, N, K) or sa.shape != (K // 128, E * max_m) \
+            or sb.shape != (E, N // 128, K // 128) or masked_m.shape[0] != E:
+        raise ValueError("grouped_gemm_masked: inconsistent operand shapes")
+    y = out if out is not None else torch.empty((E, max_m, N), dtype=torch.bfloat16,
+                                                device=xq.device)
+    _check("fp8_grouped_gemm_masked",
+           L.fp8_grouped_gemm_masked(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(masked_m),
+                                     _ptr(y), E, max_m, N, K, _flags(ue8m0, precise), _stream(xq)))
+    return y

@@ -1,0 +1,220 @@
+// fp8gemm_api.hip -- host side of libfp8gemm.so: argument validation, kernel
+// instance choice and launches for the C ABI declared in include/fp8gemm.h.
+//
+// Every entry point validates on the host first and enqueues nothing on an
+// error; then it launches asynchronously on the caller's stream.  Nothing is
+// allocated, freed or synchronized here.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "../../include/fp8gemm.h"
+#include "kernels_gemm.h"
+#include "kernels_quant.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;     // rows/cols fit int32 tile math
+constexpr int kMaxDevices = 64;
+constexpr uint32_t kGemmFlags = FP8_FLAG_UE8M0 | FP8_FLAG_PRECISE;
+
+// Per-device compute-unit count, filled once per device.
+std::atomic<int> g_cu_count[kMaxDevices];
+std::once_flag g_cu_once[kMaxDevices];
+
+fp8_status current_device_cus(int* cus) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return FP8_ERR_NO_DEVICE;
+    }
+    std::call_once(g_cu_once[dev], [dev]() {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            n = 0;
+        g_cu_count[dev].store(n);
+    });
+    const int n = g_cu_count[dev].load();
+    if (n <= 0) {
+        (void)hipGetLastError();
+        return FP8_ERR_NO_DEVICE;
+    }
+    *cus = n;
+    return FP8_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+fp8_status launch_status() {
+    return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM instances.  Naming: BM x BN workgroup tile, WAVES_M x WAVES_N waves.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int MODE, int PATH>
+fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream) {
+    p.m_tiles = (int)((MODE == fp8k::kMasked ? p.max_m : p.M) + BM - 1) / BM;
+    p.n_tiles = (int)((p.N + BN - 1) / BN);
+    p.group_m = 16;
+    int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
+    if (MODE == fp8k::kMasked) tiles *= p.E;   // upper bound; the kernel counts the real ones
+    int grid = (int)(tiles < cus ? tiles : cus);
+    if (grid <= 0) return FP8_OK;
+    hipLaunchKernelGGL((fp8k::gemm_kernel<BM, BN, WM, WN, MODE, PATH>), dim3(grid),
+                       dim3(64 * WM * WN), 0, stream, p);
+    return launch_status();
+}
+
+template <int MODE, int PATH>
+fp8_status dispatch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream) {
+    if constexpr (MODE == fp8k::kDense) {
+        if (p.M <= 64) return launch_gemm<64, 96, 2, 2, MODE, PATH>(p, cus, stream);
+        const int64_t big = ((p.M + 255) / 256) * ((p.N + 127) / 128);
+        if (big >= 2 * cus) return launch_gemm<256, 128, 4, 1, MODE, PATH>(p, cus, stream);
+        return launch_gemm<128, 128, 2, 2, MODE, PATH>(p, cus, stream);
+    } else if constexpr (MODE == fp8k::kContiguous) {
+        // The M tile must equal the layout alignment (128): one expert per tile.
+        return launch_gemm<128, 256, 2, 2, MODE, PATH>(p, cus, stream);
+    } else {
+        return launch_gemm<256, 128, 4, 1, MODE, PATH>(p, cus, stream);
+    }
+}
+
+template <int MODE>
+fp8_status run_gemm(const fp8k::GemmParams& p, uint32_t flags, hipStream_t stream) {
+    int cus = 0;
+    fp8_status st = current_device_cus(&cus);
+    if (st != FP8_OK) return st;
+    const bool pow2 = flags & FP8_FLAG_UE8M0, precise = flags & FP8_FLAG_PRECISE;
+    if (precise)
+        return pow2 ? dispatch_gemm<MODE, fp8k::kPathF16Pow2>(p, cus, stream)
+                    : dispatch_gemm<MODE, fp8k::kPathF16>(p, cus, stream);
+    return pow2 ? dispatch_gemm<MODE, fp8k::kPathFp8Pow2>(p, cus, stream)
+                : dispatch_gemm<MODE, fp8k::kPathFp8>(p, cus, stream);
+}
+
+bool dims_ok(int64_t a) { return a >= 0 && a < kMaxDim; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_string(fp8_status s) {
+    switch (s) {
+        case FP8_OK: return "ok";
+        case FP8_ERR_INVALID_ARG: return "invalid argument (null pointer, bad dimension or flag)";
+        case FP8_ERR_SHAPE: return "unsupported shape (K must be a multiple of 128; grouped N too)";
+        case FP8_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+        case FP8_ERR_UNSUPPORTED: return "unsupported configuration";
+        case FP8_ERR_NO_DEVICE: return "no usable HIP device";
+        case FP8_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t fp8_get_mk_alignment_for_contiguous_layout(void) { return 128; }
+
+fp8_status fp8_quant_1x128(const float* x, int64_t M, int64_t K, uint8_t* xq, float* sa,
+                           uint32_t flags, void* stream) {
+    if (!dims_ok(M) || !dims_ok(K) || (flags & ~FP8_FLAG_UE8M0)) return FP8_ERR_INVALID_ARG;
+    if (K % 128) return FP8_ERR_SHAPE;
+    if (M == 0 || K == 0) return FP8_OK;
+    if (!x || !xq || !sa) return FP8_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(sa)) return FP8_ERR_ALIGNMENT;
+    int cus = 0;
+    fp8_status st = current_device_cus(&cus);
+    if (st != FP8_OK) return st;
+    const int64_t groups = M * (K / 128);
+    const int64_t blocks = (groups + 7) / 8;
+    if (blocks > 0x7FFFFFFF) return FP8_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    if (flags & FP8_FLAG_UE8M0)
+        hipLaunchKernelGGL(fp8k::quant_1x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s,
+                           x, xq, sa, M, K, groups);
+    else
+        hipLaunchKernelGGL(fp8k::quant_1x128_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s,
+                           x, xq, sa, M, K, groups);
+    return launch_status();
+}
+
+fp8_status fp8_quant_128x128(const float* w, int64_t N, int64_t K, uint8_t* wq, float* sb,
+                             uint32_t flags, void* stream) {
+    if (!dims_ok(N) || !dims_ok(K) || (flags & ~FP8_FLAG_UE8M0)) return FP8_ERR_INVALID_ARG;
+    if (K % 128) return FP8_ERR_SHAPE;
+    if (N == 0 || K == 0) return FP8_OK;
+    if (!w || !wq || !sb) return FP8_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(wq) || !aligned16(sb)) return FP8_ERR_ALIGNMENT;
+    int cus = 0;
+    fp8_status st = current_device_cus(&cus);
+    if (st != FP8_OK) return st;
+    const int64_t blocks = ((N + 127) / 128) * (K / 128);
+    if (blocks > 0x7FFFFFFF) return FP8_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    if (flags & FP8_FLAG_UE8M0)
+        hipLaunchKernelGGL(fp8k::quant_128x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0,
+                           s, w, wq, sb, N, K);
+    else
+        hipLaunchKernelGGL(fp8k::quant_128x128_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
+                           s, w, wq, sb, N, K);
+    return launch_status();
+}
+
+fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sb,
+                       uint16_t* y, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                       void* stream) {
+    if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K) || (flags & ~kGemmFlags))
+        return FP8_ERR_INVALID_ARG;
+    if (K % 128) return FP8_ERR_SHAPE;
+    if (M == 0 || N == 0) return FP8_OK;
+    if (K == 0) return FP8_ERR_SHAPE;
+    if (!xq || !sa || !wq || !sb || !y) return FP8_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(sa) || !aligned16(sb))
+        return FP8_ERR_ALIGNMENT;
+    fp8k::GemmParams p{};
+    p.xq = xq; p.sa = sa; p.wq = wq; p.sb = sb; p.y = y;
+    p.M = M; p.N = N; p.K = K; p.E = 1;
+    return run_gemm<fp8k::kDense>(p, flags, (hipStream_t)stream);
+}
+
+fp8_status fp8_grouped_gemm_contiguous(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                                       const float* sb, const int32_t* m_indices, uint16_t* y,
+                                       int64_t M, int64_t N, int64_t K, int32_t E,
+                                       uint32_t flags, void* stream) {
+    if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K) || E < 0 || (flags & ~kGemmFlags))
+        return FP8_ERR_INVALID_ARG;
+    if (K % 128 || N % 128) return FP8_ERR_SHAPE;
+    if (M == 0 || N == 0 || E == 0) return FP8_OK;
+    if (K == 0) return FP8_ERR_SHAPE;
+    if (!xq || !sa || !wq || !sb || !m_indices || !y) return FP8_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(sa) || !aligned16(sb) ||
+        !aligned16(m_indices))
+        return FP8_ERR_ALIGNMENT;
+    fp8k::GemmParams p{};
+    p.xq = xq; p.sa = sa; p.wq = wq; p.sb = sb; p.y = y; p.m_indices = m_indices;
+    p.M = M; p.N = N; p.K = K; p.E = E;
+    return run_gemm<fp8k::kContiguous>(p, flags, (hipStream_t)stream);
+}
+
+fp8_status fp8_grouped_gemm_masked(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                                   const float* sb, const int32_t* masked_m, uint16_t* y,
+                                   int32_t E, int64_t max_m, int64_t N, int64_t K,
+                                   uint32_t flags, void* stream) {
+    if (E < 0 || !dims_ok(max_m) || !dims_ok(N) || !dims_ok(K) ||
+        !dims_ok((int64_t)E * max_m) || (flags & ~kGemmFlags))
+        return FP8_ERR_INVALID_ARG;
+    if (K % 128 || N % 128) return FP8_ERR_SHAPE;
+    if (E == 0 || max_m == 0 || N == 0) return FP8_OK;
+    if (K == 0) return FP8_ERR_SHAPE;
+    if (!xq || !sa || !wq || !sb || !masked_m || !y) return FP8_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(sa) || !aligned16(sb) ||
+        !aligned16(masked_m))
+        return FP8_ERR_ALIGNMENT;
+    fp8k::GemmParams p{};
+    p.xq = xq; p.sa = sa; p.wq = wq; p.sb = sb; p.y = y; p.masked_m = masked_m;
+    p.M = (int64_t)E * max_m; p.N = N; p.K = K; p.E = E; p.max_m = max_m;
+    return run_gemm<fp8k::kMasked>(p, flags, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+/*
+ * fp8gemm.h -- C ABI of libfp8gemm.so: fine-grained block-scaled E4M3 GEMM
+ * (Y = X * W^T, BF16 out) and its quantizers, hand-written for AMD gfx950
+ * (MI355X, CDNA4).
+ *
+ * Sources (page title, section):
+ *   [DG]  "DeepGEMM 完全拆解：300 行 FP8 GEMM 内核，如何逼近 Hopper 的算力峰值"
+ *   [TC]  "GPU GEMM 优化完全拆解(四): tcgen05 与 Blackwell", section 六 (6.1)
+ *   [MLC] "Blackwell Tensor Core: tcgen05.mma", section "Block-Scaled MMA"
+ *
+ * Common conventions
+ *   - Every pointer argument is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees, retains or synchronizes; each call only
+ *     enqueues kernels on `stream` (a hipStream_t, NULL = the null stream) and
+ *     returns.  Outputs must not alias inputs.
+ *   - E4M3 is OCP E4M3FN (bias 7, largest finite 448, NaN = S.1111.111).
+ *     BF16 outputs are stored as raw uint16_t bit patterns, rounded to
+ *     nearest-even.
+ *   - Layouts are row-major.  The activation scale table is "MN-major":
+ *     sa[kb][m] at sa + kb*M + m, kb = k/128  ([DG] "为什么只做 NT 布局": the
+ *     (M, K/128) activation scales are handed over transposed as (K/128, M)).
+ *     The weight scale table is sb[nb][kb] at sb + nb*(K/128) + kb, nb = n/128.
+ *   - K must be a multiple of 128 (the scale granularity along K; [DG]
+ *     "线程组织": the K block is fixed at 128 because scaling is per 128
+ *     channels).
+ *   - Errors are detected on the host before anything is enqueued:
+ *       FP8_ERR_INVALID_ARG  null pointer, negative or oversized dimension,
+ *                            unknown flag bit
+ *       FP8_ERR_SHAPE        K % 128 != 0; N % 128 != 0 for grouped calls
+ *       FP8_ERR_ALIGNMENT    a pointer not 16-byte aligned
+ *       FP8_ERR_NO_DEVICE    no HIP device is usable
+ *       FP8_ERR_LAUNCH       the kernel launch reported an error
+ *     A call with an empty problem (M == 0, E == 0, N == 0 ...) returns FP8_OK
+ *     and enqueues nothing.  Device-side data (expert indices, valid counts)
+ *     is never reported as an error: its handling is defined per call.
+ *   - NaN or infinite inputs give unspecified (but in-bounds) results.
+ *   - Thread safety: all calls are reentrant; the only global state is a
+ *     per-device cache of the compute-unit count, filled once.
+ */
+#ifndef FP8GEMM_H
+#define FP8GEMM_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8_OK = 0,
+    FP8_ERR_INVALID_ARG = 1,
+    FP8_ERR_SHAPE = 2,
+    FP8_ERR_ALIGNMENT = 3,
+    FP8_ERR_UNSUPPORTED = 4,
+    FP8_ERR_NO_DEVICE = 5,
+    FP8_ERR_LAUNCH = 6
+} fp8_status;
+
+/* Quantizers: round each group's scale up to a power of two (UE8M0, [DG]
+ * "离群值如何摧毁 per-tensor 量化": Blackwell MXFP8 takes power-of-two UE8M0
+ * scales).  GEMMs: the scales are powers of two; only the biased exponent of
+ * each FP32 scale is used (value 2^(e-127)) and the block scaling runs inside
+ * the matrix instruction. */
+#define FP8_FLAG_UE8M0 1u
+
+/* GEMMs only: form every 128-K block partial from products that are exact and
+ * sums accumulated in FP32, by widening the E4M3 operands to FP16 (exact) and
+ * using FP16 matrix instructions, at half the FP8 matrix rate.  Without this
+ * flag the partials come from the FP8 matrix instruction, which on gfx950
+ * truncates, within each group of 8 consecutive products, every product to a
+ * multiple of 2^(E-13), 2^E being the group's largest product magnitude
+ * (measured: the analog of the limited FP8 accumulation precision that the
+ * DeepGEMM page, section "细粒度缩放在 GEMM 层面引爆的两个问题", reports for
+ * H800 tensor cores).  Either way the partials are promoted into FP32 every
+ * 128-K block.  With FP8_FLAG_UE8M0 and without this flag, the block scaling
+ * runs inside the scaled FP8 matrix instruction and the K sum stays in its
+ * FP32 accumulator. */
+#define FP8_FLAG_PRECISE 2u
+
+/*
+ * Activation quantizer, 1x128 groups ([DG] "离群值如何摧毁 per-tensor 量化":
+ * activations are grouped per token and per 128 channels; the scale is the
+ * group's absolute maximum over 448, computed online).
+ *   x   fp32 (M, K)           input
+ *   xq  u8   (M, K)           output codes, q = E4M3(fl32(x / s))
+ *   sa  fp32 [K/128][M]       output scales, s = fl32(max(amax, 1e-4) / 448)
+ *                             (rounded up to 2^k with FP8_FLAG_UE8M0)
+ */
+fp8_status fp8_quant_1x128(const float* x, int64_t M, int64_t K, uint8_t* xq,
+                           float* sa, uint32_t flags, void* stream);
+
+/*
+ * Weight quantizer, 128x128 blocks ([DG] same section: weights are grouped 128
+ * input by 128 output channels).  The last block row is ragged when
+ * N % 128 != 0.
+ *   w   fp32 (N, K)                 input
+ *   wq  u8   (N, K)                 output codes
+ *   sb  fp32 [ceil(N/128)][K/128]   output block scales (as for sa)
+ */
+fp8_status fp8_quant_128x128(const float* w, int64_t N, int64_t K, uint8_t* wq,
+                             float* sb, uint32_t flags, void* stream);
+
+/*
+ * Dense NT GEMM ([DG] "为什么只做 NT 布局": Y = X W^T with X (M,K) row-major and
+ * W stored (N,K) K-contiguous; [TC] 6.1 block-scaled GEMM definition;
+ * [DG] "主循环骨架": FP32 partial sums of each 128-K block are multiplied by
+ * sA*sB and added to a full-precision accumulator).
+ *   Y[m][n] = sum_kb sa[kb][m] * sb[n/128][kb] * sum_{k in kb} xq[m][k]*wq[n][k]
+ *   xq u8 (M,K), sa fp32 [K/128][M], wq u8 (N,K), sb fp32 [ceil(N/128)][K/128],
+ *   y  bf16 bits (M,N).
+ */
+fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                       const float* sb, uint16_t* y, int64_t M, int64_t N,
+                       int64_t K, uint32_t flags, void* stream);
+
+/*
+ * Grouped GEMM, contiguous layout ([DG] "分组 GEMM 的两种布局": the tokens of
+ * each expert form one segment along M, N and K are shared by all experts,
+ * each segment is aligned to the M block reported by
+ * fp8_get_mk_alignment_for_contiguous_layout()).
+ *   xq u8 (M,K), sa fp32 [K/128][M], m_indices int32 (M) on the device,
+ *   wq u8 (E,N,K), sb fp32 (E, N/128, K/128), y bf16 bits (M,N).  N % 128 == 0.
+ *   Row r uses expert m_indices[r].  Each aligned 128-row block is computed
+ *   with the expert of its first row whose index lies in [0,E); a row is
+ *   written only if its index equals that expert, every other row (padding
+ *   rows with -1, out-of-range indices, rows of another expert in the same
+ *   block) is left untouched.
+ */
+fp8_status fp8_grouped_gemm_contiguous(const uint8_t* xq, const float* sa,
+                                       const uint8_t* wq, const float* sb,
+                                       const int32_t* m_indices, uint16_t* y,
+                                       int64_t M, int64_t N, int64_t K,
+                                       int32_t E, uint32_t flags, void* stream);
+
+/*
+ * Grouped GEMM, masked layout ([DG] "分组 GEMM 的两种布局": decode with counts
+ * unknown to the host, only the valid positions are computed; [DG]
+ * "统一块调度器与 rasterization": the scheduler skips experts without work and
+ * covers only valid rows).
+ *   xq u8 (E,max_m,K), sa fp32 [K/128][E*max_m], masked_m int32 (E) on the
+ *   device, wq u8 (E,N,K), sb fp32 (E,N/128,K/128), y bf16 bits (E,max_m,N).
+ *   N % 128 == 0.  Row m of expert e is written iff m < clamp(masked_m[e], 0,
+ *   max_m); every other row of y is left untouched and rows of xq past the
+ *   count need not hold finite values.
+ */
+fp8_status fp8_grouped_gemm_masked(const uint8_t* xq, const float* sa,
+                                   const uint8_t* wq, const float* sb,
+                                   const int32_t* masked_m, uint16_t* y,
+                                   int32_t E, int64_t max_m, int64_t N,
+                                   int64_t K, uint32_t flags, void* stream);
+
+/* M alignment every expert segment of the contiguous layout must have
+ * ([DG] "分组 GEMM 的两种布局": the alignment query).  Returns 128. */
+int32_t fp8_get_mk_alignment_for_contiguous_layout(void);
+
+/* Static description of a status code (never NULL). */
+const char* fp8_status_string(fp8_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

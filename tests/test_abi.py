@@ -1,0 +1,107 @@
+"""C-ABI checks that need no GPU: the library loads, exports exactly what
+include/fp8gemm.h declares, and rejects bad arguments on the host before any
+device call (status codes as documented in the header)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fine_grained_block_e4m3_amd as fp8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8gemm.h")
+
+OK, INVALID, SHAPE, ALIGN, UNSUP, NODEV, LAUNCH = range(7)
+P = ctypes.c_void_p
+A = P(4096)           # an aligned fake device address: never dereferenced on the host
+MIS = P(4097)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fp8.LIB_PATH):
+        from fine_grained_block_e4m3_amd import build
+        build.build()
+    return fp8.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fp8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert _declared() == sorted(fp8.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), f"{name} not exported"
+
+
+def test_constants(L):
+    assert L.fp8_get_mk_alignment_for_contiguous_layout() == 128
+    for s in range(7):
+        assert L.fp8_status_string(s)
+    assert L.fp8_status_string(99) == b"unknown status"
+
+
+def _gemm(L, xq=A, sa=A, wq=A, sb=A, y=A, M=4, N=8, K=128, flags=0):
+    return L.fp8_gemm_nt(xq, sa, wq, sb, y, M, N, K, flags, None)
+
+
+def test_gemm_validation(L):
+    assert _gemm(L, xq=None) == INVALID
+    assert _gemm(L, y=None) == INVALID
+    assert _gemm(L, M=-1) == INVALID
+    assert _gemm(L, N=1 << 31) == INVALID
+    assert _gemm(L, flags=4) == INVALID
+    assert _gemm(L, K=100) == SHAPE
+    assert _gemm(L, K=0) == SHAPE
+    assert _gemm(L, xq=MIS) == ALIGN
+    assert _gemm(L, y=MIS) == ALIGN
+    # empty problems are a no-op, even with null pointers
+    assert _gemm(L, M=0, xq=None, y=None) == OK
+    assert _gemm(L, N=0) == OK
+
+
+def test_quant_validation(L):
+    assert L.fp8_quant_1x128(None, 4, 128, A, A, 0, None) == INVALID
+    assert L.fp8_quant_1x128(A, 4, 130, A, A, 0, None) == SHAPE
+    assert L.fp8_quant_1x128(MIS, 4, 128, A, A, 0, None) == ALIGN
+    assert L.fp8_quant_1x128(A, 0, 128, None, None, 0, None) == OK
+    assert L.fp8_quant_128x128(A, 4, 128, None, A, 0, None) == INVALID
+    assert L.fp8_quant_128x128(A, 4, 64, A, A, 0, None) == SHAPE
+    assert L.fp8_quant_128x128(A, 4, 128, A, A, 4, None) == INVALID
+
+
+def test_grouped_validation(L):
+    c = L.fp8_grouped_gemm_contiguous
+    assert c(A, A, A, A, A, A, 256, 128, 128, 2, 0, None) in (NODEV, OK, LAUNCH)
+    assert c(A, A, A, A, A, A, 256, 100, 128, 2, 0, None) == SHAPE     # N % 128
+    assert c(A, A, A, A, None, A, 256, 128, 128, 2, 0, None) == INVALID
+    assert c(A, A, A, A, A, A, 256, 128, 128, -1, 0, None) == INVALID
+    assert c(A, A, A, A, A, A, 256, 128, 128, 0, 0, None) == OK
+    m = L.fp8_grouped_gemm_masked
+    assert m(A, A, A, A, A, A, 4, 256, 128, 256, 0, None) in (NODEV, OK, LAUNCH)
+    assert m(A, A, A, A, A, A, 4, 256, 128, 200, 0, None) == SHAPE
+    assert m(A, A, A, A, A, A, 4, 256, 96, 256, 0, None) == SHAPE
+    assert m(A, A, A, A, None, A, 4, 256, 128, 256, 0, None) == INVALID
+    assert m(A, A, A, A, A, MIS, 4, 256, 128, 256, 0, None) == ALIGN
+    assert m(A, A, A, A, A, A, 0, 256, 128, 256, 0, None) == OK
+
+
+def test_no_device_reported_without_gpu(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert _gemm(L) == NODEV
+    assert L.fp8_quant_1x128(A, 4, 128, A, A, 0, None) == NODEV
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 128)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fp8.quant_1x128(x)

@@ -1,0 +1,190 @@
+"""GPU dense block-scaled GEMM against the oracle.
+
+Two accumulation paths are tested:
+  * PRECISE (FP8_FLAG_PRECISE): exact products, FP32 partials -- held to the
+    tolerance |y - ref| <= 8e-3 |ref| + 1e-3 rms(ref) on every input;
+  * default FP8 matrix instruction: held to that tolerance on the headline
+    workloads (every element, slow tests) and elsewhere to the tolerance or
+    the bound of the measured FP8-MFMA truncation model, whichever is larger.
+Bit-exact where the result is exactly representable (layout probes, small
+integers with power-of-two scales) on both paths.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_block_e4m3_amd as fp8
+import oracle
+import workloads
+from gpu_helpers import (assert_close, assert_close_or_bounded, bf16_bits, bf16_to_f64,
+                         check_guards, dev, fp8_mfma_error_bound, guarded, say)
+
+pytestmark = pytest.mark.gpu
+
+DEC = oracle.e4m3_decode(np.arange(256))
+PATHS = [pytest.param(False, id="fp8"), pytest.param(True, id="precise")]
+
+
+def run_gemm(xq, sa, wq, sb, ue8m0=False, precise=False, guard=2048):
+    M, K = xq.shape
+    N = wq.shape[0]
+    say(f"gemm_nt M={M} N={N} K={K} ue8m0={ue8m0} precise={precise}")
+    full, y = guarded((M, N), guard)
+    fp8.gemm_nt(dev(xq), dev(sa), dev(wq), dev(sb), ue8m0=ue8m0, precise=precise, out=y)
+    torch.cuda.synchronize()
+    check_guards(full, M * N, guard)
+    return bf16_bits(y)
+
+
+def check(y, xq, sa, wq, sb, ref, precise, ue8m0=False, what=""):
+    if precise:
+        return assert_close(y, ref, what)
+    bound = fp8_mfma_error_bound(xq, sa, wq, sb, ref, pow2=ue8m0)
+    return assert_close_or_bounded(y, ref, bound, what)
+
+
+def unit_scales(M, N, K):
+    return np.ones((K // 128, M), np.float32), np.ones(((N + 127) // 128, K // 128), np.float32)
+
+
+@pytest.mark.parametrize("precise", PATHS)
+@pytest.mark.parametrize("M,N,K", [(64, 96, 256), (200, 256, 384), (512, 1024, 256)])
+def test_layout_probe_onehot_x(M, N, K, precise):
+    """X row m is one-hot at k(m): Y[m, n] = W[n, k(m)] exactly."""
+    rng = np.random.default_rng(M + N)
+    km = (np.arange(M) * 37 + 11) % K
+    xq = np.zeros((M, K), np.uint8)
+    xq[np.arange(M), km] = 0x38          # 1.0
+    wq = workloads.random_codes(rng, (N, K))
+    sa, sb = unit_scales(M, N, K)
+    y = run_gemm(xq, sa, wq, sb, precise=precise)
+    assert np.array_equal(bf16_to_f64(y), DEC[wq][:, km].T)
+
+
+@pytest.mark.parametrize("precise", PATHS)
+@pytest.mark.parametrize("M,N,K", [(64, 96, 256), (200, 256, 384), (512, 1024, 256)])
+def test_layout_probe_onehot_w(M, N, K, precise):
+    """W row n is one-hot at k(n): Y[m, n] = X[m, k(n)] exactly."""
+    rng = np.random.default_rng(M * N)
+    kn = (np.arange(N) * 53 + 7) % K
+    wq = np.zeros((N, K), np.uint8)
+    wq[np.arange(N), kn] = 0x38
+    xq = workloads.random_codes(rng, (M, K))
+    sa, sb = unit_scales(M, N, K)
+    y = run_gemm(xq, sa, wq, sb, precise=precise)
+    assert np.array_equal(bf16_to_f64(y), DEC[xq][:, kn])
+
+
+@pytest.mark.parametrize("precise", PATHS)
+@pytest.mark.parametrize("M,N,K,ue8m0", [(64, 96, 256, False), (300, 384, 256, False),
+                                         (130, 256, 256, True), (2048, 8192, 128, False)])
+def test_exact_small_integers_pow2_scales(M, N, K, ue8m0, precise):
+    """Codes in {0, +-1}, per-row and per-block power-of-two scales constant
+    along K: every Y is 2^e times an integer of magnitude <= K = 256, exact in
+    FP32 and BF16; the GPU must match bit for bit."""
+    rng = np.random.default_rng(M + K)
+    xq = rng.choice(np.array([0x00, 0x38, 0xB8], np.uint8), (M, K))
+    wq = rng.choice(np.array([0x00, 0x38, 0xB8], np.uint8), (N, K))
+    r = workloads.random_pow2(rng, M, -3, 3)
+    c = workloads.random_pow2(rng, (N + 127) // 128, -3, 3)
+    sa = np.ascontiguousarray(np.tile(r, (K // 128, 1)))
+    sb = np.ascontiguousarray(np.tile(c[:, None], (1, K // 128)))
+    ref = oracle.gemm_nt(xq, sa, wq, sb)
+    y = run_gemm(xq, sa, wq, sb, ue8m0=ue8m0, precise=precise)
+    assert np.array_equal(bf16_to_f64(y), ref)
+
+
+@pytest.mark.parametrize("precise", PATHS)
+def test_config1_parity_and_end_to_end(precise):
+    """M=128, N=256, K=512 with 1% outliers x50: the tolerance on every element."""
+    wl = workloads.config(1)
+    xq, sa = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    ref = oracle.gemm_nt(xq, sa, wq, sb)
+    y = run_gemm(xq, sa, wq, sb, precise=precise)
+    assert_close(y, ref, "config 1")
+    say("config 1 end to end")
+    gxq, gsa = fp8.quant_1x128(dev(wl.x))
+    gwq, gsb = fp8.quant_128x128(dev(wl.w))
+    y2 = bf16_bits(fp8.gemm_nt(gxq, gsa, gwq, gsb, precise=precise))
+    assert np.array_equal(y2, y)
+
+
+@pytest.mark.parametrize("precise", PATHS)
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (63, 96, 256), (65, 224, 384), (300, 300, 256),
+                                   (257, 130, 128), (5, 50, 256), (64, 1536, 1536),
+                                   (1000, 777, 640)])
+def test_ragged_shapes(M, N, K, precise):
+    wl = workloads.dense(M, N, K, seed=M * 7 + N, outlier_frac=0.01, outlier_mult=50.0)
+    xq, sa = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    ref = oracle.gemm_nt(xq, sa, wq, sb)
+    y = run_gemm(xq, sa, wq, sb, precise=precise)
+    say(f"stats {check(y, xq, sa, wq, sb, ref, precise, what=f'{M}x{N}x{K}')}")
+
+
+@pytest.mark.parametrize("precise", PATHS)
+@pytest.mark.parametrize("M,N,K", [(96, 256, 512), (2048, 8192, 256)])
+def test_ue8m0_paths(M, N, K, precise):
+    wl = workloads.dense(M, N, K, seed=M + 3, outlier_frac=0.01, outlier_mult=50.0)
+    xq, sa = oracle.quant_1x128(wl.x, oracle.FLAG_UE8M0)
+    wq, sb = oracle.quant_128x128(wl.w, oracle.FLAG_UE8M0)
+    y = run_gemm(xq, sa, wq, sb, ue8m0=True, precise=precise)
+    if M * N <= 1 << 16:
+        ref = oracle.gemm_nt(xq, sa, wq, sb, oracle.FLAG_UE8M0)
+        say(f"stats {check(y, xq, sa, wq, sb, ref, precise, ue8m0=True, what='ue8m0')}")
+    else:
+        rng = np.random.default_rng(1)
+        mi, ni = rng.integers(0, M, 20000), rng.integers(0, N, 20000)
+        ref = oracle.gemm_nt_elems(xq, sa, wq, sb, mi, ni, oracle.FLAG_UE8M0)
+        if precise:
+            assert_close(y[mi, ni], ref, "ue8m0 sampled")
+        else:
+            full = np.zeros((M, N))
+            bound = fp8_mfma_error_bound(xq, sa, wq, sb, full, pow2=True)[mi, ni] \
+                + 2.0 ** -8 * np.abs(ref)
+            assert_close_or_bounded(y[mi, ni], ref, bound, "ue8m0 sampled")
+
+
+@pytest.mark.parametrize("precise", PATHS)
+def test_large_tile_instance_sampled(precise):
+    """A shape with >= 512 tiles of 256x128 takes the large-tile instance."""
+    M, N, K = 2048, 8192, 384
+    wl = workloads.dense(M, N, K, seed=9, outlier_frac=0.001, outlier_mult=100.0)
+    xq, sa = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    y = run_gemm(xq, sa, wq, sb, precise=precise)
+    rng = np.random.default_rng(2)
+    mi, ni = rng.integers(0, M, 30000), rng.integers(0, N, 30000)
+    mi = np.concatenate([mi, np.zeros(N, int), np.full(N, M - 1), np.arange(M), np.arange(M)])
+    ni = np.concatenate([ni, np.arange(N), np.arange(N), np.zeros(M, int), np.full(M, N - 1)])
+    ref = oracle.gemm_nt_elems(xq, sa, wq, sb, mi, ni)
+    assert_close(y[mi, ni], ref, "large tiles")
+
+
+@pytest.mark.parametrize("precise", PATHS)
+def test_deterministic_repeats(precise):
+    wl = workloads.dense(300, 512, 1024, seed=77, outlier_frac=0.01, outlier_mult=50.0)
+    xq, sa = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    a = [dev(t) for t in (xq, sa, wq, sb)]
+    say(f"determinism x10 precise={precise}")
+    first = bf16_bits(fp8.gemm_nt(*a, precise=precise))
+    for _ in range(9):
+        assert np.array_equal(bf16_bits(fp8.gemm_nt(*a, precise=precise)), first)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("precise", PATHS)
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_size_dense_configs_every_element(cfg, precise):
+    """The headline dense workloads: the tolerance on all M*N elements."""
+    wl = workloads.config(cfg)
+    say(f"config {cfg}: oracle quantization")
+    xq, sa = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    y = run_gemm(xq, sa, wq, sb, precise=precise)
+    say(f"config {cfg}: oracle GEMM ({2 * xq.shape[0] * wq.shape[0] * xq.shape[1]:.3g} FLOP)")
+    ref = oracle.gemm_nt(xq, sa, wq, sb)
+    stats = assert_close(y, ref, f"config {cfg}")
+    say(f"config {cfg} error stats: {stats}")

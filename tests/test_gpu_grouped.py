@@ -1,0 +1,177 @@
+"""GPU grouped (MoE) GEMMs against the oracle.  Row handling is bit-exact:
+every row the oracle leaves unwritten must keep its sentinel bits.  Values
+follow the same two-path rule as the dense tests (PRECISE: the tolerance
+everywhere; FP8 matrix instruction: the tolerance on the headline workloads,
+elsewhere the tolerance or the measured truncation-model bound)."""
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_block_e4m3_amd as fp8
+import oracle
+import workloads
+from gpu_helpers import (SENTINEL, assert_close, assert_close_or_bounded, bf16_bits, dev,
+                         fp8_mfma_error_bound, say, sentinel_like)
+
+pytestmark = pytest.mark.gpu
+PATHS = [pytest.param(False, id="fp8"), pytest.param(True, id="precise")]
+
+
+def quant(wl):
+    flags = oracle.FLAG_UE8M0 if wl.ue8m0 else 0
+    xq, sa = oracle.quant_1x128(wl.x, flags)
+    wq, sb = oracle.quant_128x128(wl.w, flags)
+    return xq, sa, wq, sb, flags
+
+
+def run_contiguous(xq, sa, wq, sb, idx, E, flags, precise):
+    M, K = xq.shape
+    N = wq.shape[0] // E
+    say(f"contiguous M={M} N={N} K={K} E={E} flags={flags} precise={precise}")
+    y = sentinel_like((M, N))
+    fp8.grouped_gemm_contiguous(dev(xq), dev(sa), dev(wq.reshape(E, N, K)),
+                                dev(sb.reshape(E, N // 128, K // 128)),
+                                dev(idx.astype(np.int32)), ue8m0=bool(flags), precise=precise,
+                                out=y)
+    return bf16_bits(y)
+
+
+def run_masked(xq, sa, wq, sb, mm, E, max_m, flags, precise):
+    MT, K = xq.shape
+    N = wq.shape[0] // E
+    say(f"masked E={E} max_m={max_m} N={N} K={K} counts={list(mm)} flags={flags} "
+        f"precise={precise}")
+    y = sentinel_like((E, max_m, N))
+    fp8.grouped_gemm_masked(dev(xq.reshape(E, max_m, K)), dev(sa), dev(wq.reshape(E, N, K)),
+                            dev(sb.reshape(E, N // 128, K // 128)), dev(mm.astype(np.int32)),
+                            ue8m0=bool(flags), precise=precise, out=y)
+    return bf16_bits(y).reshape(E * max_m, N)
+
+
+def grouped_bound(xq, sa, wq, sb, ref, row_expert, E, pow2):
+    """FP8-MFMA model bound, row by row with each row's own expert weights."""
+    N = wq.shape[0] // E
+    NB = N // 128
+    bound = np.zeros_like(ref)
+    for e in range(E):
+        rows = np.nonzero(row_expert == e)[0]
+        if len(rows):
+            bound[rows] = fp8_mfma_error_bound(xq[rows], np.ascontiguousarray(sa[:, rows]),
+                                               wq[e * N:(e + 1) * N], sb[e * NB:(e + 1) * NB],
+                                               ref[rows], pow2=pow2)
+    return bound
+
+
+def check_rows(y, ref, written, what, bound=None):
+    assert np.all(y[~written] == SENTINEL), f"{what}: a row outside the valid set was written"
+    if not written.any():
+        return
+    if bound is None:
+        say(f"stats {assert_close(y[written], ref[written], what)}")
+    else:
+        say(f"stats {assert_close_or_bounded(y[written], ref[written], bound[written], what)}")
+
+
+@pytest.mark.parametrize("precise", PATHS)
+@pytest.mark.parametrize("counts", [[0, 130, 1, 169], [500, 0, 0, 0], [1, 1, 1, 1],
+                                    [128, 256, 0, 7]])
+def test_contiguous_routing(counts, precise):
+    wl = workloads.contiguous(E=4, tokens=sum(counts), N=256, K=384, seed=sum(counts),
+                              counts=np.array(counts))
+    xq, sa, wq, sb, flags = quant(wl)
+    ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E)
+    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, flags, precise)
+    bound = None if precise else grouped_bound(xq, sa, wq, sb, ref,
+                                               np.where(written, wl.m_indices, -1), wl.E, False)
+    check_rows(y, ref, written, f"contiguous {counts}", bound)
+
+
+@pytest.mark.parametrize("precise", PATHS)
+def test_contiguous_dirichlet_and_bad_indices(precise):
+    wl = workloads.contiguous(E=8, tokens=1500, N=384, K=256, seed=41)
+    idx = wl.m_indices.copy()
+    # contract violations, defined as "skip": out-of-range experts and a
+    # foreign expert inside another expert's aligned block
+    idx[idx == 3] = 99
+    first5 = np.nonzero(idx == 5)[0]
+    if len(first5) > 3:
+        idx[first5[1:3]] = 6
+    xq, sa, wq, sb, flags = quant(wl)
+    ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, idx, wl.E)
+    y = run_contiguous(xq, sa, wq, sb, idx, wl.E, flags, precise)
+    bound = None if precise else grouped_bound(xq, sa, wq, sb, ref,
+                                               np.where(written, idx, -1), wl.E, False)
+    check_rows(y, ref, written, "contiguous dirichlet", bound)
+
+
+@pytest.mark.parametrize("precise", PATHS)
+def test_contiguous_ue8m0(precise):
+    wl = workloads.contiguous(E=3, tokens=400, N=256, K=256, seed=42)
+    xq, sa = oracle.quant_1x128(wl.x, oracle.FLAG_UE8M0)
+    wq, sb = oracle.quant_128x128(wl.w, oracle.FLAG_UE8M0)
+    ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E,
+                                             oracle.FLAG_UE8M0)
+    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, oracle.FLAG_UE8M0, precise)
+    bound = None if precise else grouped_bound(xq, sa, wq, sb, ref,
+                                               np.where(written, wl.m_indices, -1), wl.E, True)
+    check_rows(y, ref, written, "contiguous ue8m0", bound)
+
+
+@pytest.mark.parametrize("precise", PATHS)
+@pytest.mark.parametrize("ue8m0", [True, False])
+@pytest.mark.parametrize("max_m", [200, 256, 300])
+def test_masked_counts(ue8m0, max_m, precise):
+    mm = np.array([0, 1, 127, 128, 255, 256, -3, 999], np.int32)
+    E = len(mm)
+    wl = workloads.masked(E, max_m, 256, 384, seed=max_m, ue8m0=ue8m0, masked_m=mm)
+    xq, sa, wq, sb, flags = quant(wl)
+    ref, written = oracle.grouped_masked(xq, sa, wq, sb, mm, E, max_m, flags)
+    y = run_masked(xq, sa, wq, sb, mm, E, max_m, flags, precise)
+    bound = None
+    if not precise:
+        row_expert = np.where(written, np.arange(E * max_m) // max_m, -1)
+        bound = grouped_bound(xq, sa, wq, sb, ref, row_expert, E, ue8m0)
+    check_rows(y, ref, written, f"masked max_m={max_m}", bound)
+
+
+def test_masked_rows_past_count_never_read():
+    """Rows past the count may hold NaN codes and NaN scales: the output must
+    not change."""
+    E, max_m, N, K = 3, 256, 256, 256
+    mm = np.array([5, 0, 200], np.int32)
+    wl = workloads.masked(E, max_m, N, K, seed=3, masked_m=mm)
+    xq, sa, wq, sb, flags = quant(wl)
+    y0 = run_masked(xq, sa, wq, sb, mm, E, max_m, flags, False)
+    xq2 = xq.copy()
+    sa2 = sa.copy()
+    for e in range(E):
+        xq2[e * max_m + mm[e]:(e + 1) * max_m] = 0x7F      # NaN codes
+        sa2[:, e * max_m + mm[e]:(e + 1) * max_m] = np.nan
+    y1 = run_masked(xq2, sa2, wq, sb, mm, E, max_m, flags, False)
+    assert np.array_equal(y0, y1)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("precise", PATHS)
+def test_full_size_contiguous_config4_every_element(precise):
+    wl = workloads.config(4)
+    say("config 4: oracle quantization")
+    xq, sa, wq, sb, flags = quant(wl)
+    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, flags, precise)
+    say("config 4: oracle grouped GEMM")
+    ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E)
+    assert np.array_equal(written, wl.m_indices >= 0)
+    check_rows(y, ref, written, "config 4")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("precise", PATHS)
+def test_full_size_masked_config5_every_element(precise):
+    wl = workloads.config(5)
+    say("config 5: oracle quantization")
+    xq, sa, wq, sb, flags = quant(wl)
+    E, max_m = wl.E, wl.max_m
+    y = run_masked(xq, sa, wq, sb, wl.masked_m, E, max_m, flags, precise)
+    say("config 5: oracle grouped GEMM")
+    ref, written = oracle.grouped_masked(xq, sa, wq, sb, wl.masked_m, E, max_m, flags)
+    check_rows(y, ref, written, "config 5")
