@@ -140,6 +140,20 @@ def _cpu_model() -> str:
     return platform.processor()
 
 
+def copy_calibration(n_bytes: int = 1 << 30, reps: int = 3):
+    """Plain device-to-device copies of a known size: the FETCH_SIZE /
+    WRITE_SIZE counters of these dispatches give the scale from counter KiB to
+    HBM bytes."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes, "reps": reps}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,7 +162,12 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 1 GiB device copies (scale for HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -28,6 +28,8 @@ HIPCC_FLAGS = [
     # FP32 division must be the correctly rounded IEEE operation (quantizers)
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-fast-math",
+    # MFMA results in VGPRs: the promotion FMAs read them without v_accvgpr_read
+    # "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

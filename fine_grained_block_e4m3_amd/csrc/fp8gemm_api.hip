@@ -18,6 +18,8 @@ namespace {
 constexpr int64_t kMaxDim = (int64_t)1 << 31;     // rows/cols fit int32 tile math
 constexpr int kMaxDevices = 64;
 constexpr uint32_t kGemmFlags = FP8_FLAG_UE8M0 | FP8_FLAG_PRECISE;
+// Per-lane operand offsets inside a tile are 32-bit: 256 rows * K < 2^31.
+constexpr int64_t kMaxGemmK = (int64_t)1 << 22;
 
 // Per-device compute-unit count, filled once per device.
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -53,32 +55,35 @@ fp8_status launch_status() {
 // ---------------------------------------------------------------------------
 // GEMM instances.  Naming: BM x BN workgroup tile, WAVES_M x WAVES_N waves.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int MODE, int PATH>
+template <int BM, int BN, int WM, int WN, int MODE, int PATH, int GROUP_M = 4>
 fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream) {
     p.m_tiles = (int)((MODE == fp8k::kMasked ? p.max_m : p.M) + BM - 1) / BM;
     p.n_tiles = (int)((p.N + BN - 1) / BN);
-    p.group_m = 16;
+    p.group_m = GROUP_M;
     int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
     if (MODE == fp8k::kMasked) tiles *= p.E;   // upper bound; the kernel counts the real ones
     int grid = (int)(tiles < cus ? tiles : cus);
     if (grid <= 0) return FP8_OK;
     hipLaunchKernelGGL((fp8k::gemm_kernel<BM, BN, WM, WN, MODE, PATH>), dim3(grid),
-                       dim3(64 * WM * WN), 0, stream, p);
+                       dim3(64 * WM * WN), 0, stream, p.xq, p.sa, p.wq, p.sb, p.y, p.m_indices,
+                       p.masked_m, p);
     return launch_status();
 }
 
+// Instances.  Compute-bound shapes use 8 waves (2 per SIMD) so that one wave's
+// promotion FMAs run while the other wave's MFMAs occupy the matrix core.
 template <int MODE, int PATH>
 fp8_status dispatch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream) {
     if constexpr (MODE == fp8k::kDense) {
         if (p.M <= 64) return launch_gemm<64, 96, 2, 2, MODE, PATH>(p, cus, stream);
         const int64_t big = ((p.M + 255) / 256) * ((p.N + 127) / 128);
-        if (big >= 2 * cus) return launch_gemm<256, 128, 4, 1, MODE, PATH>(p, cus, stream);
+        if (big >= 2 * cus) return launch_gemm<256, 128, 4, 2, MODE, PATH>(p, cus, stream);
         return launch_gemm<128, 128, 2, 2, MODE, PATH>(p, cus, stream);
     } else if constexpr (MODE == fp8k::kContiguous) {
         // The M tile must equal the layout alignment (128): one expert per tile.
-        return launch_gemm<128, 256, 2, 2, MODE, PATH>(p, cus, stream);
+        return launch_gemm<128, 256, 2, 4, MODE, PATH>(p, cus, stream);
     } else {
-        return launch_gemm<256, 128, 4, 1, MODE, PATH>(p, cus, stream);
+        return launch_gemm<256, 128, 4, 2, MODE, PATH>(p, cus, stream);
     }
 }
 
@@ -167,6 +172,7 @@ fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq, co
     if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K) || (flags & ~kGemmFlags))
         return FP8_ERR_INVALID_ARG;
     if (K % 128) return FP8_ERR_SHAPE;
+    if (K > kMaxGemmK) return FP8_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return FP8_OK;
     if (K == 0) return FP8_ERR_SHAPE;
     if (!xq || !sa || !wq || !sb || !y) return FP8_ERR_INVALID_ARG;
@@ -185,6 +191,7 @@ fp8_status fp8_grouped_gemm_contiguous(const uint8_t* xq, const float* sa, const
     if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K) || E < 0 || (flags & ~kGemmFlags))
         return FP8_ERR_INVALID_ARG;
     if (K % 128 || N % 128) return FP8_ERR_SHAPE;
+    if (K > kMaxGemmK) return FP8_ERR_UNSUPPORTED;
     if (M == 0 || N == 0 || E == 0) return FP8_OK;
     if (K == 0) return FP8_ERR_SHAPE;
     if (!xq || !sa || !wq || !sb || !m_indices || !y) return FP8_ERR_INVALID_ARG;
@@ -205,6 +212,7 @@ fp8_status fp8_grouped_gemm_masked(const uint8_t* xq, const float* sa, const uin
         !dims_ok((int64_t)E * max_m) || (flags & ~kGemmFlags))
         return FP8_ERR_INVALID_ARG;
     if (K % 128 || N % 128) return FP8_ERR_SHAPE;
+    if (K > kMaxGemmK) return FP8_ERR_UNSUPPORTED;
     if (E == 0 || max_m == 0 || N == 0) return FP8_OK;
     if (K == 0) return FP8_ERR_SHAPE;
     if (!xq || !sa || !wq || !sb || !masked_m || !y) return FP8_ERR_INVALID_ARG;

@@ -22,16 +22,28 @@
 //   * FP8_FLAG_UE8M0 (power-of-two scales): the scales are fed to
 //     v_mfma_scale_f32_16x16x128_f8f6f4 as E8M0 operands and the whole K
 //     loop accumulates inside the matrix core -- no VALU promotion.
-//   * Operands reach LDS with global_load_lds_dwordx4 (no VGPR staging).
+//   * Operands reach LDS with buffer_load_dwordx4 ... lds (no VGPR staging)
+//     through per-tile buffer resources whose range ends at the last valid
+//     row: rows past it (M edge, masked rows past the count, N edge) are
+//     fetched as zeros by the hardware range check, never from memory.
 //     Each tile row is one 128-byte K block; its eight 16-byte chunks are
 //     XOR-swizzled by the row index so the fragment reads (16 rows, same
-//     chunk) hit distinct banks.  Two LDS stages: the loads of block kb+1
-//     fly while block kb is multiplied.
+//     chunk) hit distinct banks.  The activation scales of the tile's rows
+//     ride in the same stage (one direct-to-LDS dword load per wave).  A ring
+//     of STAGES buffers keeps STAGES-1 K blocks in flight; each wave waits on
+//     its own vector-memory counter for the oldest stage, then one workgroup
+//     barrier publishes it.
+//   * Per 128-K block the wave issues the MFMAs of subtile column j while the
+//     VALU promotes the partials of column j-1, so matrix core and VALU work
+//     side by side (DeepGEMM page, "主循环骨架": promotion on the CUDA cores
+//     overlaps the tensor-core work).
 //   * Persistent grid: each workgroup walks tiles with stride gridDim.x
 //     (DeepGEMM page, "线程组织": persistent launch with an in-kernel block
 //     scheduler; "统一块调度器与 rasterization": grouped raster order so tiles
 //     running together share operand rows in L2).
 #pragma once
+
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -48,14 +60,21 @@ enum GemmMode : int { kDense = 0, kContiguous = 1, kMasked = 2 };
 //   kPathF16Pow2   as kPathF16, promotion by the power-of-two part of each scale
 enum GemmPath : int { kPathFp8 = 0, kPathFp8Pow2 = 1, kPathF16 = 2, kPathF16Pow2 = 3 };
 
+// Operand pointers (passed to the kernel as separate __restrict__ arguments):
+//   xq (M, K) codes; masked: (E*max_m, K)
+//   sa [K/128][M]; masked: [K/128][E*max_m]
+//   wq (N, K); grouped: (E, N, K)
+//   sb [ceil(N/128)][K/128]; grouped: (E, N/128, K/128)
+//   y  (M, N) BF16 bits; masked: (E*max_m, N)
+//   m_indices (contiguous): expert of each row; masked_m (masked): valid rows
 struct GemmParams {
-    const uint8_t* xq;          // (M, K) codes; masked: (E*max_m, K)
-    const float* sa;            // [K/128][M]; masked: [K/128][E*max_m]
-    const uint8_t* wq;          // (N, K); grouped: (E, N, K)
-    const float* sb;            // [ceil(N/128)][K/128]; grouped: (E, N/128, K/128)
-    uint16_t* y;                // (M, N) BF16 bits; masked: (E*max_m, N)
-    const int32_t* m_indices;   // contiguous: expert of each row
-    const int32_t* masked_m;    // masked: valid rows of each expert
+    const uint8_t* xq;
+    const float* sa;
+    const uint8_t* wq;
+    const float* sb;
+    uint16_t* y;
+    const int32_t* m_indices;
+    const int32_t* masked_m;
     int64_t M;                  // rows of X (masked: E*max_m)
     int64_t N;                  // output columns (per expert)
     int64_t K;
@@ -66,8 +85,93 @@ struct GemmParams {
     int32_t group_m;            // raster group height in tiles
 };
 
-// LDS chunk swizzle: chunk c of row r lives in slot c ^ swz(r).
-__device__ __forceinline__ int lds_swz(int row) { return row & 7; }
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (gfx9 encoding: vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14;
+// expcnt and lgkmcnt left at their maxima, i.e. not waited on).
+// Workgroup barrier without a memory fence.  Each wave has already waited on
+// its own vector-memory counter for the LDS data it needs; the barrier only
+// orders the waves.  (The fence of __syncthreads() would also wait for the
+// younger prefetch stages still in flight.)  The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Raw buffer resource (V#) over [base, base + bytes), held in SGPRs: loads at
+// offsets >= bytes return zeros.  gfx9 dword3: 32-bit data format, raw
+// addressing (stride 0).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    return i32x4{uniform((int)(uint32_t)b), uniform((int)(uint32_t)(b >> 32) & 0xFFFF),
+                 uniform((int)bytes), 0x00020000};
+}
+
+// Byte address of an LDS location (the value M0 takes for an LDS DMA).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(FP8K_LDS const void*)p;
+}
+
+// Wave-wide DMAs from a buffer into LDS.  N loads of 16 bytes per lane:
+// load q writes lane l's bytes at LDS m0 + 1024*q + 16*l and reads them from
+// buffer offset voff[q] + 1024*q + soff (the instruction offset moves both
+// addresses, so callers pass voff[q] already reduced by 1024*q).  M0 is
+// restored afterwards.  The loads count on this wave's vmcnt.  They are issued
+// from asm so that the compiler does not treat them as LDS stores that may
+// alias the stage being read (it would wait for every DMA in flight).
+template <int N>
+__device__ __forceinline__ void dma_lds16(uint32_t m0, const uint32_t (&voff)[N], i32x4 rsrc, int soff) {
+    static_assert(N >= 1 && N <= 4, "1..4 loads per group");
+    int saved;
+    if constexpr (N == 1)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved) : "s"(m0), "v"(voff[0]), "s"(rsrc), "s"(soff));
+    else if constexpr (N == 2)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %2, %4, %5 offen lds\n\t"
+                     "buffer_load_dwordx4 %3, %4, %5 offen offset:1024 lds\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved) : "s"(m0), "v"(voff[0]), "v"(voff[1]), "s"(rsrc), "s"(soff));
+    else if constexpr (N == 3)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %2, %5, %6 offen lds\n\t"
+                     "buffer_load_dwordx4 %3, %5, %6 offen offset:1024 lds\n\t"
+                     "buffer_load_dwordx4 %4, %5, %6 offen offset:2048 lds\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "s"(m0), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "s"(rsrc), "s"(soff));
+    else
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %2, %6, %7 offen lds\n\t"
+                     "buffer_load_dwordx4 %3, %6, %7 offen offset:1024 lds\n\t"
+                     "buffer_load_dwordx4 %4, %6, %7 offen offset:2048 lds\n\t"
+                     "buffer_load_dwordx4 %5, %6, %7 offen offset:3072 lds\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "s"(m0), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
+                       "s"(rsrc), "s"(soff));
+}
+// One wave-wide DMA of 4 bytes per lane: lane l's dword lands at m0 + 4*l.
+__device__ __forceinline__ void dma_lds4(uint32_t m0, uint32_t voff, i32x4 rsrc, int soff) {
+    int saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dword %2, %3, %4 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff));
+}
+
+// LDS chunk swizzle: chunk c of row r lives in slot c ^ swz(r).  A fragment
+// read touches 16 consecutive rows (a 16-aligned run) at one logical chunk;
+// with swz(r) = (r mod 8) ^ ((r / 8) mod 2) those reads run at the full LDS
+// rate on gfx950 (measured; r mod 8 and (r / 2) mod 8 leave a residual
+// conflict).  Depending on r mod 16 only, it keeps every subtile of a wave at
+// a fixed offset from the first.
+__device__ __forceinline__ int lds_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // Logical tile -> (m tile, n tile) in grouped raster order: group_m m-tiles
 // are walked m-fastest for each n tile before the next group of m-tiles.
@@ -83,7 +187,10 @@ __device__ __forceinline__ void raster(int t, int m_tiles, int n_tiles, int grou
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, int PATH>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
+    const uint8_t* __restrict__ xq_, const float* __restrict__ sa_, const uint8_t* __restrict__ wq_,
+    const float* __restrict__ sb_, uint16_t* __restrict__ y_, const int32_t* __restrict__ m_indices_,
+    const int32_t* __restrict__ masked_m_, GemmParams p) {
     constexpr int NWAVES = WAVES_M * WAVES_N;
     constexpr int TM = BM / WAVES_M;   // wave tile rows (m)
     constexpr int TN = BN / WAVES_N;   // wave tile columns (n)
@@ -91,11 +198,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmPar
     constexpr int FJ = TN / 16;        // ... along n
     constexpr int XLOADS = BM / 8 / NWAVES;   // 1 KB direct-to-LDS loads per wave per stage
     constexpr int WLOADS = BN / 8 / NWAVES;
-    constexpr int STAGE = (BM + BN) * 128;
+    // LDS layout, by operand then stage: [X0][X1][W0][W1][sA0][sA1].  The
+    // operand base lives in the per-lane address and the stage offset (at most
+    // 32 KB) in the ds_read immediate.
+    constexpr int W_BASE = 2 * BM * 128;
+    constexpr int SA_BASE = W_BASE + 2 * BN * 128;   // per-wave activation-scale slices (64 floats)
+    constexpr int LDS_BYTES = SA_BASE + 2 * NWAVES * 256;
+    // A wave's 16-wide n subtiles all lie in one 128-row weight block when its
+    // n range is 128-aligned inside a 128-aligned tile: one sB per K block.
+    constexpr bool kUniformSb = (BN % 128 == 0 || 128 % BN == 0) && (128 % TN == 0 || TN % 128 == 0)
+                                && TN <= 128;
+    constexpr bool kF16 = PATH == kPathF16 || PATH == kPathF16Pow2;
+    constexpr bool kPow2 = PATH == kPathFp8Pow2 || PATH == kPathF16Pow2;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 subtiles");
+    static_assert(TM <= 64, "one scale load per wave covers at most 64 rows");
     static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "tile rows per wave");
+    static_assert(XLOADS >= 1 && XLOADS <= 4 && WLOADS >= 1 && WLOADS <= 4, "loads per wave");
+    static_assert(BM * 128 <= 65535 && BN * 128 <= 65535, "stage offsets are ds_read immediates");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+    // Two LDS stages: the loads of K block kb+1 fly while block kb is used.
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
@@ -103,13 +225,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmPar
     const int64_t K = p.K;
     const int KB = (int)(K / 128);
     const int64_t N = p.N;
+    const int g = lane >> 4;             // K group of this lane: bytes [32g, 32g+32)
 
     // Masked layout: tiles are counted per expert from the device-side counts.
     int total_tiles;
     if constexpr (MODE == kMasked) {
         int acc = 0;
         for (int e = 0; e < p.E; ++e) {
-            int v = p.masked_m[e];
+            int v = masked_m_[e];
             v = v < 0 ? 0 : (v > p.max_m ? (int)p.max_m : v);
             acc += (v + BM - 1) / BM;
         }
@@ -118,7 +241,55 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmPar
         total_tiles = p.m_tiles * p.n_tiles;
     }
 
-    for (int t = blockIdx.x; t < total_tiles; t += gridDim.x) {
+    // ---- per-lane constants, shared by every tile ----
+    // DMA: a wave load fills 1 KB = 8 rows R0..R0+7 of 8-row group grp = R0/8;
+    // lane l writes slot l%8 of row R0 + l/8, which must hold logical chunk
+    // slot ^ swz(row) = slot ^ (l/8) ^ (grp mod 2).  Source offset within the
+    // tile: (R0 + l/8)*K + 16*chunk (K is a multiple of 128, so the chunk term
+    // folds in with an XOR), reduced by 1024*q for the q-th load of a group.
+    const int rl = lane >> 3;
+    const uint32_t lane_off = (uint32_t)(rl * K) | (uint32_t)(((lane & 7) ^ rl) << 4);
+    uint32_t vx[XLOADS], vw[WLOADS];
+#pragma unroll
+    for (int q = 0; q < XLOADS; ++q) {
+        const int grp = wave * XLOADS + q;
+        vx[q] = (lane_off ^ (uint32_t)((grp & 1) << 4)) + (uint32_t)(grp * 8 * K) - 1024u * q;
+    }
+#pragma unroll
+    for (int q = 0; q < WLOADS; ++q) {
+        const int grp = wave * WLOADS + q;
+        vw[q] = (lane_off ^ (uint32_t)((grp & 1) << 4)) + (uint32_t)(grp * 8 * K) - 1024u * q;
+    }
+    const uint32_t sa_lane = (uint32_t)(4 * (wm * TM + (lane % TM)));
+    // LDS fragment addresses within a stage: row r, 16-byte chunk c at
+    // r*128 + 16*(c ^ swz(r)); this lane reads chunks 2g and 2g+1.
+    // The swizzle depends on the row mod 16 only, so subtile i of this wave
+    // sits at a fixed distance 2048*i from subtile 0: one base address per
+    // 16-byte half, the subtile and stage offsets are ds_read immediates.
+    uint32_t xa[2], wa[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = lane & 15;
+        xa[h] = (uint32_t)((wm * TM + r) * 128 + (((2 * g + h) ^ lds_swz(r)) << 4));
+        wa[h] = (uint32_t)(W_BASE + (wn * TN + r) * 128 + (((2 * g + h) ^ lds_swz(r)) << 4));
+    }
+    const uint32_t saa = (uint32_t)(SA_BASE + wave * 256 + 4 * (lane & 15));
+    const uint32_t lds0 = uniform((int)lds_addr(smem));
+
+    // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs,
+    // so workgroup b of a wave of G lands on XCD b%8.  Give each XCD a run of
+    // G/8 consecutive logical tiles (a compact raster patch sharing operand
+    // rows in that XCD's L2).
+    const int G = gridDim.x;
+    const bool remap = (G & 7) == 0;
+    const int rounds = (total_tiles + G - 1) / G;
+
+    for (int round = 0; round < rounds; ++round) {
+        int t = blockIdx.x;
+        if (remap) t = (t & 7) * (G >> 3) + (t >> 3);
+        t += round * G;
+        if (t >= total_tiles) continue;
+
         // ---------------- tile decode ----------------
         int mt, nt;
         int64_t row0;       // first X row of the tile
@@ -129,7 +300,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmPar
             nt = t - mt_t * p.n_tiles;
             int base = 0, e = 0, valid = 0;
             for (; e < p.E; ++e) {
-                valid = p.masked_m[e];
+                valid = masked_m_[e];
                 valid = valid < 0 ? 0 : (valid > p.max_m ? (int)p.max_m : valid);
                 const int nmt = (valid + BM - 1) / BM;
                 if (mt_t < base + nmt) break;
@@ -147,7 +318,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmPar
                 // expert of this aligned block: its first row naming one in [0, E)
                 int e = -1;
                 for (int r = 0; r < BM && row0 + r < p.M; ++r) {
-                    const int v = p.m_indices[row0 + r];
+                    const int v = m_indices_[row0 + r];
                     if (v >= 0 && v < p.E) { e = v; break; }
                 }
                 if (e < 0) continue;   // only padding rows: nothing to compute
@@ -155,66 +326,42 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmPar
             }
         }
         const int64_t n0 = (int64_t)nt * BN;
-        const uint8_t* __restrict__ wq = p.wq;
-        const float* __restrict__ sb = p.sb;
+        const uint8_t* wq = wq_;
+        const float* sb = sb_;
         if constexpr (MODE != kDense) {
             wq += (int64_t)expert * N * K;
             sb += (int64_t)expert * (N / 128) * KB;
         }
-        const int64_t last_row = row_end - 1;
-        const int64_t last_n = N - 1;
+        const int rows_valid = (int)min((int64_t)BM, row_end - row0);
+        const int cols_valid = (int)min((int64_t)BN, N - n0);
 
-        // ---------------- per-lane operand addresses ----------------
-        // Direct-to-LDS loads: a wave instruction fills 1 KB = 8 rows; lane l
-        // writes slot l%8 of row l/8, which holds logical chunk slot^swz(row).
-        const uint8_t* xsrc[XLOADS];
-        const uint8_t* wsrc[WLOADS];
-        {
-            const int rl = lane >> 3, slot = lane & 7;
-#pragma unroll
-            for (int q = 0; q < XLOADS; ++q) {
-                const int r = (wave * XLOADS + q) * 8 + rl;
-                int64_t gr = row0 + r;
-                gr = gr < last_row ? gr : last_row;
-                xsrc[q] = p.xq + gr * K + ((slot ^ lds_swz(r)) << 4);
-            }
-#pragma unroll
-            for (int q = 0; q < WLOADS; ++q) {
-                const int r = (wave * WLOADS + q) * 8 + rl;
-                int64_t gn = n0 + r;
-                gn = gn < last_n ? gn : last_n;
-                wsrc[q] = wq + gn * K + ((slot ^ lds_swz(r)) << 4);
-            }
-        }
-        // Activation-scale rows of this lane (one per m subtile).
-        int64_t sa_row[FI];
-#pragma unroll
-        for (int i = 0; i < FI; ++i) {
-            int64_t gr = row0 + wm * TM + 16 * i + (lane & 15);
-            sa_row[i] = gr < last_row ? gr : last_row;
-        }
+        // Buffer resources of this tile: rows past the valid range read zeros.
+        const i32x4 xr = make_rsrc(xq_ + row0 * K, (uint32_t)(rows_valid * K));
+        const i32x4 wr = make_rsrc(wq + n0 * K, (uint32_t)(cols_valid * K));
+        const float* sa_row0 = sa_ + row0;
         // Weight-scale rows (uniform per subtile).
         int sb_row[FJ];
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
-            int64_t n = n0 + wn * TN + 16 * j;
-            n = n < last_n ? n : last_n;
-            sb_row[j] = (int)(n >> 7);
+            const int64_t n = n0 + wn * TN + 16 * j;
+            sb_row[j] = uniform((int)((n < N ? n : N - 1) >> 7));
         }
 
-        auto issue_stage = [&](int kb, int buf) {
-            uint8_t* base = smem + buf * STAGE;
-            const int64_t koff = (int64_t)kb * 128;
-#pragma unroll
-            for (int q = 0; q < XLOADS; ++q)
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)(xsrc[q] + koff),
-                    (FP8K_LDS void*)(base + (wave * XLOADS + q) * 1024), 16, 0, 0);
-#pragma unroll
-            for (int q = 0; q < WLOADS; ++q)
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)(wsrc[q] + koff),
-                    (FP8K_LDS void*)(base + BM * 128 + (wave * WLOADS + q) * 1024), 16, 0, 0);
+        // Issue the loads of K block kb into stage s.  Past the last block the
+        // resources get an empty range, so the loads are discarded by the
+        // range check without a branch (the loop body stays one basic block).
+        auto issue_stage = [&](int kb, auto bufc) {
+            constexpr uint32_t s = decltype(bufc)::value;
+            const bool live = kb < KB;
+            const int koff = kb * 128;
+            i32x4 xrr = xr, wrr = wr;
+            xrr[2] = live ? xr[2] : 0;
+            wrr[2] = live ? wr[2] : 0;
+            dma_lds16<XLOADS>(lds0 + s * BM * 128 + (uint32_t)(wave * XLOADS * 1024), vx, xrr, koff);
+            dma_lds16<WLOADS>(lds0 + W_BASE + s * BN * 128 + (uint32_t)(wave * WLOADS * 1024), vw, wrr, koff);
+            const i32x4 sr = make_rsrc(sa_row0 + (int64_t)(live ? kb : 0) * p.M,
+                                       live ? (uint32_t)(4 * rows_valid) : 0u);
+            dma_lds4(lds0 + SA_BASE + s * NWAVES * 256 + (uint32_t)(wave * 256), sa_lane, sr, 0);
         };
 
         f32x4 acc[FI][FJ];
@@ -223,115 +370,154 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GemmPar
 #pragma unroll
             for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        float sa_cur[FI], sa_nxt[FI];
-        float sb_cur[FJ], sb_nxt[FJ];
-#pragma unroll
-        for (int i = 0; i < FI; ++i) sa_cur[i] = p.sa[sa_row[i]];
+        // All waves are done with the previous tile's buffers.
+        lds_barrier();
+        issue_stage(0, std::integral_constant<int, 0>{});
+        float sb_cur[FJ];
 #pragma unroll
         for (int j = 0; j < FJ; ++j) sb_cur[j] = sb[(int64_t)sb_row[j] * KB];
 
-        issue_stage(0, 0);
-        __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) lgkmcnt(0): stage 0 and scales landed
-        __syncthreads();
-
-        const int g = lane >> 4;             // K group of this lane: bytes [32g, 32g+32)
-        for (int kb = 0; kb < KB; ++kb) {
-            const int buf = kb & 1;
-            if (kb + 1 < KB) {
-                issue_stage(kb + 1, buf ^ 1);
+        auto step = [&](int kb, auto bufc) {
+            constexpr int BUF = decltype(bufc)::value;
+            constexpr uint32_t XOFF = BUF * BM * 128, WOFF = BUF * BN * 128, SOFF = BUF * NWAVES * 256;
+            // This wave's loads of stage kb have landed (only stage kb is in
+            // flight); after the barrier everyone's have, and everyone is done
+            // with the other buffer, which then receives stage kb+1.
+            wait_vmcnt<0>();
+            lds_barrier();
+            issue_stage(kb + 1, std::integral_constant<int, 1 - BUF>{});
+            const int kn = kb + 1 < KB ? kb + 1 : kb;
+            float sb_nxt[FJ];
 #pragma unroll
-                for (int i = 0; i < FI; ++i) sa_nxt[i] = p.sa[(int64_t)(kb + 1) * p.M + sa_row[i]];
-#pragma unroll
-                for (int j = 0; j < FJ; ++j) sb_nxt[j] = sb[(int64_t)sb_row[j] * KB + kb + 1];
-            }
-            const uint8_t* xs = smem + buf * STAGE;
-            const uint8_t* ws = xs + BM * 128;
+            for (int j = 0; j < FJ; ++j) sb_nxt[j] = sb[(int64_t)sb_row[j] * KB + kn];
 
-            // X fragments (MFMA B operand): row wm*TM+16i+l%16, bytes [32g, 32g+32)
-            i32x8 xf[FI];
+            // fragments: X (MFMA B operand), W (MFMA A operand), sA per row
+            i32x8 xf[FI], wfr[FJ];
+            float sa_v[FI];
 #pragma unroll
             for (int i = 0; i < FI; ++i) {
-                const int r = wm * TM + 16 * i + (lane & 15);
-                const uint8_t* rp = xs + r * 128;
-                const i32x4 lo = *reinterpret_cast<const i32x4*>(rp + (((2 * g) ^ lds_swz(r)) << 4));
-                const i32x4 hi = *reinterpret_cast<const i32x4*>(rp + (((2 * g + 1) ^ lds_swz(r)) << 4));
+                const i32x4 lo = *reinterpret_cast<const i32x4*>(smem + XOFF + 2048 * i + xa[0]);
+                const i32x4 hi = *reinterpret_cast<const i32x4*>(smem + XOFF + 2048 * i + xa[1]);
                 xf[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                sa_v[i] = *reinterpret_cast<const float*>(smem + SOFF + saa + 64 * i);
             }
-            constexpr bool kF16 = PATH == kPathF16 || PATH == kPathF16Pow2;
-            constexpr bool kPow2 = PATH == kPathFp8Pow2 || PATH == kPathF16Pow2;
-            // FP16 copies of the X fragments (exact widening), four K quarters each
-            f16x8 xh[kF16 ? FI : 1][4];
-            if constexpr (kF16) {
-#pragma unroll
-                for (int i = 0; i < FI; ++i)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) xh[i][q] = e4m3x8_to_f16(xf[i][2 * q], xf[i][2 * q + 1]);
-            }
-            float sa_eff[FI];
-#pragma unroll
-            for (int i = 0; i < FI; ++i) sa_eff[i] = kPow2 ? pow2_part(sa_cur[i]) : sa_cur[i];
 #pragma unroll
             for (int j = 0; j < FJ; ++j) {
-                const int r = wn * TN + 16 * j + (lane & 15);
-                const uint8_t* rp = ws + r * 128;
-                const i32x4 lo = *reinterpret_cast<const i32x4*>(rp + (((2 * g) ^ lds_swz(r)) << 4));
-                const i32x4 hi = *reinterpret_cast<const i32x4*>(rp + (((2 * g + 1) ^ lds_swz(r)) << 4));
-                const i32x8 wf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                if constexpr (PATH == kPathFp8Pow2) {
+                const i32x4 lo = *reinterpret_cast<const i32x4*>(smem + WOFF + 2048 * j + wa[0]);
+                const i32x4 hi = *reinterpret_cast<const i32x4*>(smem + WOFF + 2048 * j + wa[1]);
+                wfr[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+
+            if constexpr (PATH == kPathFp8Pow2) {
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) {
                     const int sw = e8m0_of(sb_cur[j]);
 #pragma unroll
                     for (int i = 0; i < FI; ++i)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            wf, xf[i], acc[i][j], 0, 0, 0, sw, 0, e8m0_of(sa_cur[i]));
-                } else {
-                    f32x4 part[FI];
-                    if constexpr (kF16) {
-                        f16x8 wh[4];
+                            wfr[j], xf[i], acc[i][j], 0, 0, 0, sw, 0, e8m0_of(sa_v[i]));
+                }
+            } else {
+                f16x8 xh[kF16 ? FI : 1][4];
+                if constexpr (kF16) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) wh[q] = e4m3x8_to_f16(wf[2 * q], wf[2 * q + 1]);
+                    for (int i = 0; i < FI; ++i)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            xh[i][q] = e4m3x8_to_f16(xf[i][2 * q], xf[i][2 * q + 1]);
+                }
+                // promotion scales
+                float s_uni[FI];
+                if constexpr (kUniformSb) {
+                    const float sbv = kPow2 ? pow2_part(sb_cur[0]) : sb_cur[0];
+#pragma unroll
+                    for (int i = 0; i < FI; ++i) s_uni[i] = (kPow2 ? pow2_part(sa_v[i]) : sa_v[i]) * sbv;
+                }
+                if constexpr (!kF16) {
+                    // scheduling template: the LDS reads first, then one MFMA
+                    // followed by the promotion FMAs it can hide
+                    __builtin_amdgcn_sched_group_barrier(0x100, 3 * FI + 2 * FJ, 0);
+#pragma unroll
+                    for (int q = 0; q < FI * FJ; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                    }
+                }
+                // Software pipeline over subtile columns: the MFMAs of column j
+                // are issued before the promotion of column j-1.
+                f32x4 prev[FI];
+#pragma unroll
+                for (int j = 0; j <= FJ; ++j) {
+                    f32x4 cur[FI];
+                    if (j < FJ) {
+                        if constexpr (kF16) {
+                            f16x8 wh[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                wh[q] = e4m3x8_to_f16(wfr[j][2 * q], wfr[j][2 * q + 1]);
+#pragma unroll
+                            for (int i = 0; i < FI; ++i) {
+                                cur[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    wh[0], xh[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                                for (int q = 1; q < 4; ++q)
+                                    cur[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[q], xh[i][q],
+                                                                                    cur[i], 0, 0, 0);
+                            }
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < FI; ++i)
+                                cur[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    wfr[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                        }
+                    }
+                    if (j > 0) {
+                        const int jp = j - 1;
 #pragma unroll
                         for (int i = 0; i < FI; ++i) {
-                            part[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                wh[0], xh[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                            float s;
+                            if constexpr (kUniformSb) {
+                                s = s_uni[i];
+                            } else {
+                                const float sbj = kPow2 ? pow2_part(sb_cur[jp]) : sb_cur[jp];
+                                s = (kPow2 ? pow2_part(sa_v[i]) : sa_v[i]) * sbj;
+                            }
 #pragma unroll
-                            for (int q = 1; q < 4; ++q)
-                                part[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[q], xh[i][q],
-                                                                                 part[i], 0, 0, 0);
+                            for (int r2 = 0; r2 < 4; ++r2)
+                                acc[i][jp][r2] = fmaf(s, prev[i][r2], acc[i][jp][r2]);
                         }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < FI; ++i)
-                            part[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                wf, xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                     }
-                    const float sbj = kPow2 ? pow2_part(sb_cur[j]) : sb_cur[j];
+                    if (j < FJ) {
 #pragma unroll
-                    for (int i = 0; i < FI; ++i) {
-                        const float s = sa_eff[i] * sbj;
-#pragma unroll
-                        for (int r2 = 0; r2 < 4; ++r2) acc[i][j][r2] = fmaf(s, part[i][r2], acc[i][j][r2]);
+                        for (int i = 0; i < FI; ++i) prev[i] = cur[i];
                     }
                 }
             }
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < FI; ++i) sa_cur[i] = sa_nxt[i];
 #pragma unroll
             for (int j = 0; j < FJ; ++j) sb_cur[j] = sb_nxt[j];
+        };
+        // K loop unrolled by the two stages (straight-line body), then the tail.
+        int kb = 0;
+        for (; kb + 2 <= KB; kb += 2) {
+            step(kb, std::integral_constant<int, 0>{});
+            step(kb + 1, std::integral_constant<int, 1>{});
         }
+        if (kb < KB) step(kb, std::integral_constant<int, 0>{});
 
         // ---------------- epilogue: BF16 (RNE), predicated stores ----------------
+        const int g4 = 4 * g;
 #pragma unroll
         for (int i = 0; i < FI; ++i) {
-            const int64_t m = row0 + wm * TM + 16 * i + (lane & 15);
-            bool ok = m <= last_row;
-            if constexpr (MODE == kContiguous) ok = ok && p.m_indices[m < last_row ? m : last_row] == expert;
+            const int mloc = wm * TM + 16 * i + (lane & 15);
+            const int64_t m = row0 + mloc;
+            bool ok = mloc < rows_valid;
+            if constexpr (MODE == kContiguous)
+                if (ok) ok = m_indices_[m] == expert;
             if (!ok) continue;
-            uint16_t* yrow = p.y + m * N;
+            uint16_t* yrow = y_ + m * N;
 #pragma unroll
             for (int j = 0; j < FJ; ++j) {
-                const int64_t n = n0 + wn * TN + 16 * j + 4 * g;
+                const int64_t n = n0 + wn * TN + 16 * j + g4;
                 const uint32_t lo = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
                 const uint32_t hi = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
                 if ((N & 3) == 0 && n + 3 < N) {
