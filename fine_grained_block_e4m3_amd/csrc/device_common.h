@@ -18,6 +18,10 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // Wave-uniform value (moves it to a scalar register).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)uniform((int)(uint32_t)v), hi = (uint32_t)uniform((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
 
 // Two FP32 values to packed E4M3 bytes with the hardware converter
 // (round-to-nearest-even, OCP E4M3FN on gfx950), placed in the low (hi=false)

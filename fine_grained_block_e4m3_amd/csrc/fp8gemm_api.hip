@@ -55,7 +55,7 @@ fp8_status launch_status() {
 // ---------------------------------------------------------------------------
 // GEMM instances.  Naming: BM x BN workgroup tile, WAVES_M x WAVES_N waves.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int MODE, int PATH, int GROUP_M = 4>
+template <int BM, int BN, int WM, int WN, int MODE, int PATH, int STAGES = 2, int GROUP_M = 4>
 fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream) {
     p.m_tiles = (int)((MODE == fp8k::kMasked ? p.max_m : p.M) + BM - 1) / BM;
     p.n_tiles = (int)((p.N + BN - 1) / BN);
@@ -64,7 +64,7 @@ fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream) {
     if (MODE == fp8k::kMasked) tiles *= p.E;   // upper bound; the kernel counts the real ones
     int grid = (int)(tiles < cus ? tiles : cus);
     if (grid <= 0) return FP8_OK;
-    hipLaunchKernelGGL((fp8k::gemm_kernel<BM, BN, WM, WN, MODE, PATH>), dim3(grid),
+    hipLaunchKernelGGL((fp8k::gemm_kernel<BM, BN, WM, WN, MODE, PATH, STAGES>), dim3(grid),
                        dim3(64 * WM * WN), 0, stream, p.xq, p.sa, p.wq, p.sb, p.y, p.m_indices,
                        p.masked_m, p);
     return launch_status();
@@ -76,8 +76,12 @@ template <int MODE, int PATH>
 fp8_status dispatch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream) {
     if constexpr (MODE == fp8k::kDense) {
         if (p.M <= 64) return launch_gemm<64, 96, 2, 2, MODE, PATH>(p, cus, stream);
+        constexpr bool kF16 = PATH == fp8k::kPathF16 || PATH == fp8k::kPathF16Pow2;
+        const int64_t huge = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+        if constexpr (!kF16)
+            if (huge >= cus) return launch_gemm<256, 256, 2, 4, MODE, PATH>(p, cus, stream);
         const int64_t big = ((p.M + 255) / 256) * ((p.N + 127) / 128);
-        if (big >= 2 * cus) return launch_gemm<256, 128, 4, 2, MODE, PATH>(p, cus, stream);
+        if (big >= 2 * cus || (kF16 && huge >= cus)) return launch_gemm<256, 128, 4, 2, MODE, PATH>(p, cus, stream);
         return launch_gemm<128, 128, 2, 2, MODE, PATH>(p, cus, stream);
     } else if constexpr (MODE == fp8k::kContiguous) {
         // The M tile must equal the layout alignment (128): one expert per tile.

@@ -156,6 +156,16 @@ __device__ __forceinline__ void dma_lds16(uint32_t m0, const uint32_t (&voff)[N]
                      : "s"(m0), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
                        "s"(rsrc), "s"(soff));
 }
+// One wave-wide 16-byte-per-lane DMA: lane l's bytes land at
+// m0 + 1024*Q + 16*l and come from buffer offset voff + 1024*Q + soff.
+template <int Q>
+__device__ __forceinline__ void dma_lds16_one(uint32_t m0, uint32_t voff, i32x4 rsrc, int soff) {
+    int saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, %4 offen offset:%5 lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff), "i"(1024 * Q));
+}
 // One wave-wide DMA of 4 bytes per lane: lane l's dword lands at m0 + 4*l.
 __device__ __forceinline__ void dma_lds4(uint32_t m0, uint32_t voff, i32x4 rsrc, int soff) {
     int saved;
@@ -186,7 +196,16 @@ __device__ __forceinline__ void raster(int t, int m_tiles, int n_tiles, int grou
     nt = r / gm;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, int PATH>
+// Calls f(integral_constant<int, 0>) ... f(integral_constant<int, S-1>) in order.
+template <int S, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (S > 0) {
+        static_for<S - 1>(f);
+        f(std::integral_constant<int, S - 1>{});
+    }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, int PATH, int STAGES>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     const uint8_t* __restrict__ xq_, const float* __restrict__ sa_, const uint8_t* __restrict__ wq_,
     const float* __restrict__ sb_, uint16_t* __restrict__ y_, const int32_t* __restrict__ m_indices_,
@@ -198,12 +217,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     constexpr int FJ = TN / 16;        // ... along n
     constexpr int XLOADS = BM / 8 / NWAVES;   // 1 KB direct-to-LDS loads per wave per stage
     constexpr int WLOADS = BN / 8 / NWAVES;
-    // LDS layout, by operand then stage: [X0][X1][W0][W1][sA0][sA1].  The
-    // operand base lives in the per-lane address and the stage offset (at most
-    // 32 KB) in the ds_read immediate.
-    constexpr int W_BASE = 2 * BM * 128;
-    constexpr int SA_BASE = W_BASE + 2 * BN * 128;   // per-wave activation-scale slices (64 floats)
-    constexpr int LDS_BYTES = SA_BASE + 2 * NWAVES * 256;
+    constexpr int NPIECE = XLOADS + WLOADS + 1;   // loads per wave per stage
+    constexpr int PER_STAGE = NPIECE;
+    // Scales of a stage: waves 0 .. NSA-1 load the activation scales of the
+    // tile's rows (64 each), the other waves each load a copy of the weight
+    // scales of the tile's 128-row weight blocks (one per lane).  Every wave
+    // issues the same number of loads, so one vmcnt target serves all.
+    constexpr int NSA = BM / 64;
+    // LDS layout, by operand then stage: [X0 X1 ..][W0 W1 ..][scales0 ..].
+    // The operand base lives in the per-lane address and the stage offset in
+    // the ds_read immediate.
+    constexpr int W_BASE = STAGES * BM * 128;
+    constexpr int SC_BASE = W_BASE + STAGES * BN * 128;
+    constexpr int LDS_BYTES = SC_BASE + STAGES * NWAVES * 256;
     // A wave's 16-wide n subtiles all lie in one 128-row weight block when its
     // n range is 128-aligned inside a 128-aligned tile: one sB per K block.
     constexpr bool kUniformSb = (BN % 128 == 0 || 128 % BN == 0) && (128 % TN == 0 || TN % 128 == 0)
@@ -211,12 +237,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     constexpr bool kF16 = PATH == kPathF16 || PATH == kPathF16Pow2;
     constexpr bool kPow2 = PATH == kPathFp8Pow2 || PATH == kPathF16Pow2;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 subtiles");
-    static_assert(TM <= 64, "one scale load per wave covers at most 64 rows");
+    static_assert(BM % 64 == 0 && NSA < NWAVES, "activation scales: 64 rows per wave, one wave left for sB");
+    static_assert(BN / 128 + 2 <= 64, "one scale load covers the tile's weight blocks");
     static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "tile rows per wave");
     static_assert(XLOADS >= 1 && XLOADS <= 4 && WLOADS >= 1 && WLOADS <= 4, "loads per wave");
-    static_assert(BM * 128 <= 65535 && BN * 128 <= 65535, "stage offsets are ds_read immediates");
+    static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS holds the stage ring");
+    static_assert((STAGES - 2) * PER_STAGE <= 63, "vmcnt range");
 
-    // Two LDS stages: the loads of K block kb+1 fly while block kb is used.
+    // A ring of STAGES LDS buffers: the loads of K blocks kb+1 .. kb+STAGES-1
+    // fly while block kb is used.
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
@@ -260,7 +289,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         const int grp = wave * WLOADS + q;
         vw[q] = (lane_off ^ (uint32_t)((grp & 1) << 4)) + (uint32_t)(grp * 8 * K) - 1024u * q;
     }
-    const uint32_t sa_lane = (uint32_t)(4 * (wm * TM + (lane % TM)));
     // LDS fragment addresses within a stage: row r, 16-byte chunk c at
     // r*128 + 16*(c ^ swz(r)); this lane reads chunks 2g and 2g+1.
     // The swizzle depends on the row mod 16 only, so subtile i of this wave
@@ -273,7 +301,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         xa[h] = (uint32_t)((wm * TM + r) * 128 + (((2 * g + h) ^ lds_swz(r)) << 4));
         wa[h] = (uint32_t)(W_BASE + (wn * TN + r) * 128 + (((2 * g + h) ^ lds_swz(r)) << 4));
     }
-    const uint32_t saa = (uint32_t)(SA_BASE + wave * 256 + 4 * (lane & 15));
+    // activation scale of row r of the tile at SC + 4r; weight scales at
+    // SC + 256*NSA + 4*slot (the first copy)
+    const uint32_t saa = (uint32_t)(SC_BASE + 4 * (wm * TM + (lane & 15)));
+    const bool sa_wave = wave < NSA;
+    const uint32_t sc_voff = sa_wave ? (uint32_t)(4 * (64 * wave + lane)) : (uint32_t)(4 * lane * KB);
     const uint32_t lds0 = uniform((int)lds_addr(smem));
 
     // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs,
@@ -339,29 +371,61 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         const i32x4 xr = make_rsrc(xq_ + row0 * K, (uint32_t)(rows_valid * K));
         const i32x4 wr = make_rsrc(wq + n0 * K, (uint32_t)(cols_valid * K));
         const float* sa_row0 = sa_ + row0;
-        // Weight-scale rows (uniform per subtile).
-        int sb_row[FJ];
+        // Weight scales: lane l of a wave's scale load fetches block row
+        // nb0 + l; rows past the last weight block read zero.
+        const int nb0 = (int)(n0 >> 7);
+        const int nbl = (int)min((int64_t)(BN / 128 + 2), (N + 127) / 128 - nb0);
+        // This wave's scale load, as a base that advances adv bytes per K
+        // block, an soffset of sstep bytes per K block and a byte range.
+        const uint64_t sc_base = uniform_u64(sa_wave ? (uint64_t)sa_row0 : (uint64_t)(sb + (int64_t)nb0 * KB));
+        const uint32_t sc_adv = sa_wave ? (uint32_t)(4 * p.M) : 0u;
+        const int sc_step = sa_wave ? 0 : 4;
+        const uint32_t sc_rec = uniform(sa_wave ? (int)(4 * rows_valid) : (int)(4 * nbl * KB));
+        // LDS slot of each subtile's weight block (the last block for
+        // subtiles past N, whose columns are never stored)
+        uint32_t sb_slot[FJ];
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             const int64_t n = n0 + wn * TN + 16 * j;
-            sb_row[j] = uniform((int)((n < N ? n : N - 1) >> 7));
+            sb_slot[j] = (uint32_t)(SC_BASE + 256 * NSA + 4 * ((int)((n < N ? n : N - 1) >> 7) - nb0));
         }
 
         // Issue the loads of K block kb into stage s.  Past the last block the
         // resources get an empty range, so the loads are discarded by the
         // range check without a branch (the loop body stays one basic block).
-        auto issue_stage = [&](int kb, auto bufc) {
+        // A stage is issued as NPIECE single loads (X rows, W rows, scales)
+        // so that they can be spread between the MFMAs of a step.
+        struct StageLoads {
+            uint32_t xm0, wm0, sm0;
+            i32x4 xr, wr, sr;
+            int koff, soff;
+        };
+        auto stage_loads = [&](int kb, auto bufc) {
             constexpr uint32_t s = decltype(bufc)::value;
-            const bool live = kb < KB;
-            const int koff = kb * 128;
-            i32x4 xrr = xr, wrr = wr;
-            xrr[2] = live ? xr[2] : 0;
-            wrr[2] = live ? wr[2] : 0;
-            dma_lds16<XLOADS>(lds0 + s * BM * 128 + (uint32_t)(wave * XLOADS * 1024), vx, xrr, koff);
-            dma_lds16<WLOADS>(lds0 + W_BASE + s * BN * 128 + (uint32_t)(wave * WLOADS * 1024), vw, wrr, koff);
-            const i32x4 sr = make_rsrc(sa_row0 + (int64_t)(live ? kb : 0) * p.M,
-                                       live ? (uint32_t)(4 * rows_valid) : 0u);
-            dma_lds4(lds0 + SA_BASE + s * NWAVES * 256 + (uint32_t)(wave * 256), sa_lane, sr, 0);
+            // all ones for a real block, zero past the last one (only the
+            // ranges are cleared: nothing outside an empty range is read)
+            const int live = -(int)(kb < KB);
+            StageLoads L;
+            L.xm0 = lds0 + s * BM * 128 + (uint32_t)(wave * XLOADS * 1024);
+            L.wm0 = lds0 + W_BASE + s * BN * 128 + (uint32_t)(wave * WLOADS * 1024);
+            L.sm0 = lds0 + SC_BASE + s * NWAVES * 256 + (uint32_t)(wave * 256);
+            L.xr = xr;
+            L.wr = wr;
+            L.xr[2] = xr[2] & live;
+            L.wr[2] = wr[2] & live;
+            // scales: activation row kb of sA, or weight-block column kb of sB
+            const uint64_t scb = sc_base + (uint64_t)(uint32_t)kb * sc_adv;
+            L.sr = i32x4{(int)(uint32_t)scb, (int)(uint32_t)(scb >> 32) & 0xFFFF, (int)sc_rec & live,
+                         0x00020000};
+            L.koff = kb * 128;
+            L.soff = kb * sc_step;
+            return L;
+        };
+        auto issue_piece = [&](const StageLoads& L, auto pc) {
+            constexpr int P = decltype(pc)::value;
+            if constexpr (P < XLOADS) dma_lds16_one<P>(L.xm0, vx[P], L.xr, L.koff);
+            else if constexpr (P < XLOADS + WLOADS) dma_lds16_one<P - XLOADS>(L.wm0, vw[P - XLOADS], L.wr, L.koff);
+            else dma_lds4(L.sm0, sc_voff, L.sr, L.soff);
         };
 
         f32x4 acc[FI][FJ];
@@ -372,137 +436,172 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 
         // All waves are done with the previous tile's buffers.
         lds_barrier();
-        issue_stage(0, std::integral_constant<int, 0>{});
-        float sb_cur[FJ];
-#pragma unroll
-        for (int j = 0; j < FJ; ++j) sb_cur[j] = sb[(int64_t)sb_row[j] * KB];
+        static_for<STAGES - 1>([&](auto sc) {
+            const StageLoads L = stage_loads(decltype(sc)::value, sc);
+            static_for<NPIECE>([&](auto pc) { issue_piece(L, pc); });
+        });
 
         auto step = [&](int kb, auto bufc) {
             constexpr int BUF = decltype(bufc)::value;
             constexpr uint32_t XOFF = BUF * BM * 128, WOFF = BUF * BN * 128, SOFF = BUF * NWAVES * 256;
-            // This wave's loads of stage kb have landed (only stage kb is in
-            // flight); after the barrier everyone's have, and everyone is done
-            // with the other buffer, which then receives stage kb+1.
-            wait_vmcnt<0>();
+            // This wave's loads of block kb have landed (blocks kb+1 ..
+            // kb+STAGES-2 may still fly); after the barrier everyone's have,
+            // and everyone is done with block kb-1's buffer, which then
+            // receives block kb+STAGES-1.
+            // The scheduling fences keep this step's instructions between
+            // its barrier and the next one (the barrier asm orders memory
+            // operations only; MFMAs and FMAs could otherwise drift past it).
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<(STAGES - 2) * PER_STAGE>();
             lds_barrier();
-            issue_stage(kb + 1, std::integral_constant<int, 1 - BUF>{});
-            const int kn = kb + 1 < KB ? kb + 1 : kb;
-            float sb_nxt[FJ];
-#pragma unroll
-            for (int j = 0; j < FJ; ++j) sb_nxt[j] = sb[(int64_t)sb_row[j] * KB + kn];
+            __builtin_amdgcn_sched_barrier(0);
+            // Block kb+STAGES-1 goes to the buffer freed by block kb-1; its
+            // loads are spread over the subtile rows below, a few after each
+            // row's MFMAs, so that no wave stalls long on a full load queue
+            // while it has matrix work to issue.
+            const StageLoads L = stage_loads(kb + STAGES - 1, std::integral_constant<int, (BUF + STAGES - 1) % STAGES>{});
+            // (Fences: VALU and SALU work may move across, MFMAs and memory
+            // instructions may not.)
+            auto pieces_of_row = [&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                __builtin_amdgcn_sched_barrier(0x0006);
+                static_for<NPIECE>([&](auto pc) {
+                    constexpr int P = decltype(pc)::value;
+                    if constexpr (P * FI / NPIECE == i) issue_piece(L, pc);
+                });
+                __builtin_amdgcn_sched_barrier(0x0006);
+            };
 
-            // fragments: X (MFMA B operand), W (MFMA A operand), sA per row
-            i32x8 xf[FI], wfr[FJ];
-            float sa_v[FI];
+            // Scales of this block: sB of each subtile column here, sA of the
+            // lane's row in subtile row i when row i is used.
+            float sb_cur[FJ];
+            auto read_sa = [&](int i) { return *reinterpret_cast<const float*>(smem + SOFF + saa + 64 * i); };
 #pragma unroll
-            for (int i = 0; i < FI; ++i) {
-                const i32x4 lo = *reinterpret_cast<const i32x4*>(smem + XOFF + 2048 * i + xa[0]);
-                const i32x4 hi = *reinterpret_cast<const i32x4*>(smem + XOFF + 2048 * i + xa[1]);
-                xf[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                sa_v[i] = *reinterpret_cast<const float*>(smem + SOFF + saa + 64 * i);
+            for (int j = 0; j < FJ; ++j) {
+                if (kUniformSb && j > 0) sb_cur[j] = sb_cur[0];
+                else sb_cur[j] = *reinterpret_cast<const float*>(smem + SOFF + sb_slot[j]);
             }
+            // W fragments (MFMA A operand) stay in registers for the block;
+            // X fragments (B operand) stream one 16-row subtile at a time.
+            i32x8 wfr[FJ];
 #pragma unroll
             for (int j = 0; j < FJ; ++j) {
                 const i32x4 lo = *reinterpret_cast<const i32x4*>(smem + WOFF + 2048 * j + wa[0]);
                 const i32x4 hi = *reinterpret_cast<const i32x4*>(smem + WOFF + 2048 * j + wa[1]);
                 wfr[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
+            auto read_x = [&](int i) {
+                const i32x4 lo = *reinterpret_cast<const i32x4*>(smem + XOFF + 2048 * i + xa[0]);
+                const i32x4 hi = *reinterpret_cast<const i32x4*>(smem + XOFF + 2048 * i + xa[1]);
+                return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            };
 
             if constexpr (PATH == kPathFp8Pow2) {
+                // power-of-two scales as E8M0 operands: the matrix core scales
+                // and accumulates; no promotion
+                int sbe[FJ];
 #pragma unroll
-                for (int j = 0; j < FJ; ++j) {
-                    const int sw = e8m0_of(sb_cur[j]);
+                for (int j = 0; j < FJ; ++j) sbe[j] = e8m0_of(sb_cur[j]);
+                i32x8 xc = read_x(0);
+                static_for<FI>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    i32x8 xn = xc;
+                    if constexpr (i + 1 < FI) xn = read_x(i + 1);
+                    const int sae = e8m0_of(read_sa(i));
+                    pieces_of_row(ic);
 #pragma unroll
-                    for (int i = 0; i < FI; ++i)
+                    for (int j = 0; j < FJ; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            wfr[j], xf[i], acc[i][j], 0, 0, 0, sw, 0, e8m0_of(sa_v[i]));
-                }
+                            wfr[j], xc, acc[i][j], 0, 0, 0, sbe[j], 0, sae);
+                    xc = xn;
+                });
             } else {
-                f16x8 xh[kF16 ? FI : 1][4];
+                // W fragments widened to FP16 once per block on the precise path
+                f16x8 wh[kF16 ? FJ : 1][4];
                 if constexpr (kF16) {
 #pragma unroll
-                    for (int i = 0; i < FI; ++i)
+                    for (int j = 0; j < FJ; ++j)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            xh[i][q] = e4m3x8_to_f16(xf[i][2 * q], xf[i][2 * q + 1]);
+                        for (int q = 0; q < 4; ++q) wh[j][q] = e4m3x8_to_f16(wfr[j][2 * q], wfr[j][2 * q + 1]);
                 }
-                // promotion scales
-                float s_uni[FI];
-                if constexpr (kUniformSb) {
-                    const float sbv = kPow2 ? pow2_part(sb_cur[0]) : sb_cur[0];
-#pragma unroll
-                    for (int i = 0; i < FI; ++i) s_uni[i] = (kPow2 ? pow2_part(sa_v[i]) : sa_v[i]) * sbv;
-                }
-                if constexpr (!kF16) {
-                    // scheduling template: the LDS reads first, then one MFMA
-                    // followed by the promotion FMAs it can hide
-                    __builtin_amdgcn_sched_group_barrier(0x100, 3 * FI + 2 * FJ, 0);
-#pragma unroll
-                    for (int q = 0; q < FI * FJ; ++q) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                // Software pipeline over subtile rows: the MFMAs of row i are
+                // issued before the promotion of row i-1 by sA*sB.  With a
+                // large wave tile (128 accumulator registers) the partials of
+                // a row are promoted right after its MFMAs instead; the other
+                // wave on the SIMD covers the MFMA latency.
+                constexpr bool kPipe = true;
+                constexpr int LAG = kPipe ? 1 : 0;
+                f32x4 prev[FJ];
+                i32x8 xc = read_x(0);
+                float sa_prev = 0.f, sa_c = read_sa(0);
+                static_for<FI + LAG>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    i32x8 xn = xc;
+                    float sa_n = sa_c;
+                    if constexpr (i + 1 < FI) {
+                        xn = read_x(i + 1);
+                        sa_n = read_sa(i + 1);
                     }
-                }
-                // Software pipeline over subtile columns: the MFMAs of column j
-                // are issued before the promotion of column j-1.
-                f32x4 prev[FI];
-#pragma unroll
-                for (int j = 0; j <= FJ; ++j) {
-                    f32x4 cur[FI];
-                    if (j < FJ) {
+                    f32x4 cur[FJ];
+                    if constexpr (i < FI) pieces_of_row(ic);
+                    if constexpr (i < FI) {
                         if constexpr (kF16) {
-                            f16x8 wh[4];
+                            f16x8 xh[4];
 #pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                wh[q] = e4m3x8_to_f16(wfr[j][2 * q], wfr[j][2 * q + 1]);
+                            for (int q = 0; q < 4; ++q) xh[q] = e4m3x8_to_f16(xc[2 * q], xc[2 * q + 1]);
 #pragma unroll
-                            for (int i = 0; i < FI; ++i) {
-                                cur[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                    wh[0], xh[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                            for (int j = 0; j < FJ; ++j) {
+                                cur[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    wh[j][0], xh[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                                 for (int q = 1; q < 4; ++q)
-                                    cur[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[q], xh[i][q],
-                                                                                    cur[i], 0, 0, 0);
+                                    cur[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[j][q], xh[q], cur[j], 0, 0, 0);
                             }
                         } else {
 #pragma unroll
-                            for (int i = 0; i < FI; ++i)
-                                cur[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                    wfr[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                            for (int j = 0; j < FJ; ++j)
+                                cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    wfr[j], xc, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                         }
                     }
-                    if (j > 0) {
-                        const int jp = j - 1;
+                    if constexpr (!kPipe) {
 #pragma unroll
-                        for (int i = 0; i < FI; ++i) {
-                            float s;
-                            if constexpr (kUniformSb) {
-                                s = s_uni[i];
-                            } else {
-                                const float sbj = kPow2 ? pow2_part(sb_cur[jp]) : sb_cur[jp];
-                                s = (kPow2 ? pow2_part(sa_v[i]) : sa_v[i]) * sbj;
-                            }
+                        for (int j = 0; j < FJ; ++j) prev[j] = cur[j];
+                        sa_prev = sa_c;
+                    }
+                    if constexpr (i + 1 - LAG > 0) {
+                        constexpr int ip = i - LAG;
+                        const float sav = kPow2 ? pow2_part(sa_prev) : sa_prev;
 #pragma unroll
-                            for (int r2 = 0; r2 < 4; ++r2)
-                                acc[i][jp][r2] = fmaf(s, prev[i][r2], acc[i][jp][r2]);
+                        for (int j = 0; j < FJ; ++j) {
+                            float sc;
+                            if (kUniformSb && j > 0) sc = sav * (kPow2 ? pow2_part(sb_cur[0]) : sb_cur[0]);
+                            else sc = sav * (kPow2 ? pow2_part(sb_cur[j]) : sb_cur[j]);
+#pragma unroll
+                            for (int r2 = 0; r2 < 4; ++r2) acc[ip][j][r2] = fmaf(sc, prev[j][r2], acc[ip][j][r2]);
                         }
                     }
-                    if (j < FJ) {
+                    if constexpr (kPipe && i < FI) {
 #pragma unroll
-                        for (int i = 0; i < FI; ++i) prev[i] = cur[i];
+                        for (int j = 0; j < FJ; ++j) prev[j] = cur[j];
                     }
-                }
+                    xc = xn;
+                    if constexpr (kPipe) sa_prev = sa_c;
+                    sa_c = sa_n;
+                    // A row's promotion stays in its row: at most two rows of
+                    // partials are live.
+                    __builtin_amdgcn_sched_barrier(0);
+                });
             }
-#pragma unroll
-            for (int j = 0; j < FJ; ++j) sb_cur[j] = sb_nxt[j];
+            __builtin_amdgcn_sched_barrier(0);
         };
-        // K loop unrolled by the two stages (straight-line body), then the tail.
+        // K loop unrolled by the ring size (straight-line body), then the tail.
         int kb = 0;
-        for (; kb + 2 <= KB; kb += 2) {
-            step(kb, std::integral_constant<int, 0>{});
-            step(kb + 1, std::integral_constant<int, 1>{});
-        }
-        if (kb < KB) step(kb, std::integral_constant<int, 0>{});
+        for (; kb + STAGES <= KB; kb += STAGES)
+            static_for<STAGES>([&](auto sc) { step(kb + decltype(sc)::value, sc); });
+        static_for<STAGES - 1>([&](auto sc) {
+            if (kb + decltype(sc)::value < KB) step(kb + decltype(sc)::value, sc);
+        });
 
         // ---------------- epilogue: BF16 (RNE), predicated stores ----------------
         const int g4 = 4 * g;
@@ -531,6 +630,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             }
         }
     }
+    // The last stages issued were discarded loads; let them retire before the
+    // workgroup's LDS is released.
+    wait_vmcnt<0>();
 }
 
 }  // namespace fp8k

@@ -162,6 +162,28 @@ def test_large_tile_instance_sampled(precise):
     assert_close(y[mi, ni], ref, "large tiles")
 
 
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_huge_tile_instance_ragged_sampled(ue8m0):
+    """At least one 256x256 tile per compute unit takes the 256x256 instance:
+    here with a ragged last tile in M and N (N not a multiple of 4) and an odd
+    number of K blocks; every row and column of the ragged edges is checked."""
+    M, N, K = 1900, 8102, 640
+    flags = oracle.FLAG_UE8M0 if ue8m0 else 0
+    wl = workloads.dense(M, N, K, seed=13, outlier_frac=0.001, outlier_mult=100.0)
+    xq, sa = oracle.quant_1x128(wl.x, flags)
+    wq, sb = oracle.quant_128x128(wl.w, flags)
+    y = run_gemm(xq, sa, wq, sb, ue8m0=ue8m0)
+    rng = np.random.default_rng(3)
+    mi, ni = rng.integers(0, M, 20000), rng.integers(0, N, 20000)
+    edge_m, edge_n = np.arange(1792, M), np.arange(7936, N)
+    mi = np.concatenate([mi, np.repeat(edge_m, 16), rng.integers(0, M, 16 * len(edge_n)), np.full(N, M - 1)])
+    ni = np.concatenate([ni, rng.integers(0, N, 16 * len(edge_m)), np.repeat(edge_n, 16), np.arange(N)])
+    ref = oracle.gemm_nt_elems(xq, sa, wq, sb, mi, ni, flags)
+    bound = fp8_mfma_error_bound(xq, sa, wq, sb, np.zeros((M, N)), pow2=ue8m0)[mi, ni] \
+        + 2.0 ** -8 * np.abs(ref)
+    assert_close_or_bounded(y[mi, ni], ref, bound, "256x256 tiles, ragged edges")
+
+
 @pytest.mark.parametrize("precise", PATHS)
 def test_deterministic_repeats(precise):
     wl = workloads.dense(300, 512, 1024, seed=77, outlier_frac=0.01, outlier_mult=50.0)
