@@ -7,6 +7,7 @@
 
 namespace fp8k {
 
+typedef int   i32x2 __attribute__((ext_vector_type(2)));
 typedef int   i32x4 __attribute__((ext_vector_type(4)));
 typedef int   i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -196,6 +196,16 @@ __device__ __forceinline__ void raster(int t, int m_tiles, int n_tiles, int grou
     nt = r / gm;
 }
 
+// A 16x128 E4M3 fragment of a lane from LDS: 16 bytes at base+a0 and 16 at
+// base+a1, as four 8-byte reads.
+__device__ __forceinline__ i32x8 lds_frag(const uint8_t* base, uint32_t a0, uint32_t a1) {
+    const i32x2 p = *reinterpret_cast<const i32x2*>(base + a0);
+    const i32x2 q = *reinterpret_cast<const i32x2*>(base + a0 + 8);
+    const i32x2 r = *reinterpret_cast<const i32x2*>(base + a1);
+    const i32x2 t = *reinterpret_cast<const i32x2*>(base + a1 + 8);
+    return i32x8{p[0], p[1], q[0], q[1], r[0], r[1], t[0], t[1]};
+}
+
 // Calls f(integral_constant<int, 0>) ... f(integral_constant<int, S-1>) in order.
 template <int S, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -482,19 +492,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                 else sb_cur[j] = *reinterpret_cast<const float*>(smem + SOFF + sb_slot[j]);
             }
             // W fragments (MFMA A operand) stay in registers for the block;
-            // X fragments (B operand) stream one 16-row subtile at a time.
+            // X fragments (B operand) stream one 16-row subtile at a time,
+            // two subtiles ahead of their use.  Fragments are read as four
+            // 8-byte LDS reads: measured on gfx950, this interferes less
+            // with the MFMAs than two 16-byte reads.
             i32x8 wfr[FJ];
 #pragma unroll
-            for (int j = 0; j < FJ; ++j) {
-                const i32x4 lo = *reinterpret_cast<const i32x4*>(smem + WOFF + 2048 * j + wa[0]);
-                const i32x4 hi = *reinterpret_cast<const i32x4*>(smem + WOFF + 2048 * j + wa[1]);
-                wfr[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-            auto read_x = [&](int i) {
-                const i32x4 lo = *reinterpret_cast<const i32x4*>(smem + XOFF + 2048 * i + xa[0]);
-                const i32x4 hi = *reinterpret_cast<const i32x4*>(smem + XOFF + 2048 * i + xa[1]);
-                return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            };
+            for (int j = 0; j < FJ; ++j) wfr[j] = lds_frag(smem + WOFF + 2048 * j, wa[0], wa[1]);
+            auto read_x = [&](int i) { return lds_frag(smem + XOFF + 2048 * i, xa[0], xa[1]); };
 
             if constexpr (PATH == kPathFp8Pow2) {
                 // power-of-two scales as E8M0 operands: the matrix core scales
@@ -502,18 +507,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                 int sbe[FJ];
 #pragma unroll
                 for (int j = 0; j < FJ; ++j) sbe[j] = e8m0_of(sb_cur[j]);
-                i32x8 xc = read_x(0);
+                i32x8 xq[3];
+                static_for<(FI < 2 ? FI : 2)>([&](auto pc) { xq[decltype(pc)::value] = read_x(decltype(pc)::value); });
                 static_for<FI>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
-                    i32x8 xn = xc;
-                    if constexpr (i + 1 < FI) xn = read_x(i + 1);
+                    const i32x8 xc = xq[i % 3];
+                    if constexpr (i + 2 < FI) xq[(i + 2) % 3] = read_x(i + 2);
                     const int sae = e8m0_of(read_sa(i));
                     pieces_of_row(ic);
 #pragma unroll
                     for (int j = 0; j < FJ; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             wfr[j], xc, acc[i][j], 0, 0, 0, sbe[j], 0, sae);
-                    xc = xn;
                 });
             } else {
                 // W fragments widened to FP16 once per block on the precise path
@@ -532,16 +537,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                 constexpr bool kPipe = true;
                 constexpr int LAG = kPipe ? 1 : 0;
                 f32x4 prev[FJ];
-                i32x8 xc = read_x(0);
+                i32x8 xq[3];
+                static_for<(FI < 2 ? FI : 2)>([&](auto pc) { xq[decltype(pc)::value] = read_x(decltype(pc)::value); });
                 float sa_prev = 0.f, sa_c = read_sa(0);
                 static_for<FI + LAG>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
-                    i32x8 xn = xc;
+                    i32x8 xc = xq[i % 3];
+                    if constexpr (i + 2 < FI) xq[(i + 2) % 3] = read_x(i + 2);
                     float sa_n = sa_c;
-                    if constexpr (i + 1 < FI) {
-                        xn = read_x(i + 1);
-                        sa_n = read_sa(i + 1);
-                    }
+                    if constexpr (i + 1 < FI) sa_n = read_sa(i + 1);
                     f32x4 cur[FJ];
                     if constexpr (i < FI) pieces_of_row(ic);
                     if constexpr (i < FI) {
@@ -564,6 +568,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                                     wfr[j], xc, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                         }
                     }
+                    if constexpr (kF16) __builtin_amdgcn_sched_barrier(0);
                     if constexpr (!kPipe) {
 #pragma unroll
                         for (int j = 0; j < FJ; ++j) prev[j] = cur[j];
@@ -585,9 +590,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 #pragma unroll
                         for (int j = 0; j < FJ; ++j) prev[j] = cur[j];
                     }
-                    xc = xn;
                     if constexpr (kPipe) sa_prev = sa_c;
                     sa_c = sa_n;
+                    // FP8 path: each MFMA of this row is followed by four of the
+                    // previous row's promotion FMAs (the matrix core runs one
+                    // MFMA while the VALU takes the FMAs of this or the other
+                    // wave on the SIMD).
+                    if constexpr (!kF16 && i < FI) {
+                        static_for<FJ>([&](auto qc) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x002, decltype(qc)::value == 0 ? 5 : 4, 0);
+                        });
+                    }
                     // A row's promotion stays in its row: at most two rows of
                     // partials are live.
                     __builtin_amdgcn_sched_barrier(0);
