@@ -106,15 +106,22 @@ def cpu_baseline(wl, target_s: float):
         oracle.gemm_nt(xq, sa, wq, sb, flags)
         return time.perf_counter() - t0
 
-    ms, ns = 16, 128
+    # Grow the sample (rows of X first, then whole 128-row blocks of W) until
+    # one run takes an eighth of the target, then size the timed sample from
+    # that run's rate.
+    M_cap, N_cap = min(wl.M, 4096), wl.w.shape[0]
+    ms, ns = min(16, M_cap), min(128, N_cap)
     t = run(ms, ns)
-    scale = max(1.0, target_s / max(t, 1e-6))
-    # grow rows first (cheap quantization), then columns in whole 128-blocks
-    ms_max = min(wl.M, 4096)
-    ms2 = int(min(ms_max, max(16, ms * scale)))
-    scale2 = scale * ms / ms2
-    ns2 = int(min(wl.w.shape[0], max(128, (ns * scale2) // 128 * 128)))
-    log(f"cpu baseline: calibration {ms}x{ns} took {t:.2f}s; sample {ms2}x{ns2}x{K}")
+    while t < target_s / 8 and (ms < M_cap or ns < N_cap):
+        if ms < M_cap:
+            ms = min(M_cap, 2 * ms)
+        else:
+            ns = min(N_cap, 2 * ns)
+        t = run(ms, ns)
+    scale = target_s / max(t, 1e-6)
+    ms2 = int(min(M_cap, max(ms, ms * scale)))
+    ns2 = int(min(N_cap, max(ns, (ns * scale * ms / ms2 + 64) // 128 * 128)))
+    log(f"cpu baseline: {ms}x{ns} took {t:.2f}s; timing {ms2}x{ns2}x{K}")
     t2 = run(ms2, ns2)
     flops = 2.0 * ms2 * ns2 * K
     return {
@@ -161,7 +168,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (scale for HBM byte counters)")
     args = ap.parse_args()
