@@ -438,184 +438,215 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             else dma_lds4(L.sm0, sc_voff, L.sr, L.soff);
         };
 
+        // ---------------- K loop ----------------
+        // One software pipeline over the tile's subtile rows, global row
+        // g = kb*FI + i, across K blocks:
+        //   * the X fragment and sA of row g are read at row g-2;
+        //   * the barrier of block kb sits just before row FI-2 of block kb:
+        //     by then every wave has finished its reads of block kb and its
+        //     loads of block kb+1 have landed; after it, block kb's buffer
+        //     takes the loads of block kb+2 and block kb+1 may be read;
+        //   * the W fragments and sB of block kb+1 are read during the last
+        //     row of block kb, each W fragment right after its last MFMA;
+        //   * the loads of block kb+2 are spread over the FI rows that follow
+        //     the barrier of block kb;
+        //   * row g's partials are promoted during row g+1.
+        static_assert(STAGES == 2 && FI >= 2, "two-stage pipeline over at least two subtile rows");
+        constexpr int RB = FI - 2;   // row before which the barrier of a block sits
+        auto read_x = [&](int buf, int i) { return lds_frag(smem + buf * BM * 128 + 2048 * i, xa[0], xa[1]); };
+        // (wa already holds the W region's base)
+        auto read_w = [&](int buf, int j) { return lds_frag(smem + buf * BN * 128 + 2048 * j, wa[0], wa[1]); };
+        auto read_sa = [&](int buf, int i) {
+            return *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + saa + 64 * i);
+        };
+        auto read_sb = [&](int buf, float (&v)[FJ]) {
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                if (kUniformSb && j > 0) v[j] = v[0];
+                else v[j] = *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + sb_slot[j]);
+            }
+        };
+        // the loads of a block go out at window positions 0 .. FI-1
+        auto issue_window = [&](const StageLoads& L, auto posc) {
+            constexpr int pos = decltype(posc)::value;
+            __builtin_amdgcn_sched_barrier(0x0006);
+            static_for<NPIECE>([&](auto pc) {
+                constexpr int P = decltype(pc)::value;
+                if constexpr (P * FI / NPIECE == pos) issue_piece(L, pc);
+            });
+            __builtin_amdgcn_sched_barrier(0x0006);
+        };
+
         f32x4 acc[FI][FJ];
 #pragma unroll
         for (int i = 0; i < FI; ++i)
 #pragma unroll
             for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // All waves are done with the previous tile's buffers.
+        // Prologue: block 0 in full, then the first two window positions of
+        // block 1, then the reads of block 0 that the pipeline expects.
+        wait_vmcnt<0>();
+        lds_barrier();   // all waves are done with the previous tile's buffers
+        {
+            const StageLoads L0 = stage_loads(0, std::integral_constant<int, 0>{});
+            static_for<NPIECE>([&](auto pc) { issue_piece(L0, pc); });
+        }
+        wait_vmcnt<0>();
         lds_barrier();
-        static_for<STAGES - 1>([&](auto sc) {
-            const StageLoads L = stage_loads(decltype(sc)::value, sc);
-            static_for<NPIECE>([&](auto pc) { issue_piece(L, pc); });
-        });
+        {
+            const StageLoads L1 = stage_loads(1, std::integral_constant<int, 1>{});
+            issue_window(L1, std::integral_constant<int, 0>{});
+            issue_window(L1, std::integral_constant<int, 1>{});
+        }
+        i32x8 wfr[FJ];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) wfr[j] = read_w(0, j);
+        float sb_cur[FJ], sb_prev[FJ];
+        read_sb(0, sb_cur);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) sb_prev[j] = 0.f;
+        // X fragments and sA of the next two rows (g, g+1)
+        i32x8 xr0 = read_x(0, 0), xr1 = read_x(0, 1);
+        float sr0 = read_sa(0, 0), sr1 = read_sa(0, 1);
+        // the partials of the row before (none yet: zeros promote to nothing)
+        f32x4 prev[FJ];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) prev[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float sa_prev = 0.f;
+
+        // promotion of the previous row (partials prev, row ip of acc)
+        auto promote = [&](int ip, const float (&sbv)[FJ]) {
+            const float sav = kPow2 ? pow2_part(sa_prev) : sa_prev;
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                const float sc = sav * (kPow2 ? pow2_part(sbv[j]) : sbv[j]);
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) acc[ip][j][r2] = fmaf(sc, prev[j][r2], acc[ip][j][r2]);
+            }
+        };
 
         auto step = [&](int kb, auto bufc) {
             constexpr int BUF = decltype(bufc)::value;
-            constexpr uint32_t XOFF = BUF * BM * 128, WOFF = BUF * BN * 128, SOFF = BUF * NWAVES * 256;
-            // This wave's loads of block kb have landed (blocks kb+1 ..
-            // kb+STAGES-2 may still fly); after the barrier everyone's have,
-            // and everyone is done with block kb-1's buffer, which then
-            // receives block kb+STAGES-1.
-            // The scheduling fences keep this step's instructions between
-            // its barrier and the next one (the barrier asm orders memory
-            // operations only; MFMAs and FMAs could otherwise drift past it).
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<(STAGES - 2) * PER_STAGE>();
-            lds_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            // Block kb+STAGES-1 goes to the buffer freed by block kb-1; its
-            // loads are spread over the subtile rows below, a few after each
-            // row's MFMAs, so that no wave stalls long on a full load queue
-            // while it has matrix work to issue.
-            const StageLoads L = stage_loads(kb + STAGES - 1, std::integral_constant<int, (BUF + STAGES - 1) % STAGES>{});
-            // (Fences: VALU and SALU work may move across, MFMAs and memory
-            // instructions may not.)
-            auto pieces_of_row = [&](auto ic) {
-                constexpr int i = decltype(ic)::value;
-                __builtin_amdgcn_sched_barrier(0x0006);
-                static_for<NPIECE>([&](auto pc) {
-                    constexpr int P = decltype(pc)::value;
-                    if constexpr (P * FI / NPIECE == i) issue_piece(L, pc);
-                });
-                __builtin_amdgcn_sched_barrier(0x0006);
-            };
-
-            // Scales of this block: sB of each subtile column here, sA of the
-            // lane's row in subtile row i when row i is used.
-            float sb_cur[FJ];
-            auto read_sa = [&](int i) { return *reinterpret_cast<const float*>(smem + SOFF + saa + 64 * i); };
+            constexpr int NBUF = 1 - BUF;
+            // loads of block kb+1 (positions 2 .. FI-1 of its window) and of
+            // block kb+2 (positions 0, 1, after the barrier)
+            const StageLoads L1 = stage_loads(kb + 1, std::integral_constant<int, NBUF>{});
+            const StageLoads L2 = stage_loads(kb + 2, std::integral_constant<int, BUF>{});
+            float sb_next[FJ];
+            // W fragments widened to FP16 once per block on the precise path
+            f16x8 wh[kF16 ? FJ : 1][4];
+            if constexpr (kF16) {
 #pragma unroll
-            for (int j = 0; j < FJ; ++j) {
-                if (kUniformSb && j > 0) sb_cur[j] = sb_cur[0];
-                else sb_cur[j] = *reinterpret_cast<const float*>(smem + SOFF + sb_slot[j]);
+                for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) wh[j][q] = e4m3x8_to_f16(wfr[j][2 * q], wfr[j][2 * q + 1]);
             }
-            // W fragments (MFMA A operand) stay in registers for the block;
-            // X fragments (B operand) stream one 16-row subtile at a time,
-            // two subtiles ahead of their use.  Fragments are read as four
-            // 8-byte LDS reads: measured on gfx950, this interferes less
-            // with the MFMAs than two 16-byte reads.
-            i32x8 wfr[FJ];
-#pragma unroll
-            for (int j = 0; j < FJ; ++j) wfr[j] = lds_frag(smem + WOFF + 2048 * j, wa[0], wa[1]);
-            auto read_x = [&](int i) { return lds_frag(smem + XOFF + 2048 * i, xa[0], xa[1]); };
-
+            int sbe[FJ];
             if constexpr (PATH == kPathFp8Pow2) {
-                // power-of-two scales as E8M0 operands: the matrix core scales
-                // and accumulates; no promotion
-                int sbe[FJ];
 #pragma unroll
                 for (int j = 0; j < FJ; ++j) sbe[j] = e8m0_of(sb_cur[j]);
-                i32x8 xq[3];
-                static_for<(FI < 2 ? FI : 2)>([&](auto pc) { xq[decltype(pc)::value] = read_x(decltype(pc)::value); });
-                static_for<FI>([&](auto ic) {
-                    constexpr int i = decltype(ic)::value;
-                    const i32x8 xc = xq[i % 3];
-                    if constexpr (i + 2 < FI) xq[(i + 2) % 3] = read_x(i + 2);
-                    const int sae = e8m0_of(read_sa(i));
-                    pieces_of_row(ic);
+            }
+            static_for<FI>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (i == RB) {
+                    // every read of block kb is done (lgkm) and this wave's
+                    // loads of block kb+1 have landed (vm); then publish
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    wait_vmcnt<0>();
+                    lds_barrier();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                const i32x8 xc = xr0;
+                const float sa_c = sr0;
+                // reads two rows ahead: this block, or the next one after the barrier
+                i32x8 xn;
+                float sn;
+                if constexpr (i + 2 < FI) {
+                    xn = read_x(BUF, i + 2);
+                    sn = read_sa(BUF, i + 2);
+                } else {
+                    xn = read_x(NBUF, i + 2 - FI);
+                    sn = read_sa(NBUF, i + 2 - FI);
+                }
+                xr0 = xr1;
+                xr1 = xn;
+                sr0 = sr1;
+                sr1 = sn;
+                if constexpr (i == FI - 1) read_sb(NBUF, sb_next);
+                // loads of the blocks ahead
+                if constexpr (i < RB) issue_window(L1, std::integral_constant<int, i + 2>{});
+                else issue_window(L2, std::integral_constant<int, i - RB>{});
+
+                if constexpr (PATH == kPathFp8Pow2) {
+                    const int sae = e8m0_of(sa_c);
 #pragma unroll
-                    for (int j = 0; j < FJ; ++j)
+                    for (int j = 0; j < FJ; ++j) {
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             wfr[j], xc, acc[i][j], 0, 0, 0, sbe[j], 0, sae);
-                });
-            } else {
-                // W fragments widened to FP16 once per block on the precise path
-                f16x8 wh[kF16 ? FJ : 1][4];
-                if constexpr (kF16) {
-#pragma unroll
-                    for (int j = 0; j < FJ; ++j)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) wh[j][q] = e4m3x8_to_f16(wfr[j][2 * q], wfr[j][2 * q + 1]);
-                }
-                // Software pipeline over subtile rows: the MFMAs of row i are
-                // issued before the promotion of row i-1 by sA*sB.  With a
-                // large wave tile (128 accumulator registers) the partials of
-                // a row are promoted right after its MFMAs instead; the other
-                // wave on the SIMD covers the MFMA latency.
-                constexpr bool kPipe = true;
-                constexpr int LAG = kPipe ? 1 : 0;
-                f32x4 prev[FJ];
-                i32x8 xq[3];
-                static_for<(FI < 2 ? FI : 2)>([&](auto pc) { xq[decltype(pc)::value] = read_x(decltype(pc)::value); });
-                float sa_prev = 0.f, sa_c = read_sa(0);
-                static_for<FI + LAG>([&](auto ic) {
-                    constexpr int i = decltype(ic)::value;
-                    i32x8 xc = xq[i % 3];
-                    if constexpr (i + 2 < FI) xq[(i + 2) % 3] = read_x(i + 2);
-                    float sa_n = sa_c;
-                    if constexpr (i + 1 < FI) sa_n = read_sa(i + 1);
+                        if constexpr (i == FI - 1) wfr[j] = read_w(NBUF, j);
+                    }
+                } else {
                     f32x4 cur[FJ];
-                    if constexpr (i < FI) pieces_of_row(ic);
-                    if constexpr (i < FI) {
-                        if constexpr (kF16) {
-                            f16x8 xh[4];
+                    if constexpr (kF16) {
+                        f16x8 xh[4];
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) xh[q] = e4m3x8_to_f16(xc[2 * q], xc[2 * q + 1]);
-#pragma unroll
-                            for (int j = 0; j < FJ; ++j) {
-                                cur[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                    wh[j][0], xh[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-                                for (int q = 1; q < 4; ++q)
-                                    cur[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[j][q], xh[q], cur[j], 0, 0, 0);
-                            }
-                        } else {
-#pragma unroll
-                            for (int j = 0; j < FJ; ++j)
-                                cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                    wfr[j], xc, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                        }
-                    }
-                    if constexpr (kF16) __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (!kPipe) {
-#pragma unroll
-                        for (int j = 0; j < FJ; ++j) prev[j] = cur[j];
-                        sa_prev = sa_c;
-                    }
-                    if constexpr (i + 1 - LAG > 0) {
-                        constexpr int ip = i - LAG;
-                        const float sav = kPow2 ? pow2_part(sa_prev) : sa_prev;
+                        for (int q = 0; q < 4; ++q) xh[q] = e4m3x8_to_f16(xc[2 * q], xc[2 * q + 1]);
 #pragma unroll
                         for (int j = 0; j < FJ; ++j) {
-                            float sc;
-                            if (kUniformSb && j > 0) sc = sav * (kPow2 ? pow2_part(sb_cur[0]) : sb_cur[0]);
-                            else sc = sav * (kPow2 ? pow2_part(sb_cur[j]) : sb_cur[j]);
+                            cur[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[j][0], xh[0],
+                                                                            f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-                            for (int r2 = 0; r2 < 4; ++r2) acc[ip][j][r2] = fmaf(sc, prev[j][r2], acc[ip][j][r2]);
+                            for (int q = 1; q < 4; ++q)
+                                cur[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[j][q], xh[q], cur[j], 0, 0, 0);
+                        }
+                        if constexpr (i == FI - 1) {
+#pragma unroll
+                            for (int j = 0; j < FJ; ++j) wfr[j] = read_w(NBUF, j);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < FJ; ++j) {
+                            cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                wfr[j], xc, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                            if constexpr (i == FI - 1) wfr[j] = read_w(NBUF, j);
                         }
                     }
-                    if constexpr (kPipe && i < FI) {
+                    // the previous row: row i-1 of this block, or the last
+                    // row of the previous block (with that block's sB)
+                    if constexpr (i == 0) promote(FI - 1, sb_prev);
+                    else promote(i - 1, sb_cur);
 #pragma unroll
-                        for (int j = 0; j < FJ; ++j) prev[j] = cur[j];
-                    }
-                    if constexpr (kPipe) sa_prev = sa_c;
-                    sa_c = sa_n;
-                    // FP8 path: each MFMA of this row is followed by four of the
-                    // previous row's promotion FMAs (the matrix core runs one
-                    // MFMA while the VALU takes the FMAs of this or the other
-                    // wave on the SIMD).
-                    if constexpr (!kF16 && i < FI) {
+                    for (int j = 0; j < FJ; ++j) prev[j] = cur[j];
+                    sa_prev = sa_c;
+                    if constexpr (!kF16) {
+                        // each MFMA of this row followed by four promotion FMAs
                         static_for<FJ>([&](auto qc) {
                             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                             __builtin_amdgcn_sched_group_barrier(0x002, decltype(qc)::value == 0 ? 5 : 4, 0);
                         });
                     }
-                    // A row's promotion stays in its row: at most two rows of
-                    // partials are live.
-                    __builtin_amdgcn_sched_barrier(0);
-                });
-            }
+                }
+            });
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                sb_prev[j] = sb_cur[j];
+                sb_cur[j] = sb_next[j];
+            }
         };
-        // K loop unrolled by the ring size (straight-line body), then the tail.
+        // K loop unrolled by the two buffers (straight-line body), then the tail.
         int kb = 0;
-        for (; kb + STAGES <= KB; kb += STAGES)
-            static_for<STAGES>([&](auto sc) { step(kb + decltype(sc)::value, sc); });
-        static_for<STAGES - 1>([&](auto sc) {
-            if (kb + decltype(sc)::value < KB) step(kb + decltype(sc)::value, sc);
-        });
+        for (; kb + 2 <= KB; kb += 2) {
+            step(kb, std::integral_constant<int, 0>{});
+            step(kb + 1, std::integral_constant<int, 1>{});
+        }
+        if (kb < KB) step(kb, std::integral_constant<int, 0>{});
+        // drain: the last row's partials
+        if constexpr (PATH != kPathFp8Pow2) promote(FI - 1, sb_prev);
+        // the loads issued past the last block were discarded; let them retire
+        wait_vmcnt<0>();
 
         // ---------------- epilogue: BF16 (RNE), predicated stores ----------------
         const int g4 = 4 * g;
