@@ -75,19 +75,19 @@ fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream) {
 template <int MODE, int PATH>
 fp8_status dispatch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream) {
     if constexpr (MODE == fp8k::kDense) {
-        if (p.M <= 64) return launch_gemm<64, 96, 2, 2, MODE, PATH>(p, cus, stream);
+        if (p.M <= 64) return launch_gemm<64, 96, 2, 2, MODE, PATH, 3>(p, cus, stream);
         constexpr bool kF16 = PATH == fp8k::kPathF16 || PATH == fp8k::kPathF16Pow2;
         const int64_t huge = ((p.M + 255) / 256) * ((p.N + 255) / 256);
         if constexpr (!kF16)
             if (huge >= cus) return launch_gemm<256, 256, 2, 4, MODE, PATH>(p, cus, stream);
         const int64_t big = ((p.M + 255) / 256) * ((p.N + 127) / 128);
-        if (big >= 2 * cus || (kF16 && huge >= cus)) return launch_gemm<256, 128, 4, 2, MODE, PATH>(p, cus, stream);
-        return launch_gemm<128, 128, 2, 2, MODE, PATH>(p, cus, stream);
+        if (big >= 2 * cus || (kF16 && huge >= cus)) return launch_gemm<256, 128, 4, 2, MODE, PATH, 3>(p, cus, stream);
+        return launch_gemm<128, 128, 2, 2, MODE, PATH, 4>(p, cus, stream);
     } else if constexpr (MODE == fp8k::kContiguous) {
         // The M tile must equal the layout alignment (128): one expert per tile.
-        return launch_gemm<128, 256, 2, 4, MODE, PATH>(p, cus, stream);
+        return launch_gemm<128, 256, 2, 4, MODE, PATH, 3>(p, cus, stream);
     } else {
-        return launch_gemm<256, 128, 4, 2, MODE, PATH>(p, cus, stream);
+        return launch_gemm<256, 128, 4, 2, MODE, PATH, 3>(p, cus, stream);
     }
 }
 

@@ -451,7 +451,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         //   * the loads of block kb+2 are spread over the FI rows that follow
         //     the barrier of block kb;
         //   * row g's partials are promoted during row g+1.
-        static_assert(STAGES == 2 && FI >= 2, "two-stage pipeline over at least two subtile rows");
+        static_assert(STAGES >= 2 && FI >= 2, "pipeline of at least two stages over at least two subtile rows");
         constexpr int RB = FI - 2;   // row before which the barrier of a block sits
         auto read_x = [&](int buf, int i) { return lds_frag(smem + buf * BM * 128 + 2048 * i, xa[0], xa[1]); };
         // (wa already holds the W region's base)
@@ -466,13 +466,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                 else v[j] = *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + sb_slot[j]);
             }
         };
-        // the loads of a block go out at window positions 0 .. FI-1
+        // The loads of a block go out over the first WIN of the FI rows that
+        // follow the barrier which frees their buffer (window positions
+        // 0 .. WIN-1); the remaining rows before the next barrier leave time
+        // for the last ones to land (measured: 3/4 of the rows is best).
+        constexpr int WIN = FI >= 4 ? (3 * FI) / 4 : FI;
         auto issue_window = [&](const StageLoads& L, auto posc) {
             constexpr int pos = decltype(posc)::value;
             __builtin_amdgcn_sched_barrier(0x0006);
             static_for<NPIECE>([&](auto pc) {
                 constexpr int P = decltype(pc)::value;
-                if constexpr (P * FI / NPIECE == pos) issue_piece(L, pc);
+                if constexpr (P * WIN / NPIECE == pos) issue_piece(L, pc);
             });
             __builtin_amdgcn_sched_barrier(0x0006);
         };
@@ -483,8 +487,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 #pragma unroll
             for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // Prologue: block 0 in full, then the first two window positions of
-        // block 1, then the reads of block 0 that the pipeline expects.
+        // Prologue: block 0 in full; then blocks 1 .. STAGES-2 in full and the
+        // first two window positions of block STAGES-1; then the reads of
+        // block 0 that the pipeline expects.
         wait_vmcnt<0>();
         lds_barrier();   // all waves are done with the previous tile's buffers
         {
@@ -493,10 +498,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         }
         wait_vmcnt<0>();
         lds_barrier();
+        static_for<STAGES - 2>([&](auto sc) {
+            constexpr int b = decltype(sc)::value + 1;
+            const StageLoads Lb = stage_loads(b, std::integral_constant<int, b>{});
+            static_for<NPIECE>([&](auto pc) { issue_piece(Lb, pc); });
+        });
         {
-            const StageLoads L1 = stage_loads(1, std::integral_constant<int, 1>{});
-            issue_window(L1, std::integral_constant<int, 0>{});
-            issue_window(L1, std::integral_constant<int, 1>{});
+            const StageLoads Ll = stage_loads(STAGES - 1, std::integral_constant<int, STAGES - 1>{});
+            issue_window(Ll, std::integral_constant<int, 0>{});
+            issue_window(Ll, std::integral_constant<int, 1>{});
         }
         i32x8 wfr[FJ];
 #pragma unroll
@@ -526,12 +536,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         };
 
         auto step = [&](int kb, auto bufc) {
-            constexpr int BUF = decltype(bufc)::value;
-            constexpr int NBUF = 1 - BUF;
-            // loads of block kb+1 (positions 2 .. FI-1 of its window) and of
-            // block kb+2 (positions 0, 1, after the barrier)
-            const StageLoads L1 = stage_loads(kb + 1, std::integral_constant<int, NBUF>{});
-            const StageLoads L2 = stage_loads(kb + 2, std::integral_constant<int, BUF>{});
+            constexpr int BUF = decltype(bufc)::value;           // buffer of block kb
+            constexpr int NBUF = (BUF + 1) % STAGES;             // of block kb+1
+            // loads of block kb+STAGES-1 (window positions 2 .. FI-1, into the
+            // buffer of block kb-1) and of block kb+STAGES (positions 0, 1,
+            // after the barrier, into this block's buffer)
+            const StageLoads L1 =
+                stage_loads(kb + STAGES - 1, std::integral_constant<int, (BUF + STAGES - 1) % STAGES>{});
+            const StageLoads L2 = stage_loads(kb + STAGES, std::integral_constant<int, BUF>{});
             float sb_next[FJ];
             // W fragments widened to FP16 once per block on the precise path
             f16x8 wh[kF16 ? FJ : 1][4];
@@ -551,9 +563,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (i == RB) {
                     // every read of block kb is done (lgkm) and this wave's
-                    // loads of block kb+1 have landed (vm); then publish
+                    // loads of block kb+1 have landed (vm: only those of blocks
+                    // kb+2 .. kb+STAGES-1 may still fly); then publish
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    wait_vmcnt<0>();
+                    wait_vmcnt<(STAGES - 2) * NPIECE>();
                     lds_barrier();
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -636,13 +649,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                 sb_cur[j] = sb_next[j];
             }
         };
-        // K loop unrolled by the two buffers (straight-line body), then the tail.
+        // K loop unrolled by the ring of buffers (straight-line body), then the tail.
         int kb = 0;
-        for (; kb + 2 <= KB; kb += 2) {
-            step(kb, std::integral_constant<int, 0>{});
-            step(kb + 1, std::integral_constant<int, 1>{});
-        }
-        if (kb < KB) step(kb, std::integral_constant<int, 0>{});
+        for (; kb + STAGES <= KB; kb += STAGES)
+            static_for<STAGES>([&](auto sc) { step(kb + decltype(sc)::value, sc); });
+        static_for<STAGES - 1>([&](auto sc) {
+            if (kb + decltype(sc)::value < KB) step(kb + decltype(sc)::value, sc);
+        });
         // drain: the last row's partials
         if constexpr (PATH != kPathFp8Pow2) promote(FI - 1, sb_prev);
         // the loads issued past the last block were discarded; let them retire
