@@ -78,8 +78,18 @@ fp8_status dispatch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream)
         if (p.M <= 64) return launch_gemm<64, 96, 2, 2, MODE, PATH, 3>(p, cus, stream);
         constexpr bool kF16 = PATH == fp8k::kPathF16 || PATH == fp8k::kPathF16Pow2;
         const int64_t huge = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-        if constexpr (!kF16)
-            if (huge >= cus) return launch_gemm<256, 256, 2, 4, MODE, PATH>(p, cus, stream);
+        if constexpr (!kF16) {
+            if (huge >= cus) {
+                // 256x224 when it takes fewer waves' worth of tile area (e.g.
+                // N = 7168: 32 tiles of 224 per row fill two whole waves where
+                // 28 tiles of 256 leave the second one a quarter empty)
+                const int64_t t224 = ((p.M + 255) / 256) * ((p.N + 223) / 224);
+                const int64_t cost256 = ((huge + cus - 1) / cus) * 256;
+                const int64_t cost224 = ((t224 + cus - 1) / cus) * 224;
+                if (cost224 < cost256) return launch_gemm<256, 224, 4, 2, MODE, PATH>(p, cus, stream);
+                return launch_gemm<256, 256, 2, 4, MODE, PATH>(p, cus, stream);
+            }
+        }
         const int64_t big = ((p.M + 255) / 256) * ((p.N + 127) / 128);
         if (big >= 2 * cus || (kF16 && huge >= cus)) return launch_gemm<256, 128, 4, 2, MODE, PATH, 3>(p, cus, stream);
         return launch_gemm<128, 128, 2, 2, MODE, PATH, 4>(p, cus, stream);
@@ -135,16 +145,17 @@ fp8_status fp8_quant_1x128(const float* x, int64_t M, int64_t K, uint8_t* xq, fl
     int cus = 0;
     fp8_status st = current_device_cus(&cus);
     if (st != FP8_OK) return st;
-    const int64_t groups = M * (K / 128);
-    const int64_t blocks = (groups + 7) / 8;
+    // one wave per row segment of up to 8 groups, 4 waves per block
+    const int64_t units = M * ((K / 128 + 7) / 8);
+    const int64_t blocks = (units + 3) / 4;
     if (blocks > 0x7FFFFFFF) return FP8_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
     if (flags & FP8_FLAG_UE8M0)
         hipLaunchKernelGGL(fp8k::quant_1x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s,
-                           x, xq, sa, M, K, groups);
+                           x, xq, sa, M, K, units);
     else
         hipLaunchKernelGGL(fp8k::quant_1x128_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s,
-                           x, xq, sa, M, K, groups);
+                           x, xq, sa, M, K, units);
     return launch_status();
 }
 

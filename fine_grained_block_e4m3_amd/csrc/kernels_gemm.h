@@ -226,7 +226,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     constexpr int FI = TM / 16;        // 16x16 subtiles per wave along m
     constexpr int FJ = TN / 16;        // ... along n
     constexpr int XLOADS = BM / 8 / NWAVES;   // 1 KB direct-to-LDS loads per wave per stage
-    constexpr int WLOADS = BN / 8 / NWAVES;
+    // W rows come in 8-row groups; when they do not split evenly over the
+    // waves, the last waves' loads fall past the tile (the range check reads
+    // zeros) and land in a spare LDS area, so every wave issues as many.
+    constexpr int WGROUPS = BN / 8;
+    constexpr int WLOADS = (WGROUPS + NWAVES - 1) / NWAVES;
+    constexpr int W_WAVES = WGROUPS / WLOADS;   // waves loading rows of the tile
     constexpr int NPIECE = XLOADS + WLOADS + 1;   // loads per wave per stage
     constexpr int PER_STAGE = NPIECE;
     // Scales of a stage: waves 0 .. NSA-1 load the activation scales of the
@@ -239,17 +244,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     // the ds_read immediate.
     constexpr int W_BASE = STAGES * BM * 128;
     constexpr int SC_BASE = W_BASE + STAGES * BN * 128;
-    constexpr int LDS_BYTES = SC_BASE + STAGES * NWAVES * 256;
+    constexpr int SPARE_BASE = SC_BASE + STAGES * NWAVES * 256;
+    constexpr int LDS_BYTES = SPARE_BASE + (W_WAVES < NWAVES ? WLOADS * 1024 : 0);
     // A wave's 16-wide n subtiles all lie in one 128-row weight block when its
     // n range is 128-aligned inside a 128-aligned tile: one sB per K block.
     constexpr bool kUniformSb = (BN % 128 == 0 || 128 % BN == 0) && (128 % TN == 0 || TN % 128 == 0)
                                 && TN <= 128;
+    // Stream the W subtiles (hold X) when a wave has more of them: the
+    // resident operand's fragments stay in registers for a whole K block.
+    constexpr bool kStreamW = FJ > FI && TM >= 64;
     constexpr bool kF16 = PATH == kPathF16 || PATH == kPathF16Pow2;
     constexpr bool kPow2 = PATH == kPathFp8Pow2 || PATH == kPathF16Pow2;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 subtiles");
     static_assert(BM % 64 == 0 && NSA < NWAVES, "activation scales: 64 rows per wave, one wave left for sB");
     static_assert(BN / 128 + 2 <= 64, "one scale load covers the tile's weight blocks");
-    static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "tile rows per wave");
+    static_assert(BM % (8 * NWAVES) == 0 && BN % 8 == 0 && WGROUPS % WLOADS == 0, "tile rows per wave");
     static_assert(XLOADS >= 1 && XLOADS <= 4 && WLOADS >= 1 && WLOADS <= 4, "loads per wave");
     static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS holds the stage ring");
     static_assert((STAGES - 2) * PER_STAGE <= 63, "vmcnt range");
@@ -317,6 +326,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     const bool sa_wave = wave < NSA;
     const uint32_t sc_voff = sa_wave ? (uint32_t)(4 * (64 * wave + lane)) : (uint32_t)(4 * lane * KB);
     const uint32_t lds0 = uniform((int)lds_addr(smem));
+    // LDS destination of this wave's W loads: its rows in stage s at
+    // w_dst + s*w_sstride, or the spare area (every stage) for a wave past them
+    const bool w_wave = W_WAVES == NWAVES || wave < W_WAVES;
+    const uint32_t w_dst = w_wave ? (uint32_t)(W_BASE + wave * WLOADS * 1024) : (uint32_t)SPARE_BASE;
+    const uint32_t w_sstride = w_wave ? (uint32_t)(BN * 128) : 0u;
 
     // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs,
     // so workgroup b of a wave of G lands on XCD b%8.  Give each XCD a run of
@@ -417,7 +431,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             const int live = -(int)(kb < KB);
             StageLoads L;
             L.xm0 = lds0 + s * BM * 128 + (uint32_t)(wave * XLOADS * 1024);
-            L.wm0 = lds0 + W_BASE + s * BN * 128 + (uint32_t)(wave * WLOADS * 1024);
+            L.wm0 = lds0 + w_dst + s * w_sstride;
             L.sm0 = lds0 + SC_BASE + s * NWAVES * 256 + (uint32_t)(wave * 256);
             L.xr = xr;
             L.wr = wr;
@@ -439,38 +453,61 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         };
 
         // ---------------- K loop ----------------
-        // One software pipeline over the tile's subtile rows, global row
-        // g = kb*FI + i, across K blocks:
-        //   * the X fragment and sA of row g are read at row g-2;
-        //   * the barrier of block kb sits just before row FI-2 of block kb:
+        // One operand is held in registers for a whole K block (C resident
+        // fragments); the other streams through one 16-row subtile at a time
+        // (R rows per block).  The operand with fewer subtiles per wave is the
+        // resident one, which keeps the fragment registers low.  One software
+        // pipeline runs over the streamed rows, global row g = kb*R + r,
+        // across K blocks:
+        //   * the fragment and scale of row g are read at row g-2;
+        //   * the barrier of block kb sits just before row R-2 of block kb:
         //     by then every wave has finished its reads of block kb and its
         //     loads of block kb+1 have landed; after it, block kb's buffer
-        //     takes the loads of block kb+2 and block kb+1 may be read;
-        //   * the W fragments and sB of block kb+1 are read during the last
-        //     row of block kb, each W fragment right after its last MFMA;
-        //   * the loads of block kb+2 are spread over the FI rows that follow
-        //     the barrier of block kb;
+        //     takes the loads of block kb+STAGES and block kb+1 may be read;
+        //   * the resident fragments and scales of block kb+1 are read during
+        //     the last row of block kb, each fragment right after its last MFMA;
+        //   * the loads of the blocks ahead are spread over the rows;
         //   * row g's partials are promoted during row g+1.
-        static_assert(STAGES >= 2 && FI >= 2, "pipeline of at least two stages over at least two subtile rows");
-        constexpr int RB = FI - 2;   // row before which the barrier of a block sits
+        // Promotion scale of a subtile: the streamed row's scale times the
+        // resident fragment's scale (sA x sB in either orientation).
+        constexpr int R = kStreamW ? FJ : FI;   // streamed rows per K block
+        constexpr int C = kStreamW ? FI : FJ;   // resident fragments
+        static_assert(STAGES >= 2 && R >= 2, "pipeline of at least two stages over at least two subtile rows");
+        constexpr int RB = R - 2;   // row before which the barrier of a block sits
         auto read_x = [&](int buf, int i) { return lds_frag(smem + buf * BM * 128 + 2048 * i, xa[0], xa[1]); };
         // (wa already holds the W region's base)
         auto read_w = [&](int buf, int j) { return lds_frag(smem + buf * BN * 128 + 2048 * j, wa[0], wa[1]); };
         auto read_sa = [&](int buf, int i) {
             return *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + saa + 64 * i);
         };
-        auto read_sb = [&](int buf, float (&v)[FJ]) {
+        auto read_sb = [&](int buf, int j) {
+            return *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + sb_slot[j]);
+        };
+        auto read_row = [&](int buf, int r) {
+            if constexpr (kStreamW) return read_w(buf, r);
+            else return read_x(buf, r);
+        };
+        auto read_row_scale = [&](int buf, int r) {
+            if constexpr (kStreamW) return read_sb(buf, r);
+            else return read_sa(buf, r);
+        };
+        auto read_res = [&](int buf, int c) {
+            if constexpr (kStreamW) return read_x(buf, c);
+            else return read_w(buf, c);
+        };
+        auto read_res_scales = [&](int buf, float (&v)[C]) {
 #pragma unroll
-            for (int j = 0; j < FJ; ++j) {
-                if (kUniformSb && j > 0) v[j] = v[0];
-                else v[j] = *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + sb_slot[j]);
+            for (int c = 0; c < C; ++c) {
+                if constexpr (kStreamW) v[c] = read_sa(buf, c);
+                else if (kUniformSb && c > 0) v[c] = v[0];
+                else v[c] = read_sb(buf, c);
             }
         };
-        // The loads of a block go out over the first WIN of the FI rows that
+        // The loads of a block go out over the first WIN of the R rows that
         // follow the barrier which frees their buffer (window positions
         // 0 .. WIN-1); the remaining rows before the next barrier leave time
         // for the last ones to land (measured: 3/4 of the rows is best).
-        constexpr int WIN = FI >= 4 ? (3 * FI) / 4 : FI;
+        constexpr int WIN = R >= 4 ? (3 * R) / 4 : R;
         auto issue_window = [&](const StageLoads& L, auto posc) {
             constexpr int pos = decltype(posc)::value;
             __builtin_amdgcn_sched_barrier(0x0006);
@@ -486,6 +523,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         for (int i = 0; i < FI; ++i)
 #pragma unroll
             for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // accumulator of streamed row r, resident fragment c
+        auto accr = [&](int r, int c) -> f32x4& {
+            if constexpr (kStreamW) return acc[c][r];
+            else return acc[r][c];
+        };
 
         // Prologue: block 0 in full; then blocks 1 .. STAGES-2 in full and the
         // first two window positions of block STAGES-1; then the reads of
@@ -508,60 +550,62 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             issue_window(Ll, std::integral_constant<int, 0>{});
             issue_window(Ll, std::integral_constant<int, 1>{});
         }
-        i32x8 wfr[FJ];
+        i32x8 res[C];
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) wfr[j] = read_w(0, j);
-        float sb_cur[FJ], sb_prev[FJ];
-        read_sb(0, sb_cur);
+        for (int c = 0; c < C; ++c) res[c] = read_res(0, c);
+        float rs_cur[C], rs_prev[C];
+        read_res_scales(0, rs_cur);
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) sb_prev[j] = 0.f;
-        // X fragments and sA of the next two rows (g, g+1)
-        i32x8 xr0 = read_x(0, 0), xr1 = read_x(0, 1);
-        float sr0 = read_sa(0, 0), sr1 = read_sa(0, 1);
+        for (int c = 0; c < C; ++c) rs_prev[c] = 0.f;
+        // fragments and scales of the next two streamed rows (g, g+1)
+        i32x8 fr0 = read_row(0, 0), fr1 = read_row(0, 1);
+        float sr0 = read_row_scale(0, 0), sr1 = read_row_scale(0, 1);
         // the partials of the row before (none yet: zeros promote to nothing)
-        f32x4 prev[FJ];
+        f32x4 prev[C];
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) prev[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float sa_prev = 0.f;
+        for (int c = 0; c < C; ++c) prev[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float st_prev = 0.f;
 
-        // promotion of the previous row (partials prev, row ip of acc)
-        auto promote = [&](int ip, const float (&sbv)[FJ]) {
-            const float sav = kPow2 ? pow2_part(sa_prev) : sa_prev;
+        // promotion of the previous row (partials prev, row rp of the block
+        // whose resident scales are rsv)
+        auto promote = [&](int rp, const float (&rsv)[C]) {
+            const float stv = kPow2 ? pow2_part(st_prev) : st_prev;
 #pragma unroll
-            for (int j = 0; j < FJ; ++j) {
-                const float sc = sav * (kPow2 ? pow2_part(sbv[j]) : sbv[j]);
+            for (int c = 0; c < C; ++c) {
+                const float sc = stv * (kPow2 ? pow2_part(rsv[c]) : rsv[c]);
 #pragma unroll
-                for (int r2 = 0; r2 < 4; ++r2) acc[ip][j][r2] = fmaf(sc, prev[j][r2], acc[ip][j][r2]);
+                for (int r2 = 0; r2 < 4; ++r2) accr(rp, c)[r2] = fmaf(sc, prev[c][r2], accr(rp, c)[r2]);
             }
         };
 
         auto step = [&](int kb, auto bufc) {
             constexpr int BUF = decltype(bufc)::value;           // buffer of block kb
             constexpr int NBUF = (BUF + 1) % STAGES;             // of block kb+1
-            // loads of block kb+STAGES-1 (window positions 2 .. FI-1, into the
+            // loads of block kb+STAGES-1 (window positions 2 .. R-1, into the
             // buffer of block kb-1) and of block kb+STAGES (positions 0, 1,
             // after the barrier, into this block's buffer)
             const StageLoads L1 =
                 stage_loads(kb + STAGES - 1, std::integral_constant<int, (BUF + STAGES - 1) % STAGES>{});
             const StageLoads L2 = stage_loads(kb + STAGES, std::integral_constant<int, BUF>{});
-            float sb_next[FJ];
-            // W fragments widened to FP16 once per block on the precise path
-            f16x8 wh[kF16 ? FJ : 1][4];
+            float rs_next[C];
+            // resident fragments widened to FP16 once per block on the precise path
+            f16x8 resh[kF16 ? C : 1][4];
             if constexpr (kF16) {
 #pragma unroll
-                for (int j = 0; j < FJ; ++j)
+                for (int c = 0; c < C; ++c)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) wh[j][q] = e4m3x8_to_f16(wfr[j][2 * q], wfr[j][2 * q + 1]);
+                    for (int q = 0; q < 4; ++q) resh[c][q] = e4m3x8_to_f16(res[c][2 * q], res[c][2 * q + 1]);
             }
-            int sbe[FJ];
+            // E8M0 exponents of the resident scales (scaled-MFMA path)
+            int rse[C];
             if constexpr (PATH == kPathFp8Pow2) {
 #pragma unroll
-                for (int j = 0; j < FJ; ++j) sbe[j] = e8m0_of(sb_cur[j]);
+                for (int c = 0; c < C; ++c) rse[c] = e8m0_of(rs_cur[c]);
             }
-            static_for<FI>([&](auto ic) {
-                constexpr int i = decltype(ic)::value;
+            static_for<R>([&](auto rc) {
+                constexpr int r = decltype(rc)::value;
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (i == RB) {
+                if constexpr (r == RB) {
                     // every read of block kb is done (lgkm) and this wave's
                     // loads of block kb+1 have landed (vm: only those of blocks
                     // kb+2 .. kb+STAGES-1 may still fly); then publish
@@ -570,83 +614,98 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                     lds_barrier();
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                const i32x8 xc = xr0;
-                const float sa_c = sr0;
+                const i32x8 fc = fr0;
+                const float st_c = sr0;
                 // reads two rows ahead: this block, or the next one after the barrier
-                i32x8 xn;
+                i32x8 fn;
                 float sn;
-                if constexpr (i + 2 < FI) {
-                    xn = read_x(BUF, i + 2);
-                    sn = read_sa(BUF, i + 2);
+                if constexpr (r + 2 < R) {
+                    fn = read_row(BUF, r + 2);
+                    sn = read_row_scale(BUF, r + 2);
                 } else {
-                    xn = read_x(NBUF, i + 2 - FI);
-                    sn = read_sa(NBUF, i + 2 - FI);
+                    fn = read_row(NBUF, r + 2 - R);
+                    sn = read_row_scale(NBUF, r + 2 - R);
                 }
-                xr0 = xr1;
-                xr1 = xn;
+                fr0 = fr1;
+                fr1 = fn;
                 sr0 = sr1;
                 sr1 = sn;
-                if constexpr (i == FI - 1) read_sb(NBUF, sb_next);
+                if constexpr (r == R - 1) read_res_scales(NBUF, rs_next);
                 // loads of the blocks ahead
-                if constexpr (i < RB) issue_window(L1, std::integral_constant<int, i + 2>{});
-                else issue_window(L2, std::integral_constant<int, i - RB>{});
+                if constexpr (r < RB) issue_window(L1, std::integral_constant<int, r + 2>{});
+                else issue_window(L2, std::integral_constant<int, r - RB>{});
 
                 if constexpr (PATH == kPathFp8Pow2) {
-                    const int sae = e8m0_of(sa_c);
+                    const int ste = e8m0_of(st_c);
 #pragma unroll
-                    for (int j = 0; j < FJ; ++j) {
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            wfr[j], xc, acc[i][j], 0, 0, 0, sbe[j], 0, sae);
-                        if constexpr (i == FI - 1) wfr[j] = read_w(NBUF, j);
+                    for (int c = 0; c < C; ++c) {
+                        // operand A is the W fragment, B the X fragment
+                        if constexpr (kStreamW)
+                            accr(r, c) = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                fc, res[c], accr(r, c), 0, 0, 0, ste, 0, rse[c]);
+                        else
+                            accr(r, c) = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                res[c], fc, accr(r, c), 0, 0, 0, rse[c], 0, ste);
+                        if constexpr (r == R - 1) res[c] = read_res(NBUF, c);
                     }
                 } else {
-                    f32x4 cur[FJ];
+                    f32x4 cur[C];
                     if constexpr (kF16) {
-                        f16x8 xh[4];
+                        f16x8 fh[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) xh[q] = e4m3x8_to_f16(xc[2 * q], xc[2 * q + 1]);
+                        for (int q = 0; q < 4; ++q) fh[q] = e4m3x8_to_f16(fc[2 * q], fc[2 * q + 1]);
 #pragma unroll
-                        for (int j = 0; j < FJ; ++j) {
-                            cur[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[j][0], xh[0],
-                                                                            f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        for (int c = 0; c < C; ++c) {
+                            cur[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                            for (int q = 1; q < 4; ++q)
-                                cur[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[j][q], xh[q], cur[j], 0, 0, 0);
+                            for (int q = 0; q < 4; ++q) {
+                                if constexpr (kStreamW)
+                                    cur[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fh[q], resh[c][q], cur[c], 0, 0, 0);
+                                else
+                                    cur[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(resh[c][q], fh[q], cur[c], 0, 0, 0);
+                            }
                         }
-                        if constexpr (i == FI - 1) {
+                        if constexpr (r == R - 1) {
 #pragma unroll
-                            for (int j = 0; j < FJ; ++j) wfr[j] = read_w(NBUF, j);
+                            for (int c = 0; c < C; ++c) res[c] = read_res(NBUF, c);
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     } else {
 #pragma unroll
-                        for (int j = 0; j < FJ; ++j) {
-                            cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                wfr[j], xc, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                            if constexpr (i == FI - 1) wfr[j] = read_w(NBUF, j);
+                        for (int c = 0; c < C; ++c) {
+                            if constexpr (kStreamW)
+                                cur[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    fc, res[c], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                            else
+                                cur[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    res[c], fc, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                            if constexpr (r == R - 1) res[c] = read_res(NBUF, c);
                         }
                     }
-                    // the previous row: row i-1 of this block, or the last
-                    // row of the previous block (with that block's sB)
-                    if constexpr (i == 0) promote(FI - 1, sb_prev);
-                    else promote(i - 1, sb_cur);
+                    // the previous row: row r-1 of this block, or the last
+                    // row of the previous block (with that block's scales)
+                    if constexpr (r == 0) promote(R - 1, rs_prev);
+                    else promote(r - 1, rs_cur);
 #pragma unroll
-                    for (int j = 0; j < FJ; ++j) prev[j] = cur[j];
-                    sa_prev = sa_c;
+                    for (int c = 0; c < C; ++c) prev[c] = cur[c];
+                    st_prev = st_c;
                     if constexpr (!kF16) {
-                        // each MFMA of this row followed by four promotion FMAs
-                        static_for<FJ>([&](auto qc) {
+                        // each MFMA of this row preceded by the promotion FMAs of
+                        // the subtile whose partials its result replaces (and the
+                        // scale products)
+                        static_for<C>([&](auto qc) {
+                            constexpr int n = decltype(qc)::value == 0 || kStreamW ? 5 : 4;
+                            __builtin_amdgcn_sched_group_barrier(0x002, n, 0);
                             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                            __builtin_amdgcn_sched_group_barrier(0x002, decltype(qc)::value == 0 ? 5 : 4, 0);
                         });
                     }
                 }
             });
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < FJ; ++j) {
-                sb_prev[j] = sb_cur[j];
-                sb_cur[j] = sb_next[j];
+            for (int c = 0; c < C; ++c) {
+                rs_prev[c] = rs_cur[c];
+                rs_cur[c] = rs_next[c];
             }
         };
         // K loop unrolled by the ring of buffers (straight-line body), then the tail.
@@ -657,7 +716,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             if (kb + decltype(sc)::value < KB) step(kb + decltype(sc)::value, sc);
         });
         // drain: the last row's partials
-        if constexpr (PATH != kPathFp8Pow2) promote(FI - 1, sb_prev);
+        if constexpr (PATH != kPathFp8Pow2) promote(R - 1, rs_prev);
         // the loads issued past the last block were discarded; let them retire
         wait_vmcnt<0>();
 

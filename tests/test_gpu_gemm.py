@@ -184,6 +184,30 @@ def test_huge_tile_instance_ragged_sampled(ue8m0):
     assert_close_or_bounded(y[mi, ni], ref, bound, "256x256 tiles, ragged edges")
 
 
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_224_wide_tile_instance_ragged_sampled(ue8m0):
+    """Shapes that fill whole waves with 256x224 tiles but not with 256x256
+    ones take the 256x224 instance, which holds X in registers and streams the
+    W subtiles: here 10 x 32 tiles, the last n tile holding 106 columns that
+    straddle two weight blocks, a ragged last m tile and an odd number of K
+    blocks; every row and column of the ragged edges is checked."""
+    M, N, K = 2500, 7050, 640
+    flags = oracle.FLAG_UE8M0 if ue8m0 else 0
+    wl = workloads.dense(M, N, K, seed=17, outlier_frac=0.001, outlier_mult=100.0)
+    xq, sa = oracle.quant_1x128(wl.x, flags)
+    wq, sb = oracle.quant_128x128(wl.w, flags)
+    y = run_gemm(xq, sa, wq, sb, ue8m0=ue8m0)
+    rng = np.random.default_rng(5)
+    mi, ni = rng.integers(0, M, 20000), rng.integers(0, N, 20000)
+    edge_m, edge_n = np.arange(2304, M), np.arange(6944, N)
+    mi = np.concatenate([mi, np.repeat(edge_m, 16), rng.integers(0, M, 16 * len(edge_n)), np.full(N, M - 1)])
+    ni = np.concatenate([ni, rng.integers(0, N, 16 * len(edge_m)), np.repeat(edge_n, 16), np.arange(N)])
+    ref = oracle.gemm_nt_elems(xq, sa, wq, sb, mi, ni, flags)
+    bound = fp8_mfma_error_bound(xq, sa, wq, sb, np.zeros((M, N)), pow2=ue8m0)[mi, ni] \
+        + 2.0 ** -8 * np.abs(ref)
+    assert_close_or_bounded(y[mi, ni], ref, bound, "256x224 tiles, ragged edges")
+
+
 @pytest.mark.parametrize("precise", PATHS)
 def test_deterministic_repeats(precise):
     wl = workloads.dense(300, 512, 1024, seed=77, outlier_frac=0.01, outlier_mult=50.0)

@@ -24,7 +24,9 @@ def _q2(w, flags):
 
 
 @pytest.mark.parametrize("M,K,flags", [(128, 512, 0), (1, 128, 0), (300, 1024, 0),
-                                       (77, 384, 1), (128, 512, 1), (9, 7168, 0)])
+                                       (77, 384, 1), (128, 512, 1), (9, 7168, 0),
+                                       # a row of 8-group units plus a short one
+                                       (33, 1280, 0), (5, 1664, 1)])
 def test_quant_1x128_bitexact(M, K, flags):
     wl = workloads.dense(M, 1, K, seed=100 + M, outlier_frac=0.01, outlier_mult=50.0)
     xq_ref, sa_ref = oracle.quant_1x128(wl.x, flags)
