@@ -253,6 +253,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     // Stream the W subtiles (hold X) when a wave has more of them: the
     // resident operand's fragments stay in registers for a whole K block.
     constexpr bool kStreamW = FJ > FI && TM >= 64;
+    // With W streamed and FP32 scales, a wave's TN <= 128 columns lie in at
+    // most two weight blocks: the K loop is specialised on the subtile where
+    // the second one starts, so that the promotion scales are two products
+    // per resident fragment and block instead of one per subtile.
+    constexpr bool kSplitSb = kStreamW && TN <= 128 && PATH != kPathFp8Pow2;
     constexpr bool kF16 = PATH == kPathF16 || PATH == kPathF16Pow2;
     constexpr bool kPow2 = PATH == kPathFp8Pow2 || PATH == kPathF16Pow2;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 subtiles");
@@ -413,6 +418,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             const int64_t n = n0 + wn * TN + 16 * j;
             sb_slot[j] = (uint32_t)(SC_BASE + 256 * NSA + 4 * ((int)((n < N ? n : N - 1) >> 7) - nb0));
         }
+        // split scales: subtiles 0 .. jb-1 of this wave lie in the weight block
+        // of slot sb_slot[0], the others in the next one (for a wave past N
+        // both slots hold a loaded scale or zero, and its columns are not stored)
+        int jb = FJ;
+        if constexpr (kSplitSb) {
+            const int nw = (int)((n0 + wn * TN) & 127);
+            jb = nw == 0 ? FJ : min(FJ, (128 - nw) / 16);
+        }
 
         // Issue the loads of K block kb into stage s.  Past the last block the
         // resources get an empty range, so the loads are discarded by the
@@ -488,8 +501,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             else return read_x(buf, r);
         };
         auto read_row_scale = [&](int buf, int r) {
-            if constexpr (kStreamW) return read_sb(buf, r);
+            if constexpr (kSplitSb) return 0.f;   // the block's two products serve every row
+            else if constexpr (kStreamW) return read_sb(buf, r);
             else return read_sa(buf, r);
+        };
+        // split scales: the two weight-block scales of this wave
+        auto read_sb2 = [&](int buf, float (&v)[2]) {
+            v[0] = *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + sb_slot[0]);
+            v[1] = *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + sb_slot[0] + 4);
         };
         auto read_res = [&](int buf, int c) {
             if constexpr (kStreamW) return read_x(buf, c);
@@ -529,6 +548,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             else return acc[r][c];
         };
 
+        // The K loop, specialised on JB: with split scales, the streamed rows
+        // 0 .. JB-1 take the first weight block's products (JB = 0 otherwise).
+        auto kloop = [&](auto jbc) {
+        constexpr int JB = decltype(jbc)::value;
         // Prologue: block 0 in full; then blocks 1 .. STAGES-2 in full and the
         // first two window positions of block STAGES-1; then the reads of
         // block 0 that the pipeline expects.
@@ -565,6 +588,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 #pragma unroll
         for (int c = 0; c < C; ++c) prev[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         float st_prev = 0.f;
+        // split scales: this block's weight-block scales, the products
+        // sA(c) x sB(first / second block), and the products of the previous
+        // block's last row
+        float sb2_cur[2], pr[2][C], plast[C];
+        if constexpr (kSplitSb) {
+            read_sb2(0, sb2_cur);
+#pragma unroll
+            for (int c = 0; c < C; ++c) plast[c] = 0.f;
+        }
+        auto promote_p = [&](int rp, const float (&pv)[C]) {
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) accr(rp, c)[r2] = fmaf(pv[c], prev[c][r2], accr(rp, c)[r2]);
+        };
 
         // promotion of the previous row (partials prev, row rp of the block
         // whose resident scales are rsv)
@@ -587,7 +625,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             const StageLoads L1 =
                 stage_loads(kb + STAGES - 1, std::integral_constant<int, (BUF + STAGES - 1) % STAGES>{});
             const StageLoads L2 = stage_loads(kb + STAGES, std::integral_constant<int, BUF>{});
-            float rs_next[C];
+            float rs_next[C], sb2_next[2];
             // resident fragments widened to FP16 once per block on the precise path
             f16x8 resh[kF16 ? C : 1][4];
             if constexpr (kF16) {
@@ -630,7 +668,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                 fr1 = fn;
                 sr0 = sr1;
                 sr1 = sn;
-                if constexpr (r == R - 1) read_res_scales(NBUF, rs_next);
+                if constexpr (r == R - 1) {
+                    read_res_scales(NBUF, rs_next);
+                    if constexpr (kSplitSb) read_sb2(NBUF, sb2_next);
+                }
                 // loads of the blocks ahead
                 if constexpr (r < RB) issue_window(L1, std::integral_constant<int, r + 2>{});
                 else issue_window(L2, std::integral_constant<int, r - RB>{});
@@ -684,8 +725,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                     }
                     // the previous row: row r-1 of this block, or the last
                     // row of the previous block (with that block's scales)
-                    if constexpr (r == 0) promote(R - 1, rs_prev);
-                    else promote(r - 1, rs_cur);
+                    if constexpr (kSplitSb) {
+                        // this block's products, formed once its scales have
+                        // surely arrived (read during the previous block's last row)
+                        if constexpr (r == 1) {
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                                for (int c = 0; c < C; ++c)
+                                    pr[h][c] = (kPow2 ? pow2_part(rs_cur[c]) : rs_cur[c]) *
+                                               (kPow2 ? pow2_part(sb2_cur[h]) : sb2_cur[h]);
+                        }
+                        if constexpr (r == 0) promote_p(R - 1, plast);
+                        else promote_p(r - 1, pr[r - 1 < JB ? 0 : 1]);
+                    } else {
+                        if constexpr (r == 0) promote(R - 1, rs_prev);
+                        else promote(r - 1, rs_cur);
+                    }
 #pragma unroll
                     for (int c = 0; c < C; ++c) prev[c] = cur[c];
                     st_prev = st_c;
@@ -694,7 +750,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                         // the subtile whose partials its result replaces (and the
                         // scale products)
                         static_for<C>([&](auto qc) {
-                            constexpr int n = decltype(qc)::value == 0 || kStreamW ? 5 : 4;
+                            constexpr int n = kSplitSb ? 4 : (decltype(qc)::value == 0 || kStreamW ? 5 : 4);
                             __builtin_amdgcn_sched_group_barrier(0x002, n, 0);
                             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                         });
@@ -707,6 +763,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                 rs_prev[c] = rs_cur[c];
                 rs_cur[c] = rs_next[c];
             }
+            if constexpr (kSplitSb) {
+#pragma unroll
+                for (int c = 0; c < C; ++c) plast[c] = pr[R - 1 < JB ? 0 : 1][c];
+                sb2_cur[0] = sb2_next[0];
+                sb2_cur[1] = sb2_next[1];
+            }
         };
         // K loop unrolled by the ring of buffers (straight-line body), then the tail.
         int kb = 0;
@@ -716,7 +778,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             if (kb + decltype(sc)::value < KB) step(kb + decltype(sc)::value, sc);
         });
         // drain: the last row's partials
-        if constexpr (PATH != kPathFp8Pow2) promote(R - 1, rs_prev);
+        if constexpr (kSplitSb) promote_p(R - 1, plast);
+        else if constexpr (PATH != kPathFp8Pow2) promote(R - 1, rs_prev);
+        };
+        if constexpr (kSplitSb) {
+            // one copy of the loop per boundary position (wave-uniform)
+            static_for<FJ>([&](auto jc) {
+                if (jb == decltype(jc)::value + 1) kloop(std::integral_constant<int, decltype(jc)::value + 1>{});
+            });
+        } else {
+            kloop(std::integral_constant<int, 0>{});
+        }
         // the loads issued past the last block were discarded; let them retire
         wait_vmcnt<0>();
 
