@@ -22,6 +22,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 FLAG_UE8M0 = 1
 GROUP = 128
+MX_GROUP = 32
 
 
 def build(force: bool = False) -> str:
@@ -69,10 +70,14 @@ def lib():
         L.oracle_contiguous_layout_violations.restype = I64
         L.oracle_grouped_masked.argtypes = [P, P, P, P, P, ctypes.c_int32, I64,
                                             I64, I64, U32, P, P]
+        L.oracle_quant_mx.argtypes = [P, I64, I64, P, P]
+        L.oracle_gemm_mx.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.oracle_gemm_mx_elems.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P]
         L.oracle_num_threads.restype = ctypes.c_int
         for fn in ("oracle_quant_1x128", "oracle_quant_128x128", "oracle_gemm_nt",
                    "oracle_gemm_nt_elems", "oracle_grouped_contiguous",
-                   "oracle_grouped_masked"):
+                   "oracle_grouped_masked", "oracle_quant_mx", "oracle_gemm_mx",
+                   "oracle_gemm_mx_elems"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -192,3 +197,37 @@ def grouped_masked(xq, sa, wq, sb, masked_m, E: int, max_m: int, flags: int = 0)
                                        flags, _p(y), _p(written)),
            "grouped_masked")
     return y, written.astype(bool)
+
+
+def quant_mx(x: np.ndarray):
+    """MXFP8: x fp32 (R, K) -> (q uint8 (R, K), e uint8 (R, K/32)); 2^(e-127) is
+    the scale of each 1x32 group."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R, K = x.shape
+    q = np.empty((R, K), np.uint8)
+    e = np.empty((R, K // MX_GROUP), np.uint8)
+    _check(lib().oracle_quant_mx(_p(x), R, K, _p(q), _p(e)), "quant_mx")
+    return q, e
+
+
+def gemm_mx(xq, ea, wq, eb) -> np.ndarray:
+    """Y (M, N) float64 = MX-scaled X * W^T."""
+    xq, ea, wq, eb = (np.ascontiguousarray(a, dtype=np.uint8) for a in (xq, ea, wq, eb))
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = np.empty((M, N), np.float64)
+    _check(lib().oracle_gemm_mx(_p(xq), _p(ea), _p(wq), _p(eb), M, N, K, _p(y)), "gemm_mx")
+    return y
+
+
+def gemm_mx_elems(xq, ea, wq, eb, m_idx, n_idx) -> np.ndarray:
+    """Y[m_idx[i], n_idx[i]] of the MX GEMM, float64."""
+    xq, ea, wq, eb = (np.ascontiguousarray(a, dtype=np.uint8) for a in (xq, ea, wq, eb))
+    M, K = xq.shape
+    N = wq.shape[0]
+    m_idx = np.ascontiguousarray(m_idx, dtype=np.int64)
+    n_idx = np.ascontiguousarray(n_idx, dtype=np.int64)
+    y = np.empty(m_idx.shape, np.float64)
+    _check(lib().oracle_gemm_mx_elems(_p(xq), _p(ea), _p(wq), _p(eb), M, N, K, _p(m_idx),
+                                      _p(n_idx), m_idx.size, _p(y)), "gemm_mx_elems")
+    return y

@@ -398,3 +398,104 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------ */
+/* MXFP8: E4M3 elements, one E8M0 scale per 1x32 group along K               */
+/* ------------------------------------------------------------------------ */
+
+#define MX_GROUP 32 /* elements per MX scale, along K */
+
+/*
+ * MX quantizer of a row-major (R, K) matrix, activations and weights alike.
+ * tcgen05 page, sections 6.1 and 6.3: in the MX formats every 32 consecutive
+ * elements along K share one scale, an E8M0 byte (a pure power of two); the
+ * aside in section 5.4 names MXFP8 among the inputs of DeepGEMM's Blackwell
+ * path.  The pages give no rule for choosing the scale.  Reading: the UE8M0
+ * rule of the 1x128 quantizer, applied to each 32-group: s is the power of
+ * two at or above fl32(max(amax, 1e-4) / 448), so no code saturates.
+ *   q = E4M3(fl32(x / s)),  e[r][g] = biased exponent of s  (s = 2^(e-127)).
+ */
+int oracle_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e)
+{
+    int64_t r, G;
+    if (R < 0 || K < 0 || K % MX_GROUP) return -1;
+    G = K / MX_GROUP;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < R; ++r) {
+        int64_t g, k;
+        for (g = 0; g < G; ++g) {
+            const float* v = x + r * K + g * MX_GROUP;
+            float amax = 0.0f, s;
+            uint32_t bits;
+            for (k = 0; k < MX_GROUP; ++k) {
+                float a = fabsf(v[k]);
+                if (a > amax) amax = a;
+            }
+            s = oracle_scale_from_amax(amax, ORACLE_FLAG_UE8M0);
+            memcpy(&bits, &s, 4);
+            e[r * G + g] = (uint8_t)((bits >> 23) & 0xFFu);
+            for (k = 0; k < MX_GROUP; ++k)
+                q[r * K + g * MX_GROUP + k] = oracle_e4m3_encode(v[k] / s);
+        }
+    }
+    return 0;
+}
+
+/*
+ * One output element of the MX GEMM.  tcgen05 page, section 6.1, with
+ * SV = 32, SFA[m][g] = 2^(ea[m][g]-127) and SFB[n][g] = 2^(eb[n][g]-127):
+ *   Y[m][n] = sum_g SFA[m][g] * SFB[n][g] * sum_{k in group g} dec(xq[m][k]) * dec(wq[n][k]).
+ * Each 32-term partial is exact in binary64 (a sub-sum of the exact 128-term
+ * partials), and so is the power-of-two scale product.
+ */
+static double oracle_dot_mx(const uint8_t* xr, const uint8_t* ear, const uint8_t* wr,
+                            const uint8_t* ebr, int64_t K, const double* dec)
+{
+    int64_t G = K / MX_GROUP, g;
+    double acc = 0.0;
+    for (g = 0; g < G; ++g) {
+        double p = 0.0;
+        int k;
+        for (k = 0; k < MX_GROUP; ++k) p += dec[xr[g * MX_GROUP + k]] * dec[wr[g * MX_GROUP + k]];
+        acc += ldexp(1.0, (int)ear[g] - 127) * ldexp(1.0, (int)ebr[g] - 127) * p;
+    }
+    return acc;
+}
+
+/* Dense NT MX GEMM, Y = X * W^T with xq (M, K), ea (M, K/32), wq (N, K),
+ * eb (N, K/32), all row-major. */
+int oracle_gemm_mx(const uint8_t* xq, const uint8_t* ea, const uint8_t* wq,
+                   const uint8_t* eb, int64_t M, int64_t N, int64_t K, double* y)
+{
+    double dec[256];
+    int64_t m, G;
+    if (M < 0 || N < 0 || K < 0 || K % MX_GROUP) return -1;
+    G = K / MX_GROUP;
+    fill_decode_table(dec);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; ++m) {
+        int64_t n;
+        for (n = 0; n < N; ++n)
+            y[m * N + n] = oracle_dot_mx(xq + m * K, ea + m * G, wq + n * K, eb + n * G, K, dec);
+    }
+    return 0;
+}
+
+/* The MX GEMM on a list of (m, n) pairs: y[i] = Y[m_idx[i]][n_idx[i]]. */
+int oracle_gemm_mx_elems(const uint8_t* xq, const uint8_t* ea, const uint8_t* wq,
+                         const uint8_t* eb, int64_t M, int64_t N, int64_t K,
+                         const int64_t* m_idx, const int64_t* n_idx, int64_t count, double* y)
+{
+    double dec[256];
+    int64_t i, G;
+    if (M < 0 || N < 0 || K < 0 || K % MX_GROUP || count < 0) return -1;
+    for (i = 0; i < count; ++i)
+        if (m_idx[i] < 0 || m_idx[i] >= M || n_idx[i] < 0 || n_idx[i] >= N) return -1;
+    G = K / MX_GROUP;
+    fill_decode_table(dec);
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < count; ++i)
+        y[i] = oracle_dot_mx(xq + m_idx[i] * K, ea + m_idx[i] * G, wq + n_idx[i] * K,
+                             eb + n_idx[i] * G, K, dec);
+    return 0;
+}

@@ -11,11 +11,15 @@
  *   [TC]  "GPU GEMM 优化完全拆解(四): tcgen05 与 Blackwell", section 六 (6.1)
  *   [MLC] "Blackwell Tensor Core: tcgen05.mma", section "Block-Scaled MMA"
  *
+ * MXFP8 (the MX variant): X and W both carry one E8M0 byte per 1x32 group
+ * along K, laid out (rows, K/32) row-major; see oracle_quant_mx.
+ *
  * Layouts (all row-major, element offsets):
  *   X   fp32 (M, K)            Xq  u8 (M, K)           sa fp32 [K/128][M]
  *   W   fp32 (N, K)            Wq  u8 (N, K)           sb fp32 [ceil(N/128)][K/128]
  *   Y   fp64 (M, N)
- * K must be a multiple of 128 for every call (the scale granularity along K).
+ * K must be a multiple of 128 for every block-scaled call (the scale
+ * granularity along K) and of 32 for the MX calls.
  */
 #ifndef FP8_ORACLE_H
 #define FP8_ORACLE_H
@@ -74,6 +78,17 @@ int oracle_grouped_masked(const uint8_t* xq, const float* sa, const uint8_t* wq,
                           const float* sb, const int32_t* masked_m, int32_t E,
                           int64_t max_m, int64_t N, int64_t K, uint32_t flags,
                           double* y, uint8_t* written);
+
+/* MXFP8: one E8M0 scale byte per 1x32 group along K (both operands).
+ * x (R, K) fp32 -> q u8 (R, K), e u8 (R, K/32); K must be a multiple of 32. */
+int oracle_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e);
+/* Y (M, N) fp64 = MX X * W^T; xq (M, K), ea (M, K/32), wq (N, K), eb (N, K/32). */
+int oracle_gemm_mx(const uint8_t* xq, const uint8_t* ea, const uint8_t* wq,
+                   const uint8_t* eb, int64_t M, int64_t N, int64_t K, double* y);
+int oracle_gemm_mx_elems(const uint8_t* xq, const uint8_t* ea, const uint8_t* wq,
+                         const uint8_t* eb, int64_t M, int64_t N, int64_t K,
+                         const int64_t* m_idx, const int64_t* n_idx, int64_t count,
+                         double* y);
 
 /* Number of OpenMP threads the oracle will use. */
 int oracle_num_threads(void);
