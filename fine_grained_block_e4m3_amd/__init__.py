@@ -41,6 +41,8 @@ SYMBOLS = (
     "fp8_gemm_nt",
     "fp8_grouped_gemm_contiguous",
     "fp8_grouped_gemm_masked",
+    "fp8_quant_mx",
+    "fp8_gemm_nt_mx",
     "fp8_get_mk_alignment_for_contiguous_layout",
     "fp8_status_string",
 )
@@ -71,8 +73,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fp8_gemm_nt.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
     L.fp8_grouped_gemm_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, U32, P]
     L.fp8_grouped_gemm_masked.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, U32, P]
+    L.fp8_quant_mx.argtypes = [P, I64, I64, P, P, P]
+    L.fp8_gemm_nt_mx.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
     for fn in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_gemm_nt",
-               "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked"):
+               "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked", "fp8_quant_mx",
+               "fp8_gemm_nt_mx"):
         getattr(L, fn).restype = ctypes.c_int
     L.fp8_get_mk_alignment_for_contiguous_layout.argtypes = []
     L.fp8_get_mk_alignment_for_contiguous_layout.restype = I32
@@ -205,4 +210,34 @@ def grouped_gemm_masked(xq, sa, wq, sb, masked_m, ue8m0: bool = False, precise: 
     _check("fp8_grouped_gemm_masked",
            L.fp8_grouped_gemm_masked(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(masked_m),
                                      _ptr(y), E, max_m, N, K, _flags(ue8m0, precise), _stream(xq)))
+    return y
+
+
+def quant_mx(x: torch.Tensor, out=None):
+    """MXFP8: x fp32 (R, K) -> (q uint8 (R, K), e uint8 (R, K/32)); each 1x32
+    group's scale is 2^(e - 127)."""
+    L = load_library()
+    _need(x, "x", torch.float32, 2)
+    R, K = x.shape
+    if out is None:
+        q = torch.empty((R, K), dtype=torch.uint8, device=x.device)
+        e = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    else:
+        q, e = out
+    _check("fp8_quant_mx", L.fp8_quant_mx(_ptr(x), R, K, _ptr(q), _ptr(e), _stream(x)))
+    return q, e
+
+
+def gemm_nt_mx(xq, ea, wq, eb, out=None) -> torch.Tensor:
+    """Y (M, N) bf16 = MXFP8 X * W^T (E8M0 scale bytes per 1x32 group)."""
+    L = load_library()
+    for t, n in ((xq, "xq"), (wq, "wq"), (ea, "ea"), (eb, "eb")):
+        _need(t, n, torch.uint8, 2)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or ea.shape != (M, K // 32) or eb.shape != (N, K // 32):
+        raise ValueError("gemm_nt_mx: inconsistent operand shapes")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _check("fp8_gemm_nt_mx", L.fp8_gemm_nt_mx(_ptr(xq), _ptr(ea), _ptr(wq), _ptr(eb), _ptr(y),
+                                              M, N, K, 0, _stream(xq)))
     return y

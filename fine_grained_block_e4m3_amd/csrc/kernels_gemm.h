@@ -58,7 +58,12 @@ enum GemmMode : int { kDense = 0, kContiguous = 1, kMasked = 2 };
 //   kPathF16       E4M3 widened to FP16 (exact), four FP16 MFMAs (16x16x32) per
 //                  block: exact products, FP32 accumulation; VALU promotion
 //   kPathF16Pow2   as kPathF16, promotion by the power-of-two part of each scale
-enum GemmPath : int { kPathFp8 = 0, kPathFp8Pow2 = 1, kPathF16 = 2, kPathF16Pow2 = 3 };
+//   kPathMx        MXFP8: one E8M0 byte per 1x32 group on both operands (tcgen05
+//                  page, sections 6.1 and 6.3: SV = 32, E8M0 scales).  A lane
+//                  of the 16x16x128 MFMA holds exactly one 32-group of its row,
+//                  so each lane passes its own group's byte as the scale
+//                  operand and the matrix core accumulates over all of K.
+enum GemmPath : int { kPathFp8 = 0, kPathFp8Pow2 = 1, kPathF16 = 2, kPathF16Pow2 = 3, kPathMx = 4 };
 
 // Operand pointers (passed to the kernel as separate __restrict__ arguments):
 //   xq (M, K) codes; masked: (E*max_m, K)
@@ -257,7 +262,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     // most two weight blocks: the K loop is specialised on the subtile where
     // the second one starts, so that the promotion scales are two products
     // per resident fragment and block instead of one per subtile.
-    constexpr bool kSplitSb = kStreamW && TN <= 128 && PATH != kPathFp8Pow2;
+    constexpr bool kMx = PATH == kPathMx;
+    // scales as E8M0 operands of the scaled MFMA; K accumulated in the matrix core
+    constexpr bool kScaledMfma = PATH == kPathFp8Pow2 || kMx;
+    // a scale as carried through the pipeline: the FP32 value, or (MX) the
+    // E8M0 byte of this lane's 32-group
+    using ScaleT = std::conditional_t<kMx, int, float>;
+    constexpr bool kSplitSb = kStreamW && TN <= 128 && !kScaledMfma;
     constexpr bool kF16 = PATH == kPathF16 || PATH == kPathF16Pow2;
     constexpr bool kPow2 = PATH == kPathFp8Pow2 || PATH == kPathF16Pow2;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 subtiles");
@@ -267,6 +278,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     static_assert(XLOADS >= 1 && XLOADS <= 4 && WLOADS >= 1 && WLOADS <= 4, "loads per wave");
     static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS holds the stage ring");
     static_assert((STAGES - 2) * PER_STAGE <= 63, "vmcnt range");
+    // MX scales: one dword (a row's 4 bytes of one K block) per tile row and
+    // per tile column, one 64-lane dword load per 64 of them
+    constexpr int MX_XS_WAVES = BM / 64, MX_WS_WAVES = (BN + 63) / 64;
+    static_assert(!kMx || (MODE == kDense && MX_XS_WAVES + MX_WS_WAVES <= NWAVES),
+                  "MX: dense only, one scale load per wave");
 
     // A ring of STAGES LDS buffers: the loads of K blocks kb+1 .. kb+STAGES-1
     // fly while block kb is used.
@@ -314,22 +330,35 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         vw[q] = (lane_off ^ (uint32_t)((grp & 1) << 4)) + (uint32_t)(grp * 8 * K) - 1024u * q;
     }
     // LDS fragment addresses within a stage: row r, 16-byte chunk c at
-    // r*128 + 16*(c ^ swz(r)); this lane reads chunks 2g and 2g+1.
+    // r*128 + 16*(c ^ swz(r)); this lane reads chunks 2g and 2g+1 (MX: g, g+4).
     // The swizzle depends on the row mod 16 only, so subtile i of this wave
     // sits at a fixed distance 2048*i from subtile 0: one base address per
     // 16-byte half, the subtile and stage offsets are ds_read immediates.
+    // MX: the scaled 16x16x128 instruction takes a lane's first 16 bytes as
+    // part of K block (g/2) and its last 16 as part of block 2 + g/2 -- K
+    // chunk c of 16 bytes lives in lane group c mod 4, half c/4 -- and applies
+    // the scale of lane group j to block j (measured on gfx950).  So that the
+    // 32-groups of the data meet their own scale bytes, lane group g holds
+    // chunks g and g+4 there.  (The other paths give every 32-group of a row
+    // the same scale, and any K order common to both operands sums alike.)
     uint32_t xa[2], wa[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int r = lane & 15;
-        xa[h] = (uint32_t)((wm * TM + r) * 128 + (((2 * g + h) ^ lds_swz(r)) << 4));
-        wa[h] = (uint32_t)(W_BASE + (wn * TN + r) * 128 + (((2 * g + h) ^ lds_swz(r)) << 4));
+        const int ch = kMx ? g + 4 * h : 2 * g + h;
+        xa[h] = (uint32_t)((wm * TM + r) * 128 + ((ch ^ lds_swz(r)) << 4));
+        wa[h] = (uint32_t)(W_BASE + (wn * TN + r) * 128 + ((ch ^ lds_swz(r)) << 4));
     }
     // activation scale of row r of the tile at SC + 4r; weight scales at
     // SC + 256*NSA + 4*slot (the first copy)
-    const uint32_t saa = (uint32_t)(SC_BASE + 4 * (wm * TM + (lane & 15)));
-    const bool sa_wave = wave < NSA;
-    const uint32_t sc_voff = sa_wave ? (uint32_t)(4 * (64 * wave + lane)) : (uint32_t)(4 * lane * KB);
+    // (MX: byte g of the row's dword, the lane's own 32-group)
+    const uint32_t saa = (uint32_t)(SC_BASE + 4 * (wm * TM + (lane & 15)) + (kMx ? g : 0));
+    const bool sa_wave = kMx ? wave < MX_XS_WAVES : wave < NSA;
+    // MX: waves 0 .. BM/64-1 load the X scale dwords of 64 tile rows each,
+    // the next ones those of 64 tile columns each (scale rows are K/32 bytes)
+    const uint32_t mx_row = (uint32_t)(64 * (sa_wave ? wave : wave - MX_XS_WAVES) + lane);
+    const uint32_t sc_voff = kMx ? mx_row * (uint32_t)(K / 32)
+                                 : (sa_wave ? (uint32_t)(4 * (64 * wave + lane)) : (uint32_t)(4 * lane * KB));
     const uint32_t lds0 = uniform((int)lds_addr(smem));
     // LDS destination of this wave's W loads: its rows in stage s at
     // w_dst + s*w_sstride, or the spare area (every stage) for a wave past them
@@ -406,17 +435,29 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         const int nbl = (int)min((int64_t)(BN / 128 + 2), (N + 127) / 128 - nb0);
         // This wave's scale load, as a base that advances adv bytes per K
         // block, an soffset of sstep bytes per K block and a byte range.
-        const uint64_t sc_base = uniform_u64(sa_wave ? (uint64_t)sa_row0 : (uint64_t)(sb + (int64_t)nb0 * KB));
-        const uint32_t sc_adv = sa_wave ? (uint32_t)(4 * p.M) : 0u;
-        const int sc_step = sa_wave ? 0 : 4;
-        const uint32_t sc_rec = uniform(sa_wave ? (int)(4 * rows_valid) : (int)(4 * nbl * KB));
+        // (MX: the tile's rows of the (M, K/32) or (N, K/32) byte tables; the
+        // dword of K block kb at byte 4*kb of each row)
+        const int64_t KS = K / 32;
+        const uint64_t sc_base = uniform_u64(
+            kMx ? (sa_wave ? (uint64_t)(reinterpret_cast<const uint8_t*>(sa_) + row0 * KS)
+                           : (uint64_t)(reinterpret_cast<const uint8_t*>(sb_) + n0 * KS))
+                : (sa_wave ? (uint64_t)sa_row0 : (uint64_t)(sb + (int64_t)nb0 * KB)));
+        const uint32_t sc_adv = (!kMx && sa_wave) ? (uint32_t)(4 * p.M) : 0u;
+        const int sc_step = (!kMx && sa_wave) ? 0 : 4;
+        const uint32_t sc_rec = uniform(
+            kMx ? (sa_wave ? (int)(rows_valid * KS)
+                           : (wave < MX_XS_WAVES + MX_WS_WAVES ? (int)(cols_valid * KS) : 0))
+                : (sa_wave ? (int)(4 * rows_valid) : (int)(4 * nbl * KB)));
         // LDS slot of each subtile's weight block (the last block for
         // subtiles past N, whose columns are never stored)
         uint32_t sb_slot[FJ];
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             const int64_t n = n0 + wn * TN + 16 * j;
-            sb_slot[j] = (uint32_t)(SC_BASE + 256 * NSA + 4 * ((int)((n < N ? n : N - 1) >> 7) - nb0));
+            if constexpr (kMx)   // the column's dword, byte g
+                sb_slot[j] = (uint32_t)(SC_BASE + 4 * BM + 4 * (wn * TN + 16 * j + (lane & 15)) + g);
+            else
+                sb_slot[j] = (uint32_t)(SC_BASE + 256 * NSA + 4 * ((int)((n < N ? n : N - 1) >> 7) - nb0));
         }
         // split scales: subtiles 0 .. jb-1 of this wave lie in the weight block
         // of slot sb_slot[0], the others in the next one (for a wave past N
@@ -490,17 +531,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         auto read_x = [&](int buf, int i) { return lds_frag(smem + buf * BM * 128 + 2048 * i, xa[0], xa[1]); };
         // (wa already holds the W region's base)
         auto read_w = [&](int buf, int j) { return lds_frag(smem + buf * BN * 128 + 2048 * j, wa[0], wa[1]); };
-        auto read_sa = [&](int buf, int i) {
-            return *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + saa + 64 * i);
+        auto read_sa = [&](int buf, int i) -> ScaleT {
+            if constexpr (kMx) return *(smem + buf * NWAVES * 256 + saa + 64 * i);
+            else return *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + saa + 64 * i);
         };
-        auto read_sb = [&](int buf, int j) {
-            return *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + sb_slot[j]);
+        auto read_sb = [&](int buf, int j) -> ScaleT {
+            if constexpr (kMx) return *(smem + buf * NWAVES * 256 + sb_slot[j]);
+            else return *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + sb_slot[j]);
+        };
+        // the E8M0 operand of the scaled MFMA
+        auto e8m0 = [&](ScaleT v) -> int {
+            if constexpr (kMx) return v;
+            else return e8m0_of(v);
         };
         auto read_row = [&](int buf, int r) {
             if constexpr (kStreamW) return read_w(buf, r);
             else return read_x(buf, r);
         };
-        auto read_row_scale = [&](int buf, int r) {
+        auto read_row_scale = [&](int buf, int r) -> ScaleT {
             if constexpr (kSplitSb) return 0.f;   // the block's two products serve every row
             else if constexpr (kStreamW) return read_sb(buf, r);
             else return read_sa(buf, r);
@@ -514,11 +562,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             if constexpr (kStreamW) return read_x(buf, c);
             else return read_w(buf, c);
         };
-        auto read_res_scales = [&](int buf, float (&v)[C]) {
+        auto read_res_scales = [&](int buf, ScaleT (&v)[C]) {
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 if constexpr (kStreamW) v[c] = read_sa(buf, c);
-                else if (kUniformSb && c > 0) v[c] = v[0];
+                else if (kUniformSb && !kMx && c > 0) v[c] = v[0];
                 else v[c] = read_sb(buf, c);
             }
         };
@@ -576,18 +624,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         i32x8 res[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) res[c] = read_res(0, c);
-        float rs_cur[C], rs_prev[C];
+        ScaleT rs_cur[C], rs_prev[C];
         read_res_scales(0, rs_cur);
 #pragma unroll
-        for (int c = 0; c < C; ++c) rs_prev[c] = 0.f;
+        for (int c = 0; c < C; ++c) rs_prev[c] = ScaleT{};
         // fragments and scales of the next two streamed rows (g, g+1)
         i32x8 fr0 = read_row(0, 0), fr1 = read_row(0, 1);
-        float sr0 = read_row_scale(0, 0), sr1 = read_row_scale(0, 1);
+        ScaleT sr0 = read_row_scale(0, 0), sr1 = read_row_scale(0, 1);
         // the partials of the row before (none yet: zeros promote to nothing)
         f32x4 prev[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) prev[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float st_prev = 0.f;
+        ScaleT st_prev{};
         // split scales: this block's weight-block scales, the products
         // sA(c) x sB(first / second block), and the products of the previous
         // block's last row
@@ -625,7 +673,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             const StageLoads L1 =
                 stage_loads(kb + STAGES - 1, std::integral_constant<int, (BUF + STAGES - 1) % STAGES>{});
             const StageLoads L2 = stage_loads(kb + STAGES, std::integral_constant<int, BUF>{});
-            float rs_next[C], sb2_next[2];
+            ScaleT rs_next[C];
+            float sb2_next[2];
             // resident fragments widened to FP16 once per block on the precise path
             f16x8 resh[kF16 ? C : 1][4];
             if constexpr (kF16) {
@@ -636,9 +685,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             }
             // E8M0 exponents of the resident scales (scaled-MFMA path)
             int rse[C];
-            if constexpr (PATH == kPathFp8Pow2) {
+            if constexpr (kScaledMfma) {
 #pragma unroll
-                for (int c = 0; c < C; ++c) rse[c] = e8m0_of(rs_cur[c]);
+                for (int c = 0; c < C; ++c) rse[c] = e8m0(rs_cur[c]);
             }
             static_for<R>([&](auto rc) {
                 constexpr int r = decltype(rc)::value;
@@ -653,10 +702,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 const i32x8 fc = fr0;
-                const float st_c = sr0;
+                const ScaleT st_c = sr0;
                 // reads two rows ahead: this block, or the next one after the barrier
                 i32x8 fn;
-                float sn;
+                ScaleT sn;
                 if constexpr (r + 2 < R) {
                     fn = read_row(BUF, r + 2);
                     sn = read_row_scale(BUF, r + 2);
@@ -676,8 +725,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                 if constexpr (r < RB) issue_window(L1, std::integral_constant<int, r + 2>{});
                 else issue_window(L2, std::integral_constant<int, r - RB>{});
 
-                if constexpr (PATH == kPathFp8Pow2) {
-                    const int ste = e8m0_of(st_c);
+                if constexpr (kScaledMfma) {
+                    const int ste = e8m0(st_c);
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
                         // operand A is the W fragment, B the X fragment
@@ -779,7 +828,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         });
         // drain: the last row's partials
         if constexpr (kSplitSb) promote_p(R - 1, plast);
-        else if constexpr (PATH != kPathFp8Pow2) promote(R - 1, rs_prev);
+        else if constexpr (!kScaledMfma) promote(R - 1, rs_prev);
         };
         if constexpr (kSplitSb) {
             // one copy of the loop per boundary position (wave-uniform)

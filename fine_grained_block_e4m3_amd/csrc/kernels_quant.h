@@ -141,4 +141,53 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restr
     else quant_128x128_block<POW2, true>(w, wq, sb, N, K, nb, kb, wave_max);
 }
 
+// MXFP8 quantizer, for activations and weights alike: one E8M0 scale per 1x32
+// group along K (tcgen05 page, sections 6.1 and 6.3: MX formats share one
+// power-of-two scale over 32 elements).  The scale is the power of two at or
+// above max(amax, 1e-4)/448 (the UE8M0 rule of the 1x128 groups), so no code
+// saturates.  A wave takes one row and up to 32 consecutive groups (4 KB of
+// FP32): lane l loads 16 bytes of each of 4 row segments of 256 values, so
+// eight neighbouring lanes hold one group and its maximum is an 8-lane
+// reduction.  Only a row's last unit can be short (K/32 not a multiple of 32).
+//   x (R, K) fp32 -> q (R, K) u8, e (R, K/32) u8 (the scale is 2^(e-127))
+template <bool PARTIAL>
+__device__ __forceinline__ void quant_mx_unit(const float* __restrict__ x, uint8_t* __restrict__ q,
+                                              uint8_t* __restrict__ e, int64_t K, int64_t G,
+                                              int64_t r, int64_t g0, int lane) {
+    const int64_t off = r * K + g0 * 32 + lane * 4;
+    f32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // group g0 + 8i + lane/8; groups past the row end are not read
+        if (!PARTIAL || g0 + 8 * i + (lane >> 3) < G) v[i] = load_stream(x + off + 256 * i);
+        else v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t grp = g0 + 8 * i + (lane >> 3);
+        float amax = abs_max4(v[i]);
+#pragma unroll
+        for (int o = 4; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 8));
+        const float s = group_scale(amax, true);
+        if (!PARTIAL || grp < G) {
+            store_codes(q + off + 256 * i, cvt_e4m3x4(v[i][0] / s, v[i][1] / s, v[i][2] / s, v[i][3] / s));
+            if ((lane & 7) == 0) e[r * G + grp] = (uint8_t)(__float_as_uint(s) >> 23);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void quant_mx_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
+                                                       uint8_t* __restrict__ e, int64_t R, int64_t K,
+                                                       int64_t units) {
+    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (u >= units) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t G = K / 32;
+    const int64_t upr = (G + 31) / 32;   // units per row
+    const int64_t r = u / upr;
+    const int64_t g0 = (u - r * upr) * 32;
+    if (g0 + 32 <= G) quant_mx_unit<false>(x, q, e, K, G, r, g0, lane);
+    else quant_mx_unit<true>(x, q, e, K, G, r, g0, lane);
+}
+
 }  // namespace fp8k

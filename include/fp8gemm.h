@@ -22,7 +22,7 @@
  *     The weight scale table is sb[nb][kb] at sb + nb*(K/128) + kb, nb = n/128.
  *   - K must be a multiple of 128 (the scale granularity along K; [DG]
  *     "线程组织": the K block is fixed at 128 because scaling is per 128
- *     channels).
+ *     channels); the MX quantizer needs only K % 32 == 0.
  *   - Errors are detected on the host before anything is enqueued:
  *       FP8_ERR_INVALID_ARG  null pointer, negative or oversized dimension,
  *                            unknown flag bit
@@ -147,6 +147,34 @@ fp8_status fp8_grouped_gemm_masked(const uint8_t* xq, const float* sa,
                                    const int32_t* masked_m, uint16_t* y,
                                    int32_t E, int64_t max_m, int64_t N,
                                    int64_t K, uint32_t flags, void* stream);
+
+/*
+ * MXFP8 quantizer, for activations and weights alike ([TC] sections 6.1 and
+ * 6.3: the MX formats share one E8M0 scale, a pure power of two, over 32
+ * consecutive elements along K; [TC] 5.4 names MXFP8 among the inputs of
+ * DeepGEMM's Blackwell path).  The scale of a group is the power of two at or
+ * above max(amax, 1e-4) / 448 (the pages give no rule; this is the UE8M0 rule
+ * of the 1x128 groups), so no code saturates.
+ *   x  fp32 (R, K)     input, K % 32 == 0
+ *   q  u8   (R, K)     output codes, q = E4M3(x / s)
+ *   e  u8   (R, K/32)  output scale bytes, s = 2^(e - 127)
+ */
+fp8_status fp8_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q,
+                        uint8_t* e, void* stream);
+
+/*
+ * Dense NT GEMM on MXFP8 operands ([TC] 6.1 with scale vector length 32:
+ *   Y[m][n] = sum_g 2^(ea[m][g]-127) * 2^(eb[n][g]-127)
+ *                   * sum_{k in group g} xq[m][k] * wq[n][k]).
+ *   xq u8 (M,K), ea u8 (M, K/32), wq u8 (N,K), eb u8 (N, K/32), y bf16 bits
+ *   (M,N); K % 128 == 0.  Every lane of the scaled matrix instruction holds one
+ *   32-group of its row and takes that group's byte as its scale, so the whole
+ *   K sum stays in the instruction's FP32 accumulator.  flags must be 0.
+ */
+fp8_status fp8_gemm_nt_mx(const uint8_t* xq, const uint8_t* ea,
+                          const uint8_t* wq, const uint8_t* eb, uint16_t* y,
+                          int64_t M, int64_t N, int64_t K, uint32_t flags,
+                          void* stream);
 
 /* M alignment every expert segment of the contiguous layout must have
  * ([DG] "分组 GEMM 的两种布局": the alignment query).  Returns 128. */

@@ -76,20 +76,45 @@ def test_quant_validation(L):
     assert L.fp8_quant_128x128(A, 4, 128, A, A, 4, None) == INVALID
 
 
+def _gpu_visible() -> bool:
+    import torch
+    return torch.cuda.is_available()
+
+
 def test_grouped_validation(L):
     c = L.fp8_grouped_gemm_contiguous
-    assert c(A, A, A, A, A, A, 256, 128, 128, 2, 0, None) in (NODEV, OK, LAUNCH)
+    if not _gpu_visible():   # valid arguments: on a GPU this would launch on fake addresses
+        assert c(A, A, A, A, A, A, 256, 128, 128, 2, 0, None) in (NODEV, OK, LAUNCH)
     assert c(A, A, A, A, A, A, 256, 100, 128, 2, 0, None) == SHAPE     # N % 128
     assert c(A, A, A, A, None, A, 256, 128, 128, 2, 0, None) == INVALID
     assert c(A, A, A, A, A, A, 256, 128, 128, -1, 0, None) == INVALID
     assert c(A, A, A, A, A, A, 256, 128, 128, 0, 0, None) == OK
     m = L.fp8_grouped_gemm_masked
-    assert m(A, A, A, A, A, A, 4, 256, 128, 256, 0, None) in (NODEV, OK, LAUNCH)
+    if not _gpu_visible():
+        assert m(A, A, A, A, A, A, 4, 256, 128, 256, 0, None) in (NODEV, OK, LAUNCH)
     assert m(A, A, A, A, A, A, 4, 256, 128, 200, 0, None) == SHAPE
     assert m(A, A, A, A, A, A, 4, 256, 96, 256, 0, None) == SHAPE
     assert m(A, A, A, A, None, A, 4, 256, 128, 256, 0, None) == INVALID
     assert m(A, A, A, A, A, MIS, 4, 256, 128, 256, 0, None) == ALIGN
     assert m(A, A, A, A, A, A, 0, 256, 128, 256, 0, None) == OK
+
+
+def test_mx_validation(L):
+    q = L.fp8_quant_mx
+    assert q(None, 4, 128, A, A, None) == INVALID
+    assert q(A, -1, 128, A, A, None) == INVALID
+    assert q(A, 4, 48, A, A, None) == SHAPE           # K % 32
+    assert q(MIS, 4, 128, A, A, None) == ALIGN
+    assert q(A, 4, 128, A, MIS, None) == ALIGN
+    assert q(A, 0, 128, None, None, None) == OK
+    g = L.fp8_gemm_nt_mx
+    assert g(A, A, A, A, A, 4, 8, 128, 1, None) == INVALID   # no flags defined
+    assert g(None, A, A, A, A, 4, 8, 128, 0, None) == INVALID
+    assert g(A, A, A, A, A, 4, 8, 96, 0, None) == SHAPE      # K % 128
+    assert g(A, A, A, A, A, 4, 8, 0, 0, None) == SHAPE
+    assert g(A, MIS, A, A, A, 4, 8, 128, 0, None) == ALIGN
+    assert g(A, A, A, A, MIS, 4, 8, 128, 0, None) == ALIGN
+    assert g(A, A, A, A, A, 0, 8, 128, 0, None) == OK
 
 
 def test_no_device_reported_without_gpu(L):
@@ -98,6 +123,8 @@ def test_no_device_reported_without_gpu(L):
         pytest.skip("a GPU is visible")
     assert _gemm(L) == NODEV
     assert L.fp8_quant_1x128(A, 4, 128, A, A, 0, None) == NODEV
+    assert L.fp8_quant_mx(A, 4, 128, A, A, None) == NODEV
+    assert L.fp8_gemm_nt_mx(A, A, A, A, A, 4, 8, 128, 0, None) == NODEV
 
 
 def test_binding_refuses_cpu_tensors():
