@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fine-grained block-scaled E4M3 GEMM hot path on one GPU.
 
-    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--no-cpu-baseline] [--mx]
 
 One step = one pass of the whole hot path over one batch of synthetic input:
 1x128 activation quantization, 128x128 weight quantization and the
@@ -11,7 +11,8 @@ preallocated.  Prints ONE JSON line.
 
 Default workload: dense prefill GEMM M=4096, N=7168, K=7168 (N(0,1) inputs,
 0.1% of entries x100).  The other configurations are parity workloads that
-can also be timed with --config.
+can also be timed with --config.  --mx times the MXFP8 variant of a dense
+workload instead: 1x32 E8M0 quantization of X and of W and the MXFP8 GEMM.
 """
 from __future__ import annotations
 
@@ -74,6 +75,14 @@ def algorithmic_counts(wl):
     return flops, float(nbytes), rows
 
 
+def algorithmic_counts_mx(wl):
+    """FLOPs and algorithmic bytes of one dense MXFP8 GEMM launch: A + the
+    1x32 scale bytes of A + B + those of B + Y."""
+    M, N, K = wl.M, wl.N, wl.K
+    nbytes = M * K + M * (K // 32) + N * K + N * (K // 32) + 2 * M * N
+    return 2.0 * M * N * K, float(nbytes), M
+
+
 def load_traffic(key: str, sha: str):
     """HBM bytes per GEMM launch from committed rocprofv3 PMC counters, or None
     when they were taken for other kernel sources."""
@@ -89,7 +98,7 @@ def load_traffic(key: str, sha: str):
     return float(e["hbm_bytes_per_dispatch"])
 
 
-def cpu_baseline(wl, target_s: float):
+def cpu_baseline(wl, target_s: float, mx: bool = False):
     """Time the CPU oracle on a bounded sample of the same workload: the first
     Ms rows of X and first Ns rows of W, quantized and multiplied."""
     import numpy as np
@@ -101,9 +110,14 @@ def cpu_baseline(wl, target_s: float):
         x = np.ascontiguousarray(wl.x[:ms])
         w = np.ascontiguousarray(wl.w[:ns])
         t0 = time.perf_counter()
-        xq, sa = oracle.quant_1x128(x, flags)
-        wq, sb = oracle.quant_128x128(w, flags)
-        oracle.gemm_nt(xq, sa, wq, sb, flags)
+        if mx:
+            xq, ea = oracle.quant_mx(x)
+            wq, eb = oracle.quant_mx(w)
+            oracle.gemm_mx(xq, ea, wq, eb)
+        else:
+            xq, sa = oracle.quant_1x128(x, flags)
+            wq, sb = oracle.quant_128x128(w, flags)
+            oracle.gemm_nt(xq, sa, wq, sb, flags)
         return time.perf_counter() - t0
 
     # Grow the sample (rows of X first, then whole 128-row blocks of W) until
@@ -130,7 +144,9 @@ def cpu_baseline(wl, target_s: float):
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": f"{wl.name}: X rows [0,{ms2}) and W rows [0,{ns2}), K={K}: oracle "
-                  f"quant_1x128 + quant_128x128 + gemm_nt ({flops:.3g} FLOP) in {t2:.2f} s",
+                  + ("quant_mx(X) + quant_mx(W) + gemm_mx" if mx else
+                     "quant_1x128 + quant_128x128 + gemm_nt")
+                  + f" ({flops:.3g} FLOP) in {t2:.2f} s",
         "seconds": t2,
         "cpu_model": _cpu_model(),
     }
@@ -169,6 +185,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--mx", action="store_true",
+                    help="the MXFP8 variant (1x32 E8M0 scales on both operands) of a dense workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -198,6 +216,9 @@ def main():
     log(f"generating workload {args.config}: {workloads.CONFIG_NAMES[args.config]}")
     wl = workloads.config(args.config)
     ue8m0 = wl.ue8m0
+    if args.mx and wl.kind != "dense":
+        print("--mx: dense workloads only (configs 1-3)", file=sys.stderr)
+        sys.exit(2)
     x = torch.from_numpy(wl.x).to(dev)
     w = torch.from_numpy(wl.w).to(dev)
     M, K = wl.x.shape
@@ -206,7 +227,14 @@ def main():
     sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
     wq = torch.empty((NW, K), dtype=torch.uint8, device=dev)
     sb = torch.empty(((NW + 127) // 128, K // 128), dtype=torch.float32, device=dev)
-    if wl.kind == "dense":
+    if args.mx:
+        ea = torch.empty((K // 128, M), dtype=torch.int32, device=dev)
+        eb = torch.empty((K // 128, NW), dtype=torch.int32, device=dev)
+        y = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
+
+        def gemm():
+            fp8.gemm_nt_mx(xq, ea, wq, eb, out=y)
+    elif wl.kind == "dense":
         y = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
 
         def gemm():
@@ -229,16 +257,31 @@ def main():
         def gemm():
             fp8.grouped_gemm_masked(xq3, sa, wq3, sb3, mm, ue8m0=ue8m0, out=y)
 
-    names = ("quant_1x128", "quant_128x128", "gemm")
+    if args.mx:
+        names = ("quant_mx_x", "quant_mx_w", "gemm")
+
+        def quant_x():
+            fp8.quant_mx(x, out=(xq, ea))
+
+        def quant_w():
+            fp8.quant_mx(w, out=(wq, eb))
+    else:
+        names = ("quant_1x128", "quant_128x128", "gemm")
+
+        def quant_x():
+            fp8.quant_1x128(x, ue8m0=ue8m0, out=(xq, sa))
+
+        def quant_w():
+            fp8.quant_128x128(w, ue8m0=ue8m0, out=(wq, sb))
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fp8.quant_1x128(x, ue8m0=ue8m0, out=(xq, sa))
+        quant_x()
         if ev is not None:
             ev[1].record(stream)
-        fp8.quant_128x128(w, ue8m0=ue8m0, out=(wq, sb))
+        quant_w()
         if ev is not None:
             ev[2].record(stream)
         gemm()
@@ -262,11 +305,29 @@ def main():
                                        for i in range(args.steps)]))
                      for k, n in enumerate(names)}
 
-    flops, nbytes, rows = algorithmic_counts(wl)
+    # The GEMM again on cold caches: before each launch a 1 GiB buffer (more
+    # than the 256 MB MALL plus the L2s) is read, so that no operand comes
+    # from a cache that the step's quantizers warmed.  A read leaves clean
+    # lines, so no write-back of the flush is charged to the GEMM.  Reported
+    # beside the in-pipeline figure that the roofline uses.
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cold_ev = []
+    for _ in range(min(args.steps, 20)):
+        flush_buf.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        gemm()
+        b.record(stream)
+        cold_ev.append((a, b))
+    torch.cuda.synchronize()
+    cold_ms = float(np.mean([a.elapsed_time(b) for a, b in cold_ev]))
+    del flush_buf
+
+    flops, nbytes, rows = algorithmic_counts_mx(wl) if args.mx else algorithmic_counts(wl)
     gemm_s = per_kernel_ms["gemm"] / 1e3
     compute_bound = wl.kind == "contiguous" or (wl.kind == "dense" and flops / nbytes > 629)
     sha = kernel_source_sha()
-    traffic = load_traffic(f"gemm_cfg{args.config}", sha)
+    traffic = load_traffic(f"gemm_{'mx_' if args.mx else ''}cfg{args.config}", sha)
     if compute_bound:
         achieved = flops / gemm_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
@@ -280,27 +341,40 @@ def main():
     roof["algorithmic_flop"] = flops
     roof["algorithmic_bytes"] = nbytes
 
-    qx_bytes = 4.0 * M * K + M * K + 4.0 * M * (K // 128)
-    qw_bytes = 4.0 * NW * K + NW * K + 4.0 * sb.numel()
+    if args.mx:
+        qx_bytes = 4.0 * M * K + M * K + M * (K // 32)
+        qw_bytes = 4.0 * NW * K + NW * K + NW * (K // 32)
+    else:
+        qx_bytes = 4.0 * M * K + M * K + 4.0 * M * (K // 128)
+        qw_bytes = 4.0 * NW * K + NW * K + 4.0 * sb.numel()
     kernels = {
-        "quant_1x128": {"avg_us": per_kernel_ms["quant_1x128"] * 1e3,
-                        "GB/s": qx_bytes / (per_kernel_ms["quant_1x128"] / 1e3) / 1e9},
-        "quant_128x128": {"avg_us": per_kernel_ms["quant_128x128"] * 1e3,
-                          "GB/s": qw_bytes / (per_kernel_ms["quant_128x128"] / 1e3) / 1e9},
+        names[0]: {"avg_us": per_kernel_ms[names[0]] * 1e3,
+                   "GB/s": qx_bytes / (per_kernel_ms[names[0]] / 1e3) / 1e9},
+        names[1]: {"avg_us": per_kernel_ms[names[1]] * 1e3,
+                   "GB/s": qw_bytes / (per_kernel_ms[names[1]] / 1e3) / 1e9},
         "gemm": {"avg_us": per_kernel_ms["gemm"] * 1e3, "TFLOPS": flops / gemm_s / 1e12,
                  "GB/s": nbytes / gemm_s / 1e9,
                  "frac_mfma": flops / gemm_s / 1e12 / PEAK_FP8_TFLOPS,
                  "frac_hbm": nbytes / gemm_s / 1e9 / PEAK_HBM_GBS},
     }
 
+    kernels["gemm_cold_cache"] = {
+        "avg_us": cold_ms * 1e3, "TFLOPS": flops / (cold_ms / 1e3) / 1e12,
+        "GB/s": nbytes / (cold_ms / 1e3) / 1e9,
+        "frac_mfma": flops / (cold_ms / 1e3) / 1e12 / PEAK_FP8_TFLOPS,
+        "frac_hbm": nbytes / (cold_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "flush": "a 1 GiB buffer read before each launch"}
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu = cpu_baseline(wl, args.cpu_seconds, mx=args.mx)
 
     value = flops / (ms_per_step / 1e3) / 1e12
-    cfg = {"workload": wl.name, "kind": wl.kind, "M": int(M), "N": int(wl.N), "K": int(K),
-           "valid_rows": rows, "scales": "ue8m0" if ue8m0 else "fp32",
-           "step": "quant_1x128(X) + quant_128x128(W) + block-scaled GEMM"}
+    cfg = {"workload": ("mx_" if args.mx else "") + wl.name, "kind": wl.kind, "M": int(M),
+           "N": int(wl.N), "K": int(K), "valid_rows": rows,
+           "scales": "mx_e8m0_1x32" if args.mx else ("ue8m0" if ue8m0 else "fp32"),
+           "step": ("quant_mx(X) + quant_mx(W) + MXFP8 GEMM" if args.mx else
+                    "quant_1x128(X) + quant_128x128(W) + block-scaled GEMM")}
     if wl.kind != "dense":
         cfg["experts"] = int(wl.E)
     out = {

@@ -214,14 +214,15 @@ def grouped_gemm_masked(xq, sa, wq, sb, masked_m, ue8m0: bool = False, precise: 
 
 
 def quant_mx(x: torch.Tensor, out=None):
-    """MXFP8: x fp32 (R, K) -> (q uint8 (R, K), e uint8 (R, K/32)); each 1x32
-    group's scale is 2^(e - 127)."""
+    """MXFP8: x fp32 (R, K) -> (q uint8 (R, K), e int32 (K/128, R)).  e holds the
+    packed scale bytes: byte t of e[kb, r] is the exponent byte b of 1x32 group
+    4*kb + t of row r, whose scale is 2^(b - 127)."""
     L = load_library()
     _need(x, "x", torch.float32, 2)
     R, K = x.shape
     if out is None:
         q = torch.empty((R, K), dtype=torch.uint8, device=x.device)
-        e = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+        e = torch.empty((K // 128, R), dtype=torch.int32, device=x.device)
     else:
         q, e = out
     _check("fp8_quant_mx", L.fp8_quant_mx(_ptr(x), R, K, _ptr(q), _ptr(e), _stream(x)))
@@ -229,13 +230,16 @@ def quant_mx(x: torch.Tensor, out=None):
 
 
 def gemm_nt_mx(xq, ea, wq, eb, out=None) -> torch.Tensor:
-    """Y (M, N) bf16 = MXFP8 X * W^T (E8M0 scale bytes per 1x32 group)."""
+    """Y (M, N) bf16 = MXFP8 X * W^T; ea (K/128, M) and eb (K/128, N) are the
+    packed scale tables that quant_mx writes."""
     L = load_library()
-    for t, n in ((xq, "xq"), (wq, "wq"), (ea, "ea"), (eb, "eb")):
-        _need(t, n, torch.uint8, 2)
+    _need(xq, "xq", torch.uint8, 2)
+    _need(wq, "wq", torch.uint8, 2)
+    _need(ea, "ea", torch.int32, 2)
+    _need(eb, "eb", torch.int32, 2)
     M, K = xq.shape
     N = wq.shape[0]
-    if wq.shape[1] != K or ea.shape != (M, K // 32) or eb.shape != (N, K // 32):
+    if wq.shape[1] != K or ea.shape != (K // 128, M) or eb.shape != (K // 128, N):
         raise ValueError("gemm_nt_mx: inconsistent operand shapes")
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     _check("fp8_gemm_nt_mx", L.fp8_gemm_nt_mx(_ptr(xq), _ptr(ea), _ptr(wq), _ptr(eb), _ptr(y),

@@ -193,9 +193,9 @@ fp8_status fp8_quant_128x128(const float* w, int64_t N, int64_t K, uint8_t* wq, 
     return launch_status();
 }
 
-fp8_status fp8_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e, void* stream) {
+fp8_status fp8_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uint32_t* e, void* stream) {
     if (!dims_ok(R) || !dims_ok(K)) return FP8_ERR_INVALID_ARG;
-    if (K % 32) return FP8_ERR_SHAPE;
+    if (K % 128) return FP8_ERR_SHAPE;
     if (R == 0 || K == 0) return FP8_OK;
     if (!x || !q || !e) return FP8_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(q) || !aligned16(e)) return FP8_ERR_ALIGNMENT;
@@ -207,11 +207,11 @@ fp8_status fp8_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_
     const int64_t blocks = (units + 3) / 4;
     if (blocks > 0x7FFFFFFF) return FP8_ERR_INVALID_ARG;
     hipLaunchKernelGGL(fp8k::quant_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                       x, q, e, R, K, units);
+                       x, q, reinterpret_cast<uint8_t*>(e), R, K, units);
     return launch_status();
 }
 
-fp8_status fp8_gemm_nt_mx(const uint8_t* xq, const uint8_t* ea, const uint8_t* wq, const uint8_t* eb,
+fp8_status fp8_gemm_nt_mx(const uint8_t* xq, const uint32_t* ea, const uint8_t* wq, const uint32_t* eb,
                           uint16_t* y, int64_t M, int64_t N, int64_t K, uint32_t flags, void* stream) {
     if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K) || flags != 0) return FP8_ERR_INVALID_ARG;
     if (K % 128) return FP8_ERR_SHAPE;
@@ -223,7 +223,7 @@ fp8_status fp8_gemm_nt_mx(const uint8_t* xq, const uint8_t* ea, const uint8_t* w
         return FP8_ERR_ALIGNMENT;
     fp8k::GemmParams p{};
     p.xq = xq; p.wq = wq; p.y = y;
-    p.sa = reinterpret_cast<const float*>(ea);   // byte tables, read as such by the MX path
+    p.sa = reinterpret_cast<const float*>(ea);   // packed scale tables, read as such by the MX path
     p.sb = reinterpret_cast<const float*>(eb);
     p.M = M; p.N = N; p.K = K; p.E = 1;
     return run_gemm_mx(p, (hipStream_t)stream);

@@ -59,10 +59,10 @@ enum GemmMode : int { kDense = 0, kContiguous = 1, kMasked = 2 };
 //                  block: exact products, FP32 accumulation; VALU promotion
 //   kPathF16Pow2   as kPathF16, promotion by the power-of-two part of each scale
 //   kPathMx        MXFP8: one E8M0 byte per 1x32 group on both operands (tcgen05
-//                  page, sections 6.1 and 6.3: SV = 32, E8M0 scales).  A lane
-//                  of the 16x16x128 MFMA holds exactly one 32-group of its row,
-//                  so each lane passes its own group's byte as the scale
-//                  operand and the matrix core accumulates over all of K.
+//                  page, sections 6.1 and 6.3: SV = 32, E8M0 scales), packed
+//                  4 to a dword per (K block, row) in [K/128][rows] tables.
+//                  Each lane passes the byte of the 32-group it holds as its
+//                  scale operand and the matrix core accumulates over all of K.
 enum GemmPath : int { kPathFp8 = 0, kPathFp8Pow2 = 1, kPathF16 = 2, kPathF16Pow2 = 3, kPathMx = 4 };
 
 // Operand pointers (passed to the kernel as separate __restrict__ arguments):
@@ -316,48 +316,69 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     // slot ^ swz(row) = slot ^ (l/8) ^ (grp mod 2).  Source offset within the
     // tile: (R0 + l/8)*K + 16*chunk (K is a multiple of 128, so the chunk term
     // folds in with an XOR), reduced by 1024*q for the q-th load of a group.
+    // MX: every row's chunks are stored in the order cperm (bits 0 and 1 of
+    // the chunk index swapped; see the fragment addresses below), which is
+    // linear over XOR, so it applies to both XOR terms separately.
+    auto cperm = [](int c) { return kMx ? (c & 4) | ((c & 1) << 1) | ((c >> 1) & 1) : c; };
     const int rl = lane >> 3;
-    const uint32_t lane_off = (uint32_t)(rl * K) | (uint32_t)(((lane & 7) ^ rl) << 4);
+    const uint32_t lane_off = (uint32_t)(rl * K) | (uint32_t)(cperm((lane & 7) ^ rl) << 4);
     uint32_t vx[XLOADS], vw[WLOADS];
 #pragma unroll
     for (int q = 0; q < XLOADS; ++q) {
         const int grp = wave * XLOADS + q;
-        vx[q] = (lane_off ^ (uint32_t)((grp & 1) << 4)) + (uint32_t)(grp * 8 * K) - 1024u * q;
+        vx[q] = (lane_off ^ (uint32_t)(cperm(grp & 1) << 4)) + (uint32_t)(grp * 8 * K) - 1024u * q;
     }
 #pragma unroll
     for (int q = 0; q < WLOADS; ++q) {
         const int grp = wave * WLOADS + q;
-        vw[q] = (lane_off ^ (uint32_t)((grp & 1) << 4)) + (uint32_t)(grp * 8 * K) - 1024u * q;
+        vw[q] = (lane_off ^ (uint32_t)(cperm(grp & 1) << 4)) + (uint32_t)(grp * 8 * K) - 1024u * q;
     }
     // LDS fragment addresses within a stage: row r, 16-byte chunk c at
-    // r*128 + 16*(c ^ swz(r)); this lane reads chunks 2g and 2g+1 (MX: g, g+4).
+    // r*128 + 16*(c ^ swz(r)); this lane reads chunks 2g and 2g+1.
     // The swizzle depends on the row mod 16 only, so subtile i of this wave
     // sits at a fixed distance 2048*i from subtile 0: one base address per
     // 16-byte half, the subtile and stage offsets are ds_read immediates.
-    // MX: the scaled 16x16x128 instruction takes a lane's first 16 bytes as
-    // part of K block (g/2) and its last 16 as part of block 2 + g/2 -- K
-    // chunk c of 16 bytes lives in lane group c mod 4, half c/4 -- and applies
-    // the scale of lane group j to block j (measured on gfx950).  So that the
-    // 32-groups of the data meet their own scale bytes, lane group g holds
-    // chunks g and g+4 there.  (The other paths give every 32-group of a row
-    // the same scale, and any K order common to both operands sums alike.)
+    // MX: the scaled 16x16x128 instruction counts a lane's first 16 bytes
+    // into scale block g/2 and its last 16 into block 2 + g/2, and applies the
+    // scale of lane group j to block j (measured on gfx950).  Any K order
+    // inside a block sums alike, so a block only has to hold the two 16-byte
+    // chunks of one 32-group of the data: lane group g holds data chunks
+    // 4(g/2) + g%2 and that + 2 -- groups 0,1: {0,2},{1,3} (data group 0 in
+    // block 0, group 1 in block 2); groups 2,3: {4,6},{5,7} (data groups 2
+    // and 3 in blocks 1 and 3) -- and passes the scale of data group
+    // mx_grp = (0,2,1,3)[g].  Data chunk c is stored at logical position
+    // cperm(c), which turns exactly those chunks into positions 2g and 2g+1:
+    // the reads keep the address pattern of the other paths, which has no LDS
+    // bank conflicts (reading chunks 4(g/2) + g%2 + {0, 2} directly measured
+    // 2e7 conflict cycles per launch).  (The other paths give every 32-group
+    // of a row the same scale, and any K order common to both operands sums
+    // alike.)
+    const int mx_grp = ((g & 1) << 1) | (g >> 1);
     uint32_t xa[2], wa[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int r = lane & 15;
-        const int ch = kMx ? g + 4 * h : 2 * g + h;
+        const int ch = 2 * g + h;
         xa[h] = (uint32_t)((wm * TM + r) * 128 + ((ch ^ lds_swz(r)) << 4));
         wa[h] = (uint32_t)(W_BASE + (wn * TN + r) * 128 + ((ch ^ lds_swz(r)) << 4));
     }
     // activation scale of row r of the tile at SC + 4r; weight scales at
     // SC + 256*NSA + 4*slot (the first copy)
-    // (MX: byte g of the row's dword, the lane's own 32-group)
-    const uint32_t saa = (uint32_t)(SC_BASE + 4 * (wm * TM + (lane & 15)) + (kMx ? g : 0));
+    // (MX: the row's dword of 4 group bytes; this lane takes byte mx_grp, the
+    // 32-group whose chunks it holds.  The dword is read whole: the 4 lanes of
+    // a row then read one address, which LDS broadcasts, where byte reads of
+    // different bytes of one dword conflict.)
+    const uint32_t saa = (uint32_t)(SC_BASE + 4 * (wm * TM + (lane & 15)));
+    const uint32_t mx_shift = 8u * (uint32_t)mx_grp;
+    // MX: the dword of this lane's column in subtile j of the wave at
+    // mx_wcol + 64*j (subtile and stage offsets are immediates)
+    const uint32_t mx_wcol = (uint32_t)(SC_BASE + 4 * BM + 4 * (wn * TN + (lane & 15)));
     const bool sa_wave = kMx ? wave < MX_XS_WAVES : wave < NSA;
     // MX: waves 0 .. BM/64-1 load the X scale dwords of 64 tile rows each,
-    // the next ones those of 64 tile columns each (scale rows are K/32 bytes)
+    // the next ones those of 64 tile columns each; in the packed tables the
+    // dwords of one K block are consecutive over rows (256 bytes per wave)
     const uint32_t mx_row = (uint32_t)(64 * (sa_wave ? wave : wave - MX_XS_WAVES) + lane);
-    const uint32_t sc_voff = kMx ? mx_row * (uint32_t)(K / 32)
+    const uint32_t sc_voff = kMx ? 4u * mx_row
                                  : (sa_wave ? (uint32_t)(4 * (64 * wave + lane)) : (uint32_t)(4 * lane * KB));
     const uint32_t lds0 = uniform((int)lds_addr(smem));
     // LDS destination of this wave's W loads: its rows in stage s at
@@ -435,18 +456,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         const int nbl = (int)min((int64_t)(BN / 128 + 2), (N + 127) / 128 - nb0);
         // This wave's scale load, as a base that advances adv bytes per K
         // block, an soffset of sstep bytes per K block and a byte range.
-        // (MX: the tile's rows of the (M, K/32) or (N, K/32) byte tables; the
-        // dword of K block kb at byte 4*kb of each row)
-        const int64_t KS = K / 32;
+        // (MX: the tile's rows, or columns, of the packed [K/128][M] or
+        // [K/128][N] dword tables, advancing one table row per K block)
         const uint64_t sc_base = uniform_u64(
-            kMx ? (sa_wave ? (uint64_t)(reinterpret_cast<const uint8_t*>(sa_) + row0 * KS)
-                           : (uint64_t)(reinterpret_cast<const uint8_t*>(sb_) + n0 * KS))
+            kMx ? (sa_wave ? (uint64_t)(reinterpret_cast<const uint32_t*>(sa_) + row0)
+                           : (uint64_t)(reinterpret_cast<const uint32_t*>(sb_) + n0))
                 : (sa_wave ? (uint64_t)sa_row0 : (uint64_t)(sb + (int64_t)nb0 * KB)));
-        const uint32_t sc_adv = (!kMx && sa_wave) ? (uint32_t)(4 * p.M) : 0u;
-        const int sc_step = (!kMx && sa_wave) ? 0 : 4;
+        const uint32_t sc_adv = kMx ? (uint32_t)(4 * (sa_wave ? p.M : N))
+                                    : (sa_wave ? (uint32_t)(4 * p.M) : 0u);
+        const int sc_step = (kMx || sa_wave) ? 0 : 4;
         const uint32_t sc_rec = uniform(
-            kMx ? (sa_wave ? (int)(rows_valid * KS)
-                           : (wave < MX_XS_WAVES + MX_WS_WAVES ? (int)(cols_valid * KS) : 0))
+            kMx ? (sa_wave ? (int)(4 * rows_valid)
+                           : (wave < MX_XS_WAVES + MX_WS_WAVES ? (int)(4 * cols_valid) : 0))
                 : (sa_wave ? (int)(4 * rows_valid) : (int)(4 * nbl * KB)));
         // LDS slot of each subtile's weight block (the last block for
         // subtiles past N, whose columns are never stored)
@@ -454,9 +475,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             const int64_t n = n0 + wn * TN + 16 * j;
-            if constexpr (kMx)   // the column's dword, byte g
-                sb_slot[j] = (uint32_t)(SC_BASE + 4 * BM + 4 * (wn * TN + 16 * j + (lane & 15)) + g);
-            else
+            if constexpr (!kMx)   // (MX: mx_wcol)
                 sb_slot[j] = (uint32_t)(SC_BASE + 256 * NSA + 4 * ((int)((n < N ? n : N - 1) >> 7) - nb0));
         }
         // split scales: subtiles 0 .. jb-1 of this wave lie in the weight block
@@ -532,11 +551,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         // (wa already holds the W region's base)
         auto read_w = [&](int buf, int j) { return lds_frag(smem + buf * BN * 128 + 2048 * j, wa[0], wa[1]); };
         auto read_sa = [&](int buf, int i) -> ScaleT {
-            if constexpr (kMx) return *(smem + buf * NWAVES * 256 + saa + 64 * i);
+            if constexpr (kMx)
+                return (int)__builtin_amdgcn_ubfe(
+                    *reinterpret_cast<const uint32_t*>(smem + buf * NWAVES * 256 + saa + 64 * i), mx_shift, 8);
             else return *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + saa + 64 * i);
         };
         auto read_sb = [&](int buf, int j) -> ScaleT {
-            if constexpr (kMx) return *(smem + buf * NWAVES * 256 + sb_slot[j]);
+            if constexpr (kMx)
+                return (int)__builtin_amdgcn_ubfe(
+                    *reinterpret_cast<const uint32_t*>(smem + buf * NWAVES * 256 + mx_wcol + 64 * j), mx_shift, 8);
             else return *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + sb_slot[j]);
         };
         // the E8M0 operand of the scaled MFMA

@@ -148,11 +148,16 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restr
 // saturates.  A wave takes one row and up to 32 consecutive groups (4 KB of
 // FP32): lane l loads 16 bytes of each of 4 row segments of 256 values, so
 // eight neighbouring lanes hold one group and its maximum is an 8-lane
-// reduction.  Only a row's last unit can be short (K/32 not a multiple of 32).
-//   x (R, K) fp32 -> q (R, K) u8, e (R, K/32) u8 (the scale is 2^(e-127))
+// reduction.  Only a row's last unit can be short (K/128 not a multiple of 8).
+// The scale bytes are packed 4 to a dword per (K block, row) and the dwords
+// laid out [K/128][R] -- DeepGEMM's Blackwell path, tcgen05 page section 5.4,
+// takes packed, transposed UE8M0 scales -- so that a GEMM tile reads the
+// scales of one K block for consecutive rows from consecutive dwords.
+//   x (R, K) fp32 -> q (R, K) u8, e u32 [K/128][R]: byte t of e[kb][r] is the
+//   scale byte of group 4kb+t of row r (the scale is 2^(byte-127))
 template <bool PARTIAL>
 __device__ __forceinline__ void quant_mx_unit(const float* __restrict__ x, uint8_t* __restrict__ q,
-                                              uint8_t* __restrict__ e, int64_t K, int64_t G,
+                                              uint8_t* __restrict__ e, int64_t R, int64_t K, int64_t G,
                                               int64_t r, int64_t g0, int lane) {
     const int64_t off = r * K + g0 * 32 + lane * 4;
     f32x4 v[4];
@@ -171,7 +176,7 @@ __device__ __forceinline__ void quant_mx_unit(const float* __restrict__ x, uint8
         const float s = group_scale(amax, true);
         if (!PARTIAL || grp < G) {
             store_codes(q + off + 256 * i, cvt_e4m3x4(v[i][0] / s, v[i][1] / s, v[i][2] / s, v[i][3] / s));
-            if ((lane & 7) == 0) e[r * G + grp] = (uint8_t)(__float_as_uint(s) >> 23);
+            if ((lane & 7) == 0) e[((grp >> 2) * R + r) * 4 + (grp & 3)] = (uint8_t)(__float_as_uint(s) >> 23);
         }
     }
 }
@@ -186,8 +191,8 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const float* __restrict__
     const int64_t upr = (G + 31) / 32;   // units per row
     const int64_t r = u / upr;
     const int64_t g0 = (u - r * upr) * 32;
-    if (g0 + 32 <= G) quant_mx_unit<false>(x, q, e, K, G, r, g0, lane);
-    else quant_mx_unit<true>(x, q, e, K, G, r, g0, lane);
+    if (g0 + 32 <= G) quant_mx_unit<false>(x, q, e, R, K, G, r, g0, lane);
+    else quant_mx_unit<true>(x, q, e, R, K, G, r, g0, lane);
 }
 
 }  // namespace fp8k

@@ -22,7 +22,7 @@
  *     The weight scale table is sb[nb][kb] at sb + nb*(K/128) + kb, nb = n/128.
  *   - K must be a multiple of 128 (the scale granularity along K; [DG]
  *     "线程组织": the K block is fixed at 128 because scaling is per 128
- *     channels); the MX quantizer needs only K % 32 == 0.
+ *     channels).
  *   - Errors are detected on the host before anything is enqueued:
  *       FP8_ERR_INVALID_ARG  null pointer, negative or oversized dimension,
  *                            unknown flag bit
@@ -154,25 +154,31 @@ fp8_status fp8_grouped_gemm_masked(const uint8_t* xq, const float* sa,
  * consecutive elements along K; [TC] 5.4 names MXFP8 among the inputs of
  * DeepGEMM's Blackwell path).  The scale of a group is the power of two at or
  * above max(amax, 1e-4) / 448 (the pages give no rule; this is the UE8M0 rule
- * of the 1x128 groups), so no code saturates.
- *   x  fp32 (R, K)     input, K % 32 == 0
- *   q  u8   (R, K)     output codes, q = E4M3(x / s)
- *   e  u8   (R, K/32)  output scale bytes, s = 2^(e - 127)
+ * of the 1x128 groups), so no code saturates.  The scale bytes are packed and
+ * transposed ([TC] 5.4: DeepGEMM's Blackwell path takes packed UE8M0 scales
+ * in a transposed layout): the 4 bytes of the groups of one 128-K block of a
+ * row form one dword, and the dwords are laid out [K/128][R].
+ *   x  fp32 (R, K)          input, K % 128 == 0
+ *   q  u8   (R, K)          output codes, q = E4M3(x / s)
+ *   e  u32  [K/128][R]      output scales: byte t of e[kb*R + r] is the scale
+ *                           byte b of group 4*kb + t of row r, s = 2^(b - 127)
  */
 fp8_status fp8_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q,
-                        uint8_t* e, void* stream);
+                        uint32_t* e, void* stream);
 
 /*
  * Dense NT GEMM on MXFP8 operands ([TC] 6.1 with scale vector length 32:
- *   Y[m][n] = sum_g 2^(ea[m][g]-127) * 2^(eb[n][g]-127)
+ *   Y[m][n] = sum_g 2^(ea(m,g)-127) * 2^(eb(n,g)-127)
  *                   * sum_{k in group g} xq[m][k] * wq[n][k]).
- *   xq u8 (M,K), ea u8 (M, K/32), wq u8 (N,K), eb u8 (N, K/32), y bf16 bits
- *   (M,N); K % 128 == 0.  Every lane of the scaled matrix instruction holds one
- *   32-group of its row and takes that group's byte as its scale, so the whole
- *   K sum stays in the instruction's FP32 accumulator.  flags must be 0.
+ *   xq u8 (M,K), ea u32 [K/128][M], wq u8 (N,K), eb u32 [K/128][N] (packed as
+ *   fp8_quant_mx writes them; ea[kb][m] byte t is the exponent byte of group
+ *   4*kb + t), y bf16 bits (M,N); K % 128 == 0.  Every lane of the scaled
+ *   matrix instruction holds one 32-group of its row and takes that group's
+ *   byte as its scale, so the whole K sum stays in the instruction's FP32
+ *   accumulator.  flags must be 0.
  */
-fp8_status fp8_gemm_nt_mx(const uint8_t* xq, const uint8_t* ea,
-                          const uint8_t* wq, const uint8_t* eb, uint16_t* y,
+fp8_status fp8_gemm_nt_mx(const uint8_t* xq, const uint32_t* ea,
+                          const uint8_t* wq, const uint32_t* eb, uint16_t* y,
                           int64_t M, int64_t N, int64_t K, uint32_t flags,
                           void* stream);
 

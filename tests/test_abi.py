@@ -103,7 +103,8 @@ def test_mx_validation(L):
     q = L.fp8_quant_mx
     assert q(None, 4, 128, A, A, None) == INVALID
     assert q(A, -1, 128, A, A, None) == INVALID
-    assert q(A, 4, 48, A, A, None) == SHAPE           # K % 32
+    assert q(A, 4, 48, A, A, None) == SHAPE           # K % 128
+    assert q(A, 4, 96, A, A, None) == SHAPE
     assert q(MIS, 4, 128, A, A, None) == ALIGN
     assert q(A, 4, 128, A, MIS, None) == ALIGN
     assert q(A, 0, 128, None, None, None) == OK

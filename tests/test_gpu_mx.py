@@ -1,7 +1,8 @@
 """GPU MXFP8 path (E4M3 with one E8M0 scale per 1x32 group on both operands)
 against the oracle.
 
-The quantizer is bit-exact (codes and scale bytes).  The GEMM runs the scaled
+The quantizer is bit-exact (codes and scale bytes; the library packs the
+bytes into [K/128][rows] dwords, the oracle keeps them (rows, K/32)).  The GEMM runs the scaled
 FP8 matrix instruction with each lane's own group scale and keeps the K sum in
 its FP32 accumulator; it is held to the tolerance |y - ref| <= 8e-3 |ref| +
 1e-3 rms(ref), or to the bound of the measured FP8-MFMA truncation model where
@@ -19,6 +20,18 @@ from gpu_helpers import (assert_close_or_bounded, bf16_bits, bf16_to_f64, check_
 pytestmark = pytest.mark.gpu
 
 DEC = oracle.e4m3_decode(np.arange(256))
+
+
+def pack_scales(e: np.ndarray) -> np.ndarray:
+    """The oracle's (R, K/32) scale bytes in the library's packed layout: int32
+    [K/128][R] whose byte t of [kb][r] is group 4*kb + t of row r."""
+    R, G = e.shape
+    return np.ascontiguousarray(e.reshape(R, G // 4, 4).transpose(1, 0, 2)).view(np.int32).reshape(G // 4, R)
+
+
+def unpack_scales(p: np.ndarray) -> np.ndarray:
+    KB, R = p.shape
+    return np.ascontiguousarray(p.view(np.uint8).reshape(KB, R, 4).transpose(1, 0, 2)).reshape(R, 4 * KB)
 
 
 def mx_mfma_error_bound(xq, ea, wq, eb, ref):
@@ -43,14 +56,15 @@ def run_mx(xq, ea, wq, eb, guard=2048):
     N = wq.shape[0]
     say(f"gemm_nt_mx M={M} N={N} K={K}")
     full, y = guarded((M, N), guard)
-    fp8.gemm_nt_mx(dev(xq), dev(ea), dev(wq), dev(eb), out=y)
+    fp8.gemm_nt_mx(dev(xq), dev(pack_scales(ea)), dev(wq), dev(pack_scales(eb)), out=y)
     torch.cuda.synchronize()
     check_guards(full, M * N, guard)
     return bf16_bits(y)
 
 
-@pytest.mark.parametrize("R,K", [(128, 512), (1, 32), (300, 1024), (77, 96), (9, 7168),
-                                 (33, 1056), (5, 2080)])
+@pytest.mark.parametrize("R,K", [(128, 512), (1, 128), (300, 1024), (77, 384), (9, 7168),
+                                 # a row of 32-group units plus a short one
+                                 (33, 1152), (5, 2176)])
 def test_quant_mx_bitexact(R, K):
     wl = workloads.dense(R, 1, K, seed=300 + R, outlier_frac=0.01, outlier_mult=50.0)
     q_ref, e_ref = oracle.quant_mx(wl.x)
@@ -58,7 +72,7 @@ def test_quant_mx_bitexact(R, K):
     q, e = fp8.quant_mx(dev(wl.x))
     torch.cuda.synchronize()
     assert np.array_equal(host(q), q_ref)
-    assert np.array_equal(host(e), e_ref)
+    assert np.array_equal(unpack_scales(host(e)), e_ref)
 
 
 def test_quant_mx_zero_and_tiny_groups():
@@ -69,7 +83,7 @@ def test_quant_mx_zero_and_tiny_groups():
     q_ref, e_ref = oracle.quant_mx(x)
     q, e = fp8.quant_mx(dev(x))
     torch.cuda.synchronize()
-    assert np.array_equal(host(q), q_ref) and np.array_equal(host(e), e_ref)
+    assert np.array_equal(host(q), q_ref) and np.array_equal(unpack_scales(host(e)), e_ref)
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (1, 96, 128), (64, 288, 1536), (200, 300, 384),
@@ -138,7 +152,7 @@ def test_gemm_mx_end_to_end_from_fp32():
     torch.cuda.synchronize()
     rx, rea = oracle.quant_mx(wl.x)
     rw, reb = oracle.quant_mx(wl.w)
-    assert np.array_equal(host(xq), rx) and np.array_equal(host(ea), rea)
-    assert np.array_equal(host(wq), rw) and np.array_equal(host(eb), reb)
+    assert np.array_equal(host(xq), rx) and np.array_equal(unpack_scales(host(ea)), rea)
+    assert np.array_equal(host(wq), rw) and np.array_equal(unpack_scales(host(eb)), reb)
     ref = oracle.gemm_mx(rx, rea, rw, reb)
     assert_close_or_bounded(bf16_bits(y), ref, mx_mfma_error_bound(rx, rea, rw, reb, ref), "mx e2e")
