@@ -73,11 +73,19 @@ def lib():
         L.oracle_quant_mx.argtypes = [P, I64, I64, P, P]
         L.oracle_gemm_mx.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.oracle_gemm_mx_elems.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P]
+        L.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_decode.restype = ctypes.c_double
+        L.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+        L.oracle_e2m1_encode.restype = ctypes.c_uint8
+        L.oracle_quant_mxfp4.argtypes = [P, I64, I64, P, P]
+        L.oracle_gemm_mx_w4.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.oracle_gemm_mx_w4_elems.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P]
         L.oracle_num_threads.restype = ctypes.c_int
         for fn in ("oracle_quant_1x128", "oracle_quant_128x128", "oracle_gemm_nt",
                    "oracle_gemm_nt_elems", "oracle_grouped_contiguous",
                    "oracle_grouped_masked", "oracle_quant_mx", "oracle_gemm_mx",
-                   "oracle_gemm_mx_elems"):
+                   "oracle_gemm_mx_elems", "oracle_quant_mxfp4", "oracle_gemm_mx_w4",
+                   "oracle_gemm_mx_w4_elems"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -230,4 +238,49 @@ def gemm_mx_elems(xq, ea, wq, eb, m_idx, n_idx) -> np.ndarray:
     y = np.empty(m_idx.shape, np.float64)
     _check(lib().oracle_gemm_mx_elems(_p(xq), _p(ea), _p(wq), _p(eb), M, N, K, _p(m_idx),
                                       _p(n_idx), m_idx.size, _p(y)), "gemm_mx_elems")
+    return y
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Decode E2M1 nibbles (0..15) to float64 values."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    table = np.array([lib().oracle_e2m1_decode(c) for c in range(16)])
+    return table[codes & 0xF]
+
+
+def e2m1_encode(values) -> np.ndarray:
+    v = np.asarray(values, dtype=np.float32)
+    return np.array([lib().oracle_e2m1_encode(float(t)) for t in v.ravel()], np.uint8).reshape(v.shape)
+
+
+def quant_mxfp4(x: np.ndarray):
+    """MXFP4: x fp32 (R, K) -> (q uint8 (R, K/2) packed nibbles, element k in
+    byte k/2 (low nibble for even k); e uint8 (R, K/32))."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R, K = x.shape
+    q = np.empty((R, K // 2), np.uint8)
+    e = np.empty((R, K // MX_GROUP), np.uint8)
+    _check(lib().oracle_quant_mxfp4(_p(x), R, K, _p(q), _p(e)), "quant_mxfp4")
+    return q, e
+
+
+def gemm_mx_w4(xq, ea, wq, eb) -> np.ndarray:
+    """Y (M, N) float64 = MXFP8 X * (MXFP4 W)^T."""
+    xq, ea, wq, eb = (np.ascontiguousarray(a, dtype=np.uint8) for a in (xq, ea, wq, eb))
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = np.empty((M, N), np.float64)
+    _check(lib().oracle_gemm_mx_w4(_p(xq), _p(ea), _p(wq), _p(eb), M, N, K, _p(y)), "gemm_mx_w4")
+    return y
+
+
+def gemm_mx_w4_elems(xq, ea, wq, eb, m_idx, n_idx) -> np.ndarray:
+    xq, ea, wq, eb = (np.ascontiguousarray(a, dtype=np.uint8) for a in (xq, ea, wq, eb))
+    M, K = xq.shape
+    N = wq.shape[0]
+    m_idx = np.ascontiguousarray(m_idx, dtype=np.int64)
+    n_idx = np.ascontiguousarray(n_idx, dtype=np.int64)
+    y = np.empty(m_idx.shape, np.float64)
+    _check(lib().oracle_gemm_mx_w4_elems(_p(xq), _p(ea), _p(wq), _p(eb), M, N, K, _p(m_idx),
+                                         _p(n_idx), m_idx.size, _p(y)), "gemm_mx_w4_elems")
     return y

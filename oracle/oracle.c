@@ -499,3 +499,145 @@ int oracle_gemm_mx_elems(const uint8_t* xq, const uint8_t* ea, const uint8_t* wq
                              eb + n_idx[i] * G, K, dec);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* MXFP4 weights: E2M1 elements, one E8M0 scale per 1x32 group along K       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Decode one E2M1 nibble.  tcgen05 page, section 6.3: MXFP4 elements are
+ * E2M1 (1 sign, 2 exponent, 1 mantissa bit) with an E8M0 scale per 32.
+ * Exponent bias 1, exponent field 0 is subnormal, no infinities or NaN:
+ *   normal    (-1)^s * 2^(e-1) * (1 + m/2)
+ *   subnormal (-1)^s * m/2
+ * giving the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ */
+double oracle_e2m1_decode(uint8_t code)
+{
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/*
+ * Encode a binary32 value to E2M1: the nearest value, ties to the code with
+ * an even mantissa bit, magnitudes above 6 saturating to 6, the sign kept.
+ * Brute force over the 8 magnitudes (all distances exact in binary64).
+ */
+uint8_t oracle_e2m1_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 0x8 : 0x0;
+    double a = fabs((double)v), best_d;
+    int best = 0, c;
+    if (a >= 6.0) return (uint8_t)(sign | 0x7);
+    best_d = a;
+    for (c = 1; c <= 7; ++c) {
+        double d = fabs(a - oracle_e2m1_decode((uint8_t)c));
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/*
+ * MXFP4 quantizer of a row-major (R, K) matrix.  Reading (as for MXFP8): the
+ * scale of a 1x32 group is the power of two at or above
+ * fl32(max(amax, 1e-4) / 6), 6 being the largest E2M1 magnitude, so no
+ * element saturates.  Output: element k of row r in byte r*K/2 + k/2, the
+ * low nibble for even k; e[r][g] = biased exponent of the group's scale.
+ */
+int oracle_quant_mxfp4(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e)
+{
+    int64_t r, G;
+    if (R < 0 || K < 0 || K % MX_GROUP) return -1;
+    G = K / MX_GROUP;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < R; ++r) {
+        int64_t g, k;
+        for (g = 0; g < G; ++g) {
+            const float* v = x + r * K + g * MX_GROUP;
+            float amax = 0.0f, a, s;
+            uint32_t bits;
+            for (k = 0; k < MX_GROUP; ++k) {
+                float t = fabsf(v[k]);
+                if (t > amax) amax = t;
+            }
+            a = amax > 1e-4f ? amax : 1e-4f;
+            s = a / 6.0f;
+            memcpy(&bits, &s, 4);
+            if (bits & 0x007FFFFFu) bits = ((bits >> 23) + 1u) << 23;
+            memcpy(&s, &bits, 4);
+            e[r * G + g] = (uint8_t)((bits >> 23) & 0xFFu);
+            for (k = 0; k < MX_GROUP; k += 2) {
+                uint8_t lo = oracle_e2m1_encode(v[k] / s), hi = oracle_e2m1_encode(v[k + 1] / s);
+                q[(r * K + g * MX_GROUP + k) / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+    return 0;
+}
+
+/* One element of the MXFP8 x MXFP4 GEMM: as oracle_dot_mx, with W's elements
+ * E2M1 nibbles (tcgen05 page, section 6.1 with SV = 32). */
+static double oracle_dot_mx_w4(const uint8_t* xr, const uint8_t* ear, const uint8_t* wr,
+                               const uint8_t* ebr, int64_t K, const double* dec8,
+                               const double* dec4)
+{
+    int64_t G = K / MX_GROUP, g;
+    double acc = 0.0;
+    for (g = 0; g < G; ++g) {
+        double p = 0.0;
+        int k;
+        for (k = 0; k < MX_GROUP; ++k) {
+            int64_t kk = g * MX_GROUP + k;
+            uint8_t nib = (uint8_t)((wr[kk / 2] >> (4 * (kk & 1))) & 0xF);
+            p += dec8[xr[kk]] * dec4[nib];
+        }
+        acc += ldexp(1.0, (int)ear[g] - 127) * ldexp(1.0, (int)ebr[g] - 127) * p;
+    }
+    return acc;
+}
+
+/* Y (M, N) = X * W^T with X MXFP8 (xq (M, K), ea (M, K/32)) and W MXFP4
+ * (wq (N, K/2) packed nibbles, eb (N, K/32)); on a list of (m, n) pairs. */
+int oracle_gemm_mx_w4_elems(const uint8_t* xq, const uint8_t* ea, const uint8_t* wq,
+                            const uint8_t* eb, int64_t M, int64_t N, int64_t K,
+                            const int64_t* m_idx, const int64_t* n_idx, int64_t count, double* y)
+{
+    double dec8[256], dec4[16];
+    int64_t i, G;
+    int c;
+    if (M < 0 || N < 0 || K < 0 || K % MX_GROUP || count < 0) return -1;
+    for (i = 0; i < count; ++i)
+        if (m_idx[i] < 0 || m_idx[i] >= M || n_idx[i] < 0 || n_idx[i] >= N) return -1;
+    G = K / MX_GROUP;
+    fill_decode_table(dec8);
+    for (c = 0; c < 16; ++c) dec4[c] = oracle_e2m1_decode((uint8_t)c);
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < count; ++i)
+        y[i] = oracle_dot_mx_w4(xq + m_idx[i] * K, ea + m_idx[i] * G, wq + n_idx[i] * (K / 2),
+                                eb + n_idx[i] * G, K, dec8, dec4);
+    return 0;
+}
+
+int oracle_gemm_mx_w4(const uint8_t* xq, const uint8_t* ea, const uint8_t* wq,
+                      const uint8_t* eb, int64_t M, int64_t N, int64_t K, double* y)
+{
+    double dec8[256], dec4[16];
+    int64_t m, G;
+    int c;
+    if (M < 0 || N < 0 || K < 0 || K % MX_GROUP) return -1;
+    G = K / MX_GROUP;
+    fill_decode_table(dec8);
+    for (c = 0; c < 16; ++c) dec4[c] = oracle_e2m1_decode((uint8_t)c);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; ++m) {
+        int64_t n;
+        for (n = 0; n < N; ++n)
+            y[m * N + n] = oracle_dot_mx_w4(xq + m * K, ea + m * G, wq + n * (K / 2), eb + n * G,
+                                            K, dec8, dec4);
+    }
+    return 0;
+}

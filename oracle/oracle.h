@@ -90,6 +90,21 @@ int oracle_gemm_mx_elems(const uint8_t* xq, const uint8_t* ea, const uint8_t* wq
                          const int64_t* m_idx, const int64_t* n_idx, int64_t count,
                          double* y);
 
+/* MXFP4 (weights): E2M1 nibbles, one E8M0 scale byte per 1x32 group.
+ * x (R, K) fp32 -> q u8 (R, K/2) (element k in byte k/2, low nibble for even
+ * k), e u8 (R, K/32); K must be a multiple of 32. */
+double  oracle_e2m1_decode(uint8_t code);
+uint8_t oracle_e2m1_encode(float v);
+int oracle_quant_mxfp4(const float* x, int64_t R, int64_t K, uint8_t* q, uint8_t* e);
+/* Y (M, N) fp64 = X * W^T, X MXFP8 (xq (M, K), ea (M, K/32)), W MXFP4
+ * (wq (N, K/2), eb (N, K/32)). */
+int oracle_gemm_mx_w4(const uint8_t* xq, const uint8_t* ea, const uint8_t* wq,
+                      const uint8_t* eb, int64_t M, int64_t N, int64_t K, double* y);
+int oracle_gemm_mx_w4_elems(const uint8_t* xq, const uint8_t* ea, const uint8_t* wq,
+                            const uint8_t* eb, int64_t M, int64_t N, int64_t K,
+                            const int64_t* m_idx, const int64_t* n_idx, int64_t count,
+                            double* y);
+
 /* Number of OpenMP threads the oracle will use. */
 int oracle_num_threads(void);
 
