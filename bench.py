@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fine-grained block-scaled E4M3 GEMM hot path on one GPU.
 
-    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--no-cpu-baseline] [--mx]
+    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--no-cpu-baseline] [--mx | --w4]
 
 One step = one pass of the whole hot path over one batch of synthetic input:
 1x128 activation quantization, 128x128 weight quantization and the
@@ -12,7 +12,8 @@ preallocated.  Prints ONE JSON line.
 Default workload: dense prefill GEMM M=4096, N=7168, K=7168 (N(0,1) inputs,
 0.1% of entries x100).  The other configurations are parity workloads that
 can also be timed with --config.  --mx times the MXFP8 variant of a dense
-workload instead: 1x32 E8M0 quantization of X and of W and the MXFP8 GEMM.
+workload instead: 1x32 E8M0 quantization of X and of W and the MXFP8 GEMM;
+--w4 the MXFP4-weight variant: MXFP8 X, E2M1 W (1x32 E8M0 scales), their GEMM.
 """
 from __future__ import annotations
 
@@ -75,11 +76,12 @@ def algorithmic_counts(wl):
     return flops, float(nbytes), rows
 
 
-def algorithmic_counts_mx(wl):
-    """FLOPs and algorithmic bytes of one dense MXFP8 GEMM launch: A + the
-    1x32 scale bytes of A + B + those of B + Y."""
+def algorithmic_counts_mx(wl, w4: bool = False):
+    """FLOPs and algorithmic bytes of one dense MXFP8 (or MXFP4-weight) GEMM
+    launch: A + the 1x32 scale bytes of A + B (half a byte per element with
+    E2M1 weights) + those of B + Y."""
     M, N, K = wl.M, wl.N, wl.K
-    nbytes = M * K + M * (K // 32) + N * K + N * (K // 32) + 2 * M * N
+    nbytes = M * K + M * (K // 32) + (N * K // 2 if w4 else N * K) + N * (K // 32) + 2 * M * N
     return 2.0 * M * N * K, float(nbytes), M
 
 
@@ -98,7 +100,7 @@ def load_traffic(key: str, sha: str):
     return float(e["hbm_bytes_per_dispatch"])
 
 
-def cpu_baseline(wl, target_s: float, mx: bool = False):
+def cpu_baseline(wl, target_s: float, mx: bool = False, w4: bool = False):
     """Time the CPU oracle on a bounded sample of the same workload: the first
     Ms rows of X and first Ns rows of W, quantized and multiplied."""
     import numpy as np
@@ -110,7 +112,11 @@ def cpu_baseline(wl, target_s: float, mx: bool = False):
         x = np.ascontiguousarray(wl.x[:ms])
         w = np.ascontiguousarray(wl.w[:ns])
         t0 = time.perf_counter()
-        if mx:
+        if w4:
+            xq, ea = oracle.quant_mx(x)
+            wq, eb = oracle.quant_mxfp4(w)
+            oracle.gemm_mx_w4(xq, ea, wq, eb)
+        elif mx:
             xq, ea = oracle.quant_mx(x)
             wq, eb = oracle.quant_mx(w)
             oracle.gemm_mx(xq, ea, wq, eb)
@@ -144,7 +150,8 @@ def cpu_baseline(wl, target_s: float, mx: bool = False):
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": f"{wl.name}: X rows [0,{ms2}) and W rows [0,{ns2}), K={K}: oracle "
-                  + ("quant_mx(X) + quant_mx(W) + gemm_mx" if mx else
+                  + ("quant_mx(X) + quant_mxfp4(W) + gemm_mx_w4" if w4 else
+                     "quant_mx(X) + quant_mx(W) + gemm_mx" if mx else
                      "quant_1x128 + quant_128x128 + gemm_nt")
                   + f" ({flops:.3g} FLOP) in {t2:.2f} s",
         "seconds": t2,
@@ -187,6 +194,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--mx", action="store_true",
                     help="the MXFP8 variant (1x32 E8M0 scales on both operands) of a dense workload")
+    ap.add_argument("--w4", action="store_true",
+                    help="MXFP8 activations with MXFP4 (E2M1) weights on a dense workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -216,9 +225,10 @@ def main():
     log(f"generating workload {args.config}: {workloads.CONFIG_NAMES[args.config]}")
     wl = workloads.config(args.config)
     ue8m0 = wl.ue8m0
-    if args.mx and wl.kind != "dense":
-        print("--mx: dense workloads only (configs 1-3)", file=sys.stderr)
+    if (args.mx or args.w4) and wl.kind != "dense":
+        print("--mx / --w4: dense workloads only (configs 1-3)", file=sys.stderr)
         sys.exit(2)
+    mx = args.mx or args.w4
     x = torch.from_numpy(wl.x).to(dev)
     w = torch.from_numpy(wl.w).to(dev)
     M, K = wl.x.shape
@@ -227,7 +237,15 @@ def main():
     sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
     wq = torch.empty((NW, K), dtype=torch.uint8, device=dev)
     sb = torch.empty(((NW + 127) // 128, K // 128), dtype=torch.float32, device=dev)
-    if args.mx:
+    if args.w4:
+        ea = torch.empty((K // 128, M), dtype=torch.int32, device=dev)
+        eb = torch.empty((K // 128, NW), dtype=torch.int32, device=dev)
+        wq = torch.empty((NW, K // 2), dtype=torch.uint8, device=dev)
+        y = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
+
+        def gemm():
+            fp8.gemm_nt_mx_w4(xq, ea, wq, eb, out=y)
+    elif args.mx:
         ea = torch.empty((K // 128, M), dtype=torch.int32, device=dev)
         eb = torch.empty((K // 128, NW), dtype=torch.int32, device=dev)
         y = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
@@ -257,14 +275,17 @@ def main():
         def gemm():
             fp8.grouped_gemm_masked(xq3, sa, wq3, sb3, mm, ue8m0=ue8m0, out=y)
 
-    if args.mx:
-        names = ("quant_mx_x", "quant_mx_w", "gemm")
+    if mx:
+        names = ("quant_mx_x", "quant_mxfp4_w" if args.w4 else "quant_mx_w", "gemm")
 
         def quant_x():
             fp8.quant_mx(x, out=(xq, ea))
 
         def quant_w():
-            fp8.quant_mx(w, out=(wq, eb))
+            if args.w4:
+                fp8.quant_mxfp4(w, out=(wq, eb))
+            else:
+                fp8.quant_mx(w, out=(wq, eb))
     else:
         names = ("quant_1x128", "quant_128x128", "gemm")
 
@@ -323,11 +344,12 @@ def main():
     cold_ms = float(np.mean([a.elapsed_time(b) for a, b in cold_ev]))
     del flush_buf
 
-    flops, nbytes, rows = algorithmic_counts_mx(wl) if args.mx else algorithmic_counts(wl)
+    flops, nbytes, rows = algorithmic_counts_mx(wl, args.w4) if mx else algorithmic_counts(wl)
     gemm_s = per_kernel_ms["gemm"] / 1e3
     compute_bound = wl.kind == "contiguous" or (wl.kind == "dense" and flops / nbytes > 629)
     sha = kernel_source_sha()
-    traffic = load_traffic(f"gemm_{'mx_' if args.mx else ''}cfg{args.config}", sha)
+    variant = "w4_" if args.w4 else ("mx_" if args.mx else "")
+    traffic = load_traffic(f"gemm_{variant}cfg{args.config}", sha)
     if compute_bound:
         achieved = flops / gemm_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
@@ -341,9 +363,9 @@ def main():
     roof["algorithmic_flop"] = flops
     roof["algorithmic_bytes"] = nbytes
 
-    if args.mx:
+    if mx:
         qx_bytes = 4.0 * M * K + M * K + M * (K // 32)
-        qw_bytes = 4.0 * NW * K + NW * K + NW * (K // 32)
+        qw_bytes = 4.0 * NW * K + (NW * K // 2 if args.w4 else NW * K) + NW * (K // 32)
     else:
         qx_bytes = 4.0 * M * K + M * K + 4.0 * M * (K // 128)
         qw_bytes = 4.0 * NW * K + NW * K + 4.0 * sb.numel()
@@ -367,13 +389,14 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds, mx=args.mx)
+        cpu = cpu_baseline(wl, args.cpu_seconds, mx=args.mx, w4=args.w4)
 
     value = flops / (ms_per_step / 1e3) / 1e12
-    cfg = {"workload": ("mx_" if args.mx else "") + wl.name, "kind": wl.kind, "M": int(M),
+    cfg = {"workload": variant + wl.name, "kind": wl.kind, "M": int(M),
            "N": int(wl.N), "K": int(K), "valid_rows": rows,
-           "scales": "mx_e8m0_1x32" if args.mx else ("ue8m0" if ue8m0 else "fp32"),
-           "step": ("quant_mx(X) + quant_mx(W) + MXFP8 GEMM" if args.mx else
+           "scales": "mx_e8m0_1x32" if mx else ("ue8m0" if ue8m0 else "fp32"),
+           "step": ("quant_mx(X) + quant_mxfp4(W) + MXFP8 x MXFP4 GEMM" if args.w4 else
+                    "quant_mx(X) + quant_mx(W) + MXFP8 GEMM" if args.mx else
                     "quant_1x128(X) + quant_128x128(W) + block-scaled GEMM")}
     if wl.kind != "dense":
         cfg["experts"] = int(wl.E)
@@ -388,7 +411,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        "dtype": "fp8_e4m3 x fp4_e2m1" if args.w4 else "fp8_e4m3",
         "data": "synthetic",
         "config": cfg,
         "roofline": roof,

@@ -43,6 +43,8 @@ SYMBOLS = (
     "fp8_grouped_gemm_masked",
     "fp8_quant_mx",
     "fp8_gemm_nt_mx",
+    "fp8_quant_mxfp4",
+    "fp8_gemm_nt_mx_w4",
     "fp8_get_mk_alignment_for_contiguous_layout",
     "fp8_status_string",
 )
@@ -75,9 +77,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fp8_grouped_gemm_masked.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, U32, P]
     L.fp8_quant_mx.argtypes = [P, I64, I64, P, P, P]
     L.fp8_gemm_nt_mx.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
+    L.fp8_quant_mxfp4.argtypes = [P, I64, I64, P, P, P]
+    L.fp8_gemm_nt_mx_w4.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
     for fn in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_gemm_nt",
                "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked", "fp8_quant_mx",
-               "fp8_gemm_nt_mx"):
+               "fp8_gemm_nt_mx", "fp8_quant_mxfp4", "fp8_gemm_nt_mx_w4"):
         getattr(L, fn).restype = ctypes.c_int
     L.fp8_get_mk_alignment_for_contiguous_layout.argtypes = []
     L.fp8_get_mk_alignment_for_contiguous_layout.restype = I32
@@ -244,4 +248,36 @@ def gemm_nt_mx(xq, ea, wq, eb, out=None) -> torch.Tensor:
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     _check("fp8_gemm_nt_mx", L.fp8_gemm_nt_mx(_ptr(xq), _ptr(ea), _ptr(wq), _ptr(eb), _ptr(y),
                                               M, N, K, 0, _stream(xq)))
+    return y
+
+
+def quant_mxfp4(w: torch.Tensor, out=None):
+    """MXFP4 weights: w fp32 (R, K) -> (q uint8 (R, K/2), two E2M1 nibbles per
+    byte, the even element low; e int32 (K/128, R) packed scale bytes)."""
+    L = load_library()
+    _need(w, "w", torch.float32, 2)
+    R, K = w.shape
+    if out is None:
+        q = torch.empty((R, K // 2), dtype=torch.uint8, device=w.device)
+        e = torch.empty((K // 128, R), dtype=torch.int32, device=w.device)
+    else:
+        q, e = out
+    _check("fp8_quant_mxfp4", L.fp8_quant_mxfp4(_ptr(w), R, K, _ptr(q), _ptr(e), _stream(w)))
+    return q, e
+
+
+def gemm_nt_mx_w4(xq, ea, wq, eb, out=None) -> torch.Tensor:
+    """Y (M, N) bf16 = MXFP8 X * (MXFP4 W)^T; wq (N, K/2) packed nibbles."""
+    L = load_library()
+    _need(xq, "xq", torch.uint8, 2)
+    _need(wq, "wq", torch.uint8, 2)
+    _need(ea, "ea", torch.int32, 2)
+    _need(eb, "eb", torch.int32, 2)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] * 2 != K or ea.shape != (K // 128, M) or eb.shape != (K // 128, N):
+        raise ValueError("gemm_nt_mx_w4: inconsistent operand shapes")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _check("fp8_gemm_nt_mx_w4", L.fp8_gemm_nt_mx_w4(_ptr(xq), _ptr(ea), _ptr(wq), _ptr(eb), _ptr(y),
+                                                    M, N, K, 0, _stream(xq)))
     return y

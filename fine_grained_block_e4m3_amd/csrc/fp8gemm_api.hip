@@ -128,6 +128,13 @@ fp8_status run_gemm_mx(const fp8k::GemmParams& p, hipStream_t stream) {
     return dispatch_gemm<fp8k::kDense, fp8k::kPathMx>(p, cus, stream);
 }
 
+fp8_status run_gemm_mx_w4(const fp8k::GemmParams& p, hipStream_t stream) {
+    int cus = 0;
+    fp8_status st = current_device_cus(&cus);
+    if (st != FP8_OK) return st;
+    return dispatch_gemm<fp8k::kDense, fp8k::kPathMxW4>(p, cus, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -227,6 +234,41 @@ fp8_status fp8_gemm_nt_mx(const uint8_t* xq, const uint32_t* ea, const uint8_t* 
     p.sb = reinterpret_cast<const float*>(eb);
     p.M = M; p.N = N; p.K = K; p.E = 1;
     return run_gemm_mx(p, (hipStream_t)stream);
+}
+
+fp8_status fp8_quant_mxfp4(const float* x, int64_t R, int64_t K, uint8_t* q, uint32_t* e, void* stream) {
+    if (!dims_ok(R) || !dims_ok(K)) return FP8_ERR_INVALID_ARG;
+    if (K % 128) return FP8_ERR_SHAPE;
+    if (R == 0 || K == 0) return FP8_OK;
+    if (!x || !q || !e) return FP8_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(e)) return FP8_ERR_ALIGNMENT;
+    int cus = 0;
+    fp8_status st = current_device_cus(&cus);
+    if (st != FP8_OK) return st;
+    const int64_t units = R * ((K / 32 + 31) / 32);
+    const int64_t blocks = (units + 3) / 4;
+    if (blocks > 0x7FFFFFFF) return FP8_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(fp8k::quant_mxfp4_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       x, q, reinterpret_cast<uint8_t*>(e), R, K, units);
+    return launch_status();
+}
+
+fp8_status fp8_gemm_nt_mx_w4(const uint8_t* xq, const uint32_t* ea, const uint8_t* wq, const uint32_t* eb,
+                             uint16_t* y, int64_t M, int64_t N, int64_t K, uint32_t flags, void* stream) {
+    if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K) || flags != 0) return FP8_ERR_INVALID_ARG;
+    if (K % 128) return FP8_ERR_SHAPE;
+    if (K > kMaxGemmK) return FP8_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return FP8_OK;
+    if (K == 0) return FP8_ERR_SHAPE;
+    if (!xq || !ea || !wq || !eb || !y) return FP8_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(ea) || !aligned16(eb))
+        return FP8_ERR_ALIGNMENT;
+    fp8k::GemmParams p{};
+    p.xq = xq; p.wq = wq; p.y = y;
+    p.sa = reinterpret_cast<const float*>(ea);
+    p.sb = reinterpret_cast<const float*>(eb);
+    p.M = M; p.N = N; p.K = K; p.E = 1;
+    return run_gemm_mx_w4(p, (hipStream_t)stream);
 }
 
 fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sb,

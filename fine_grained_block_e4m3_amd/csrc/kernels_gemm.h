@@ -63,7 +63,12 @@ enum GemmMode : int { kDense = 0, kContiguous = 1, kMasked = 2 };
 //                  4 to a dword per (K block, row) in [K/128][rows] tables.
 //                  Each lane passes the byte of the 32-group it holds as its
 //                  scale operand and the matrix core accumulates over all of K.
-enum GemmPath : int { kPathFp8 = 0, kPathFp8Pow2 = 1, kPathF16 = 2, kPathF16Pow2 = 3, kPathMx = 4 };
+//   kPathMxW4      as kPathMx with W in MXFP4: E2M1 nibbles, two per byte along
+//                  K (tcgen05 page, sections 6.3 and the operand-major notes),
+//                  64 bytes per row and K block; the instruction's A operand
+//                  in E2M1 format.
+enum GemmPath : int { kPathFp8 = 0, kPathFp8Pow2 = 1, kPathF16 = 2, kPathF16Pow2 = 3, kPathMx = 4,
+                      kPathMxW4 = 5 };
 
 // Operand pointers (passed to the kernel as separate __restrict__ arguments):
 //   xq (M, K) codes; masked: (E*max_m, K)
@@ -230,11 +235,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     constexpr int TN = BN / WAVES_N;   // wave tile columns (n)
     constexpr int FI = TM / 16;        // 16x16 subtiles per wave along m
     constexpr int FJ = TN / 16;        // ... along n
+    // W with E2M1 elements: 64 bytes per row and K block instead of 128
+    constexpr bool kW4 = PATH == kPathMxW4;
+    constexpr int WROW = kW4 ? 64 : 128;
     constexpr int XLOADS = BM / 8 / NWAVES;   // 1 KB direct-to-LDS loads per wave per stage
     // W rows come in 8-row groups; when they do not split evenly over the
     // waves, the last waves' loads fall past the tile (the range check reads
     // zeros) and land in a spare LDS area, so every wave issues as many.
-    constexpr int WGROUPS = BN / 8;
+    constexpr int WGROUPS = BN * WROW / 1024;
     constexpr int WLOADS = (WGROUPS + NWAVES - 1) / NWAVES;
     constexpr int W_WAVES = WGROUPS / WLOADS;   // waves loading rows of the tile
     constexpr int NPIECE = XLOADS + WLOADS + 1;   // loads per wave per stage
@@ -248,7 +256,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     // The operand base lives in the per-lane address and the stage offset in
     // the ds_read immediate.
     constexpr int W_BASE = STAGES * BM * 128;
-    constexpr int SC_BASE = W_BASE + STAGES * BN * 128;
+    constexpr int SC_BASE = W_BASE + STAGES * BN * WROW;
     constexpr int SPARE_BASE = SC_BASE + STAGES * NWAVES * 256;
     constexpr int LDS_BYTES = SPARE_BASE + (W_WAVES < NWAVES ? WLOADS * 1024 : 0);
     // A wave's 16-wide n subtiles all lie in one 128-row weight block when its
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     // most two weight blocks: the K loop is specialised on the subtile where
     // the second one starts, so that the promotion scales are two products
     // per resident fragment and block instead of one per subtile.
-    constexpr bool kMx = PATH == kPathMx;
+    constexpr bool kMx = PATH == kPathMx || PATH == kPathMxW4;
     // scales as E8M0 operands of the scaled MFMA; K accumulated in the matrix core
     constexpr bool kScaledMfma = PATH == kPathFp8Pow2 || kMx;
     // a scale as carried through the pipeline: the FP32 value, or (MX) the
@@ -274,7 +282,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 subtiles");
     static_assert(BM % 64 == 0 && NSA < NWAVES, "activation scales: 64 rows per wave, one wave left for sB");
     static_assert(BN / 128 + 2 <= 64, "one scale load covers the tile's weight blocks");
-    static_assert(BM % (8 * NWAVES) == 0 && BN % 8 == 0 && WGROUPS % WLOADS == 0, "tile rows per wave");
+    static_assert(BM % (8 * NWAVES) == 0 && (BN * WROW) % 1024 == 0 && WGROUPS % WLOADS == 0,
+                  "tile rows per wave");
     static_assert(XLOADS >= 1 && XLOADS <= 4 && WLOADS >= 1 && WLOADS <= 4, "loads per wave");
     static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS holds the stage ring");
     static_assert((STAGES - 2) * PER_STAGE <= 63, "vmcnt range");
@@ -331,7 +340,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 #pragma unroll
     for (int q = 0; q < WLOADS; ++q) {
         const int grp = wave * WLOADS + q;
-        vw[q] = (lane_off ^ (uint32_t)(cperm(grp & 1) << 4)) + (uint32_t)(grp * 8 * K) - 1024u * q;
+        if constexpr (kW4) {
+            // E2M1 rows of 64 bytes: a load fills 16 rows; lane l writes slot
+            // l%4 of row R0 + l/4, which holds chunk slot ^ swz4(row) with
+            // swz4(r) = (r/4) mod 4 = (l/16) mod 4 for R0 a multiple of 16
+            const uint32_t off4 = (uint32_t)((lane >> 2) * (K / 2)) | (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+            vw[q] = off4 + (uint32_t)(grp * 16 * (K / 2)) - 1024u * q;
+        } else {
+            vw[q] = (lane_off ^ (uint32_t)(cperm(grp & 1) << 4)) + (uint32_t)(grp * 8 * K) - 1024u * q;
+        }
     }
     // LDS fragment addresses within a stage: row r, 16-byte chunk c at
     // r*128 + 16*(c ^ swz(r)); this lane reads chunks 2g and 2g+1.
@@ -362,6 +379,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         xa[h] = (uint32_t)((wm * TM + r) * 128 + ((ch ^ lds_swz(r)) << 4));
         wa[h] = (uint32_t)(W_BASE + (wn * TN + r) * 128 + ((ch ^ lds_swz(r)) << 4));
     }
+    // E2M1 W: an FP4 operand lane holds 32 consecutive K of its hardware
+    // scale block g (measured: nibble t is K 32g + t, low nibble first, with
+    // the scale of lane group g).  Against the X operand's order above that
+    // is data group mx_grp: one 16-byte chunk of the row's 64 bytes, read
+    // from its swizzled slot mx_grp ^ (r/4 mod 4).
+    const uint32_t wa4 = (uint32_t)(W_BASE + (wn * TN + (lane & 15)) * 64 + ((mx_grp ^ (((lane & 15) >> 2) & 3)) << 4));
     // activation scale of row r of the tile at SC + 4r; weight scales at
     // SC + 256*NSA + 4*slot (the first copy)
     // (MX: the row's dword of 4 group bytes; this lane takes byte mx_grp, the
@@ -385,7 +408,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     // w_dst + s*w_sstride, or the spare area (every stage) for a wave past them
     const bool w_wave = W_WAVES == NWAVES || wave < W_WAVES;
     const uint32_t w_dst = w_wave ? (uint32_t)(W_BASE + wave * WLOADS * 1024) : (uint32_t)SPARE_BASE;
-    const uint32_t w_sstride = w_wave ? (uint32_t)(BN * 128) : 0u;
+    const uint32_t w_sstride = w_wave ? (uint32_t)(BN * WROW) : 0u;
 
     // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs,
     // so workgroup b of a wave of G lands on XCD b%8.  Give each XCD a run of
@@ -448,7 +471,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 
         // Buffer resources of this tile: rows past the valid range read zeros.
         const i32x4 xr = make_rsrc(xq_ + row0 * K, (uint32_t)(rows_valid * K));
-        const i32x4 wr = make_rsrc(wq + n0 * K, (uint32_t)(cols_valid * K));
+        const int64_t KW = kW4 ? K / 2 : K;   // bytes per W row
+        const i32x4 wr = make_rsrc(wq + n0 * KW, (uint32_t)(cols_valid * KW));
         const float* sa_row0 = sa_ + row0;
         // Weight scales: lane l of a wave's scale load fetches block row
         // nb0 + l; rows past the last weight block read zero.
@@ -495,7 +519,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         struct StageLoads {
             uint32_t xm0, wm0, sm0;
             i32x4 xr, wr, sr;
-            int koff, soff;
+            int koff, wkoff, soff;
         };
         auto stage_loads = [&](int kb, auto bufc) {
             constexpr uint32_t s = decltype(bufc)::value;
@@ -515,13 +539,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             L.sr = i32x4{(int)(uint32_t)scb, (int)(uint32_t)(scb >> 32) & 0xFFFF, (int)sc_rec & live,
                          0x00020000};
             L.koff = kb * 128;
+            L.wkoff = kb * WROW;
             L.soff = kb * sc_step;
             return L;
         };
         auto issue_piece = [&](const StageLoads& L, auto pc) {
             constexpr int P = decltype(pc)::value;
             if constexpr (P < XLOADS) dma_lds16_one<P>(L.xm0, vx[P], L.xr, L.koff);
-            else if constexpr (P < XLOADS + WLOADS) dma_lds16_one<P - XLOADS>(L.wm0, vw[P - XLOADS], L.wr, L.koff);
+            else if constexpr (P < XLOADS + WLOADS) dma_lds16_one<P - XLOADS>(L.wm0, vw[P - XLOADS], L.wr, L.wkoff);
             else dma_lds4(L.sm0, sc_voff, L.sr, L.soff);
         };
 
@@ -549,7 +574,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         constexpr int RB = R - 2;   // row before which the barrier of a block sits
         auto read_x = [&](int buf, int i) { return lds_frag(smem + buf * BM * 128 + 2048 * i, xa[0], xa[1]); };
         // (wa already holds the W region's base)
-        auto read_w = [&](int buf, int j) { return lds_frag(smem + buf * BN * 128 + 2048 * j, wa[0], wa[1]); };
+        auto read_w = [&](int buf, int j) {
+            if constexpr (kW4) {
+                // 16 bytes (32 E2M1 values); the instruction reads 4 registers
+                const i32x2 lo = *reinterpret_cast<const i32x2*>(smem + buf * BN * 64 + 1024 * j + wa4);
+                const i32x2 hi = *reinterpret_cast<const i32x2*>(smem + buf * BN * 64 + 1024 * j + wa4 + 8);
+                return i32x8{lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
+            } else {
+                return lds_frag(smem + buf * BN * 128 + 2048 * j, wa[0], wa[1]);
+            }
+        };
         auto read_sa = [&](int buf, int i) -> ScaleT {
             if constexpr (kMx)
                 return (int)__builtin_amdgcn_ubfe(
@@ -753,12 +787,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
                         // operand A is the W fragment, B the X fragment
+                        // operand format of A (W): 0 E4M3, 4 E2M1; B (X) is E4M3
+                        constexpr int kFmtA = kW4 ? 4 : 0;
                         if constexpr (kStreamW)
                             accr(r, c) = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                fc, res[c], accr(r, c), 0, 0, 0, ste, 0, rse[c]);
+                                fc, res[c], accr(r, c), kFmtA, 0, 0, ste, 0, rse[c]);
                         else
                             accr(r, c) = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                res[c], fc, accr(r, c), 0, 0, 0, rse[c], 0, ste);
+                                res[c], fc, accr(r, c), kFmtA, 0, 0, rse[c], 0, ste);
                         if constexpr (r == R - 1) res[c] = read_res(NBUF, c);
                     }
                 } else {

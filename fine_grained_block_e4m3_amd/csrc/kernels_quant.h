@@ -195,4 +195,69 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const float* __restrict__
     else quant_mx_unit<true>(x, q, e, R, K, G, r, g0, lane);
 }
 
+// E2M1 code of a binary32 value: round to nearest, ties to the even code,
+// magnitudes above 6 to 6, the sign kept (E2M1 magnitudes 0, 0.5, 1, 1.5, 2,
+// 3, 4, 6 for codes 0..7).  Counting the decision points passed: a tie
+// between codes c and c+1 is kept at c when c is even (strict >) and moved
+// up when c is odd (>=).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+    const float a = fabsf(v);
+    const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+    return m | ((__float_as_uint(v) >> 28) & 0x8u);
+}
+
+// MXFP4 quantizer for weights: E2M1 elements with one E8M0 scale per 1x32
+// group along K (tcgen05 page, section 6.3), the scale being the power of two
+// at or above max(amax, 1e-4)/6 (6 = the largest E2M1 magnitude), so no
+// element saturates.  Elements are packed two per byte along K, the even one
+// in the low nibble.  Same wave units as the MXFP8 quantizer: one row and up
+// to 32 groups per wave, 8 lanes per group; each lane packs its 4 values into
+// 2 bytes.  The scale bytes go into the packed [K/128][R] dwords.
+//   x (R, K) fp32 -> q (R, K/2) u8, e u32 [K/128][R]
+template <bool PARTIAL>
+__device__ __forceinline__ void quant_mxfp4_unit(const float* __restrict__ x, uint8_t* __restrict__ q,
+                                                 uint8_t* __restrict__ e, int64_t R, int64_t K, int64_t G,
+                                                 int64_t r, int64_t g0, int lane) {
+    const int64_t off = r * K + g0 * 32 + lane * 4;
+    f32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (!PARTIAL || g0 + 8 * i + (lane >> 3) < G) v[i] = load_stream(x + off + 256 * i);
+        else v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t grp = g0 + 8 * i + (lane >> 3);
+        float amax = abs_max4(v[i]);
+#pragma unroll
+        for (int o = 4; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 8));
+        const float a = amax > 1e-4f ? amax : 1e-4f;
+        uint32_t bits = __float_as_uint(a / 6.0f);
+        if (bits & 0x007FFFFFu) bits = ((bits >> 23) + 1u) << 23;
+        const float s = __uint_as_float(bits);
+        if (!PARTIAL || grp < G) {
+            const uint32_t p = e2m1_code(v[i][0] / s) | (e2m1_code(v[i][1] / s) << 4) |
+                               (e2m1_code(v[i][2] / s) << 8) | (e2m1_code(v[i][3] / s) << 12);
+            *reinterpret_cast<uint16_t*>(q + off / 2 + 128 * i) = (uint16_t)p;
+            if ((lane & 7) == 0) e[((grp >> 2) * R + r) * 4 + (grp & 3)] = (uint8_t)(bits >> 23);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ e, int64_t R, int64_t K,
+                                                          int64_t units) {
+    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (u >= units) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t G = K / 32;
+    const int64_t upr = (G + 31) / 32;
+    const int64_t r = u / upr;
+    const int64_t g0 = (u - r * upr) * 32;
+    if (g0 + 32 <= G) quant_mxfp4_unit<false>(x, q, e, R, K, G, r, g0, lane);
+    else quant_mxfp4_unit<true>(x, q, e, R, K, G, r, g0, lane);
+}
+
 }  // namespace fp8k

@@ -182,6 +182,36 @@ fp8_status fp8_gemm_nt_mx(const uint8_t* xq, const uint32_t* ea,
                           int64_t M, int64_t N, int64_t K, uint32_t flags,
                           void* stream);
 
+/*
+ * MXFP4 weight quantizer ([TC] 6.3: MXFP4 = E2M1 elements with one E8M0 scale
+ * per 32; [TC] notes on operand majors: two 4-bit values are packed per byte
+ * along K).  The scale of a group is the power of two at or above
+ * max(amax, 1e-4) / 6, 6 being the largest E2M1 magnitude (a reading, as for
+ * MXFP8), so no element saturates; elements round to nearest, ties to even.
+ *   x  fp32 (R, K)          input, K % 128 == 0
+ *   q  u8   (R, K/2)        output: element k of a row in byte k/2, the even
+ *                           one in the low nibble (E2M1: sign bit 3,
+ *                           exponent bits 2..1, mantissa bit 0)
+ *   e  u32  [K/128][R]      output scales, packed as by fp8_quant_mx
+ */
+fp8_status fp8_quant_mxfp4(const float* x, int64_t R, int64_t K, uint8_t* q,
+                           uint32_t* e, void* stream);
+
+/*
+ * Dense NT GEMM with MXFP8 activations and MXFP4 weights (weight-only 4-bit
+ * decode: half the weight bytes of MXFP8):
+ *   Y[m][n] = sum_g 2^(ea(m,g)-127) * 2^(eb(n,g)-127)
+ *                   * sum_{k in group g} xq[m][k] * E2M1(wq, n, k)
+ *   xq u8 (M,K), ea u32 [K/128][M] (fp8_quant_mx), wq u8 (N, K/2),
+ *   eb u32 [K/128][N] (fp8_quant_mxfp4), y bf16 bits (M,N); K % 128 == 0.
+ *   The scaled matrix instruction takes W as an E2M1 operand and each lane's
+ *   group scale; the K sum stays in its FP32 accumulator.  flags must be 0.
+ */
+fp8_status fp8_gemm_nt_mx_w4(const uint8_t* xq, const uint32_t* ea,
+                             const uint8_t* wq, const uint32_t* eb, uint16_t* y,
+                             int64_t M, int64_t N, int64_t K, uint32_t flags,
+                             void* stream);
+
 /* M alignment every expert segment of the contiguous layout must have
  * ([DG] "分组 GEMM 的两种布局": the alignment query).  Returns 128. */
 int32_t fp8_get_mk_alignment_for_contiguous_layout(void);

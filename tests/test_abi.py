@@ -118,6 +118,20 @@ def test_mx_validation(L):
     assert g(A, A, A, A, A, 0, 8, 128, 0, None) == OK
 
 
+def test_mxfp4_validation(L):
+    q = L.fp8_quant_mxfp4
+    assert q(None, 4, 128, A, A, None) == INVALID
+    assert q(A, 4, 96, A, A, None) == SHAPE
+    assert q(A, 4, 128, MIS, A, None) == ALIGN
+    assert q(A, 0, 128, None, None, None) == OK
+    g = L.fp8_gemm_nt_mx_w4
+    assert g(A, A, A, A, A, 4, 8, 128, 2, None) == INVALID
+    assert g(A, A, None, A, A, 4, 8, 128, 0, None) == INVALID
+    assert g(A, A, A, A, A, 4, 8, 64, 0, None) == SHAPE
+    assert g(A, A, MIS, A, A, 4, 8, 128, 0, None) == ALIGN
+    assert g(A, A, A, A, A, 4, 0, 128, 0, None) == OK
+
+
 def test_no_device_reported_without_gpu(L):
     import torch
     if torch.cuda.is_available():
@@ -126,6 +140,8 @@ def test_no_device_reported_without_gpu(L):
     assert L.fp8_quant_1x128(A, 4, 128, A, A, 0, None) == NODEV
     assert L.fp8_quant_mx(A, 4, 128, A, A, None) == NODEV
     assert L.fp8_gemm_nt_mx(A, A, A, A, A, 4, 8, 128, 0, None) == NODEV
+    assert L.fp8_quant_mxfp4(A, 4, 128, A, A, None) == NODEV
+    assert L.fp8_gemm_nt_mx_w4(A, A, A, A, A, 4, 8, 128, 0, None) == NODEV
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,137 @@
+"""GPU MXFP4-weight path (E2M1 weights, one E8M0 scale per 1x32 group; MXFP8
+activations) against the oracle.
+
+The weight quantizer is bit-exact (nibbles and scale bytes; the library packs
+the scale bytes into [K/128][rows] dwords).  The GEMM runs the scaled matrix
+instruction with an E2M1 A operand; it is held to the tolerance or to the FP8
+truncation-model bound (per group of 8 K: 2^-10 of the group's largest
+product), and bit-exact where the result is exactly representable."""
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_block_e4m3_amd as fp8
+import oracle
+import workloads
+from gpu_helpers import assert_close_or_bounded, bf16_bits, bf16_to_f64, check_guards, dev, guarded, host, say
+from test_gpu_mx import pack_scales, unpack_scales
+
+pytestmark = pytest.mark.gpu
+
+DEC8 = oracle.e4m3_decode(np.arange(256))
+DEC4 = oracle.e2m1_decode(np.arange(16))
+
+
+def unpack_nibbles(q):
+    return np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[0], -1)
+
+
+def w4_bound(xq, ea, wq, eb, ref):
+    M, K = xq.shape
+    N = wq.shape[0]
+    xd = np.abs(DEC8[xq]) * np.repeat(np.ldexp(1.0, ea.astype(np.int64) - 127), 32, axis=1)
+    wd = np.abs(DEC4[unpack_nibbles(wq)]) * np.repeat(np.ldexp(1.0, eb.astype(np.int64) - 127), 32, axis=1)
+    amax = xd.reshape(M, K // 8, 8).max(axis=2)
+    bmax = wd.reshape(N, K // 8, 8).max(axis=2)
+    return 2.0 ** -8 * np.abs(ref) + 1.01 * 2.0 ** -10 * (amax @ bmax.T) + 2.0 ** -16 * (xd @ wd.T)
+
+
+def run_w4(xq, ea, wq, eb, guard=2048):
+    M, K = xq.shape
+    N = wq.shape[0]
+    say(f"gemm_nt_mx_w4 M={M} N={N} K={K}")
+    full, y = guarded((M, N), guard)
+    fp8.gemm_nt_mx_w4(dev(xq), dev(pack_scales(ea)), dev(wq), dev(pack_scales(eb)), out=y)
+    torch.cuda.synchronize()
+    check_guards(full, M * N, guard)
+    return bf16_bits(y)
+
+
+@pytest.mark.parametrize("R,K", [(96, 512), (1, 128), (300, 1024), (9, 7168), (33, 1152), (5, 2176)])
+def test_quant_mxfp4_bitexact(R, K):
+    wl = workloads.dense(1, R, K, seed=400 + R, outlier_frac=0.01, outlier_mult=50.0)
+    q_ref, e_ref = oracle.quant_mxfp4(wl.w)
+    say(f"quant_mxfp4 R={R} K={K}")
+    q, e = fp8.quant_mxfp4(dev(wl.w))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(unpack_scales(host(e)), e_ref)
+
+
+def test_quant_mxfp4_ties_signs_and_zero_groups():
+    """Every E2M1 midpoint (a tie) and its neighbours, with both signs, in
+    groups whose scale is 1 (amax 6); a zero group; a -0 entry."""
+    mags = DEC4[:8]
+    mids = (mags[:-1] + mags[1:]) / 2
+    vals = np.concatenate([mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(7)), mags]).astype(np.float32)
+    row = np.zeros(256, np.float32)
+    for g in range(8):
+        row[32 * g] = 6.0                       # scale 1 for the group
+        chunk = vals[(31 * g) % len(vals):][:31]
+        row[32 * g + 1:32 * g + 1 + len(chunk)] = chunk * (1 if g % 2 == 0 else -1)
+    x = np.stack([row, np.zeros(256, np.float32), -row])
+    x[1, 5] = -0.0
+    q_ref, e_ref = oracle.quant_mxfp4(x)
+    q, e = fp8.quant_mxfp4(dev(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q), q_ref) and np.array_equal(unpack_scales(host(e)), e_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 288, 1536), (128, 256, 512), (1, 96, 128), (200, 300, 384),
+                                   (257, 129, 256), (600, 1000, 1024)])
+def test_gemm_mx_w4_every_element(M, N, K):
+    wl = workloads.dense(M, N, K, seed=M + 3 * N, outlier_frac=0.01, outlier_mult=50.0)
+    xq, ea = oracle.quant_mx(wl.x)
+    wq, eb = oracle.quant_mxfp4(wl.w)
+    y = run_w4(xq, ea, wq, eb)
+    ref = oracle.gemm_mx_w4(xq, ea, wq, eb)
+    assert_close_or_bounded(y, ref, w4_bound(xq, ea, wq, eb, ref), f"w4 {M}x{N}x{K}")
+
+
+def test_gemm_mx_w4_integer_products_are_exact():
+    rng = np.random.default_rng(10)
+    M, N, K = 96, 160, 256
+    xq = rng.choice(np.array([0x00, 0x38, 0x40, 0xB8, 0xC0], np.uint8), (M, K)).astype(np.uint8)
+    nib = rng.choice(np.array([0, 2, 4, 10, 12], np.uint8), (N, K))            # 0, 1, 2, -1, -2
+    wq = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    ea = np.full((M, K // 32), 129, np.uint8)
+    eb = np.full((N, K // 32), 125, np.uint8)
+    y = run_w4(xq, ea, wq, eb)
+    ref = oracle.gemm_mx_w4(xq, ea, wq, eb)
+    assert np.all(np.abs(ref) <= 256)
+    assert np.array_equal(bf16_to_f64(y), ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(2500, 7050, 640), (1900, 8102, 640)])
+def test_gemm_mx_w4_large_tiles_sampled(M, N, K):
+    wl = workloads.dense(M, N, K, seed=M + N + 1, outlier_frac=0.001, outlier_mult=100.0)
+    xq, ea = oracle.quant_mx(wl.x)
+    wq, eb = oracle.quant_mxfp4(wl.w)
+    y = run_w4(xq, ea, wq, eb)
+    rng = np.random.default_rng(7)
+    em = np.arange(M - (M % 256 if M % 256 else 256), M)
+    en = np.arange(N - 200, N)
+    mi = np.concatenate([rng.integers(0, M, 20000), np.repeat(em, 8), rng.integers(0, M, 8 * len(en))])
+    ni = np.concatenate([rng.integers(0, N, 20000), rng.integers(0, N, 8 * len(em)), np.repeat(en, 8)])
+    ref = oracle.gemm_mx_w4_elems(xq, ea, wq, eb, mi, ni)
+    xd = np.abs(DEC8[xq[mi]]) * np.repeat(np.ldexp(1.0, ea.astype(np.int64) - 127), 32, axis=1)[mi]
+    wd = np.abs(DEC4[unpack_nibbles(wq[ni])]) * np.repeat(np.ldexp(1.0, eb.astype(np.int64) - 127), 32, axis=1)[ni]
+    g8 = lambda a: a.reshape(a.shape[0], K // 8, 8).max(axis=2)
+    bound = 2.0 ** -8 * np.abs(ref) + 1.01 * 2.0 ** -10 * np.sum(g8(xd) * g8(wd), axis=1) \
+        + 2.0 ** -16 * np.sum(xd * wd, axis=1)
+    assert_close_or_bounded(y[mi, ni], ref, bound, f"w4 {M}x{N}x{K} sampled")
+
+
+def test_gemm_mx_w4_end_to_end_from_fp32():
+    wl = workloads.dense(256, 512, 1024, seed=23, outlier_frac=0.001, outlier_mult=100.0)
+    xq, ea = fp8.quant_mx(dev(wl.x))
+    wq, eb = fp8.quant_mxfp4(dev(wl.w))
+    y = fp8.gemm_nt_mx_w4(xq, ea, wq, eb)
+    torch.cuda.synchronize()
+    rx, rea = oracle.quant_mx(wl.x)
+    rw, reb = oracle.quant_mxfp4(wl.w)
+    assert np.array_equal(host(xq), rx) and np.array_equal(unpack_scales(host(ea)), rea)
+    assert np.array_equal(host(wq), rw) and np.array_equal(unpack_scales(host(eb)), reb)
+    ref = oracle.gemm_mx_w4(rx, rea, rw, reb)
+    assert_close_or_bounded(bf16_bits(y), ref, w4_bound(rx, rea, rw, reb, ref), "w4 e2e")
