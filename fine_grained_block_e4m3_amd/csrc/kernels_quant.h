@@ -174,8 +174,10 @@ __device__ __forceinline__ void quant_mx_unit(const float* __restrict__ x, uint8
 #pragma unroll
         for (int o = 4; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 8));
         const float s = group_scale(amax, true);
+        // s is a power of two: 1/s is exact, and so is x * (1/s) = x / s
+        const float inv = 1.0f / s;
         if (!PARTIAL || grp < G) {
-            store_codes(q + off + 256 * i, cvt_e4m3x4(v[i][0] / s, v[i][1] / s, v[i][2] / s, v[i][3] / s));
+            store_codes(q + off + 256 * i, cvt_e4m3x4(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv));
             if ((lane & 7) == 0) e[((grp >> 2) * R + r) * 4 + (grp & 3)] = (uint8_t)(__float_as_uint(s) >> 23);
         }
     }
@@ -195,17 +197,14 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const float* __restrict__
     else quant_mx_unit<true>(x, q, e, R, K, G, r, g0, lane);
 }
 
-// E2M1 code of a binary32 value: round to nearest, ties to the even code,
-// magnitudes above 6 to 6, the sign kept (E2M1 magnitudes 0, 0.5, 1, 1.5, 2,
-// 3, 4, 6 for codes 0..7).  Counting the decision points passed: a tie
-// between codes c and c+1 is kept at c when c is even (strict >) and moved
-// up when c is odd (>=).
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-    const float a = fabsf(v);
-    const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                       (uint32_t)(a > 5.0f);
-    return m | ((__float_as_uint(v) >> 28) & 0x8u);
+// Two binary32 values to a byte of two E2M1 nibbles (the first one low) with
+// the hardware converter at scale 1: round to nearest, ties to the even code,
+// the sign kept -- checked bit-exact against the reference encoder on every
+// E2M1 midpoint and its neighbours, both signs.  (E2M1 magnitudes: 0, 0.5, 1,
+// 1.5, 2, 3, 4, 6 for codes 0..7.)  sel picks the byte of `old` written.
+__device__ __forceinline__ uint32_t cvt_e2m1x2(uint32_t old, float a, float b, int sel) {
+    return sel == 0 ? __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 0)
+                    : __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 1);
 }
 
 // MXFP4 quantizer for weights: E2M1 elements with one E8M0 scale per 1x32
@@ -236,10 +235,11 @@ __device__ __forceinline__ void quant_mxfp4_unit(const float* __restrict__ x, ui
         const float a = amax > 1e-4f ? amax : 1e-4f;
         uint32_t bits = __float_as_uint(a / 6.0f);
         if (bits & 0x007FFFFFu) bits = ((bits >> 23) + 1u) << 23;
-        const float s = __uint_as_float(bits);
+        // a power of two: 1/s is exact, and so is x * (1/s) = x / s
+        const float inv = 1.0f / __uint_as_float(bits);
         if (!PARTIAL || grp < G) {
-            const uint32_t p = e2m1_code(v[i][0] / s) | (e2m1_code(v[i][1] / s) << 4) |
-                               (e2m1_code(v[i][2] / s) << 8) | (e2m1_code(v[i][3] / s) << 12);
+            const uint32_t p = cvt_e2m1x2(cvt_e2m1x2(0u, v[i][0] * inv, v[i][1] * inv, 0),
+                                          v[i][2] * inv, v[i][3] * inv, 1);
             *reinterpret_cast<uint16_t*>(q + off / 2 + 128 * i) = (uint16_t)p;
             if ((lane & 7) == 0) e[((grp >> 2) * R + r) * 4 + (grp & 3)] = (uint8_t)(bits >> 23);
         }
