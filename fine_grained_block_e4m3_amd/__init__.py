@@ -39,6 +39,7 @@ SYMBOLS = (
     "fp8_quant_1x128",
     "fp8_quant_128x128",
     "fp8_gemm_nt",
+    "fp8_gemm_nt_qout",
     "fp8_grouped_gemm_contiguous",
     "fp8_grouped_gemm_masked",
     "fp8_quant_mx",
@@ -73,13 +74,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fp8_quant_1x128.argtypes = [P, I64, I64, P, P, U32, P]
     L.fp8_quant_128x128.argtypes = [P, I64, I64, P, P, U32, P]
     L.fp8_gemm_nt.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
+    L.fp8_gemm_nt_qout.argtypes = [P, P, P, P, P, P, I64, I64, I64, U32, P]
     L.fp8_grouped_gemm_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, U32, P]
     L.fp8_grouped_gemm_masked.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, U32, P]
     L.fp8_quant_mx.argtypes = [P, I64, I64, P, P, P]
     L.fp8_gemm_nt_mx.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
     L.fp8_quant_mxfp4.argtypes = [P, I64, I64, P, P, P]
     L.fp8_gemm_nt_mx_w4.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
-    for fn in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_gemm_nt",
+    for fn in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_gemm_nt", "fp8_gemm_nt_qout",
                "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked", "fp8_quant_mx",
                "fp8_gemm_nt_mx", "fp8_quant_mxfp4", "fp8_gemm_nt_mx_w4"):
         getattr(L, fn).restype = ctypes.c_int
@@ -171,6 +173,29 @@ def gemm_nt(xq, sa, wq, sb, ue8m0: bool = False, precise: bool = False, out=None
     _check("fp8_gemm_nt", L.fp8_gemm_nt(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(y),
                                         M, N, K, _flags(ue8m0, precise), _stream(xq)))
     return y
+
+
+def gemm_nt_qout(xq, sa, wq, sb, ue8m0: bool = False, precise: bool = False, out=None):
+    """Block-scaled X * W^T written quantized for the next GEMM: (yq uint8
+    (M, N) E4M3 codes, sy fp32 (N/128, M) 1x128 scales); N % 128 == 0."""
+    L = load_library()
+    _need(xq, "xq", torch.uint8, 2)
+    _need(wq, "wq", torch.uint8, 2)
+    _need(sa, "sa", torch.float32, 2)
+    _need(sb, "sb", torch.float32, 2)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or sa.shape != (K // 128, M) or sb.shape != ((N + 127) // 128, K // 128):
+        raise ValueError("gemm_nt_qout: inconsistent operand shapes")
+    if out is None:
+        yq = torch.empty((M, N), dtype=torch.uint8, device=xq.device)
+        sy = torch.empty((N // 128, M), dtype=torch.float32, device=xq.device)
+    else:
+        yq, sy = out
+    _check("fp8_gemm_nt_qout", L.fp8_gemm_nt_qout(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(yq),
+                                                  _ptr(sy), M, N, K, _flags(ue8m0, precise),
+                                                  _stream(xq)))
+    return yq, sy
 
 
 def grouped_gemm_contiguous(xq, sa, wq, sb, m_indices, ue8m0: bool = False, precise: bool = False,

@@ -55,7 +55,8 @@ fp8_status launch_status() {
 // ---------------------------------------------------------------------------
 // GEMM instances.  Naming: BM x BN workgroup tile, WAVES_M x WAVES_N waves.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int MODE, int PATH, int STAGES = 2, int GROUP_M = 4>
+template <int BM, int BN, int WM, int WN, int MODE, int PATH, int STAGES = 2, int GROUP_M = 4,
+          bool QOUT = false>
 fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream) {
     p.m_tiles = (int)((MODE == fp8k::kMasked ? p.max_m : p.M) + BM - 1) / BM;
     p.n_tiles = (int)((p.N + BN - 1) / BN);
@@ -64,7 +65,7 @@ fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream) {
     if (MODE == fp8k::kMasked) tiles *= p.E;   // upper bound; the kernel counts the real ones
     int grid = (int)(tiles < cus ? tiles : cus);
     if (grid <= 0) return FP8_OK;
-    hipLaunchKernelGGL((fp8k::gemm_kernel<BM, BN, WM, WN, MODE, PATH, STAGES>), dim3(grid),
+    hipLaunchKernelGGL((fp8k::gemm_kernel<BM, BN, WM, WN, MODE, PATH, STAGES, QOUT>), dim3(grid),
                        dim3(64 * WM * WN), 0, stream, p.xq, p.sa, p.wq, p.sb, p.y, p.m_indices,
                        p.masked_m, p);
     return launch_status();
@@ -102,6 +103,32 @@ fp8_status dispatch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream)
         // (measured 94 -> 82 us on 16 experts x 256 rows, N 7168, K 2048).
         return launch_gemm<128, 256, 2, 4, MODE, PATH, 3>(p, cus, stream);
     }
+}
+
+// Quantized-output instances: 128-column output groups need a tile width of
+// 128 or 256 with 64-column waves (no 256x224, no 64x96).
+template <int PATH>
+fp8_status dispatch_qout(const fp8k::GemmParams& p, int cus, hipStream_t stream) {
+    constexpr bool kF16 = PATH == fp8k::kPathF16 || PATH == fp8k::kPathF16Pow2;
+    const int64_t huge = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+    if constexpr (!kF16)
+        if (huge >= cus) return launch_gemm<256, 256, 2, 4, fp8k::kDense, PATH, 2, 4, true>(p, cus, stream);
+    const int64_t big = ((p.M + 255) / 256) * ((p.N + 127) / 128);
+    if (big >= 2 * cus || (kF16 && huge >= cus))
+        return launch_gemm<256, 128, 4, 2, fp8k::kDense, PATH, 3, 4, true>(p, cus, stream);
+    return launch_gemm<128, 128, 2, 2, fp8k::kDense, PATH, 4, 4, true>(p, cus, stream);
+}
+
+fp8_status run_gemm_qout(const fp8k::GemmParams& p, uint32_t flags, hipStream_t stream) {
+    int cus = 0;
+    fp8_status st = current_device_cus(&cus);
+    if (st != FP8_OK) return st;
+    const bool pow2 = flags & FP8_FLAG_UE8M0, precise = flags & FP8_FLAG_PRECISE;
+    if (precise)
+        return pow2 ? dispatch_qout<fp8k::kPathF16Pow2>(p, cus, stream)
+                    : dispatch_qout<fp8k::kPathF16>(p, cus, stream);
+    return pow2 ? dispatch_qout<fp8k::kPathFp8Pow2>(p, cus, stream)
+                : dispatch_qout<fp8k::kPathFp8>(p, cus, stream);
 }
 
 template <int MODE>
@@ -287,6 +314,25 @@ fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq, co
     p.xq = xq; p.sa = sa; p.wq = wq; p.sb = sb; p.y = y;
     p.M = M; p.N = N; p.K = K; p.E = 1;
     return run_gemm<fp8k::kDense>(p, flags, (hipStream_t)stream);
+}
+
+fp8_status fp8_gemm_nt_qout(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sb,
+                            uint8_t* yq, float* sy, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                            void* stream) {
+    if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K) || (flags & ~kGemmFlags))
+        return FP8_ERR_INVALID_ARG;
+    if (K % 128 || N % 128) return FP8_ERR_SHAPE;
+    if (K > kMaxGemmK) return FP8_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return FP8_OK;
+    if (K == 0) return FP8_ERR_SHAPE;
+    if (!xq || !sa || !wq || !sb || !yq || !sy) return FP8_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(sa) || !aligned16(sb) || !aligned16(yq) ||
+        !aligned16(sy))
+        return FP8_ERR_ALIGNMENT;
+    fp8k::GemmParams p{};
+    p.xq = xq; p.sa = sa; p.wq = wq; p.sb = sb; p.yq = yq; p.sy = sy;
+    p.M = M; p.N = N; p.K = K; p.E = 1;
+    return run_gemm_qout(p, flags, (hipStream_t)stream);
 }
 
 fp8_status fp8_grouped_gemm_contiguous(const uint8_t* xq, const float* sa, const uint8_t* wq,

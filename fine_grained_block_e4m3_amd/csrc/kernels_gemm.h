@@ -83,6 +83,8 @@ struct GemmParams {
     const uint8_t* wq;
     const float* sb;
     uint16_t* y;
+    uint8_t* yq;                // quantized output (QOUT): E4M3 codes (M, N)
+    float* sy;                  // ... and its 1x128 scales [N/128][M]
     const int32_t* m_indices;
     const int32_t* masked_m;
     int64_t M;                  // rows of X (masked: E*max_m)
@@ -225,7 +227,11 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, int PATH, int STAGES>
+// QOUT: the epilogue emits the output quantized for the next GEMM -- E4M3
+// codes and one FP32 scale per 1x128 group along N, [N/128][M] -- instead of
+// BF16 (DeepGEMM page, section "为什么只做 NT 布局": the activation
+// quantization belongs fused into the kernel that produces the activations).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, int PATH, int STAGES, bool QOUT = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     const uint8_t* __restrict__ xq_, const float* __restrict__ sa_, const uint8_t* __restrict__ wq_,
     const float* __restrict__ sb_, uint16_t* __restrict__ y_, const int32_t* __restrict__ m_indices_,
@@ -258,7 +264,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     constexpr int W_BASE = STAGES * BM * 128;
     constexpr int SC_BASE = W_BASE + STAGES * BN * WROW;
     constexpr int SPARE_BASE = SC_BASE + STAGES * NWAVES * 256;
-    constexpr int LDS_BYTES = SPARE_BASE + (W_WAVES < NWAVES ? WLOADS * 1024 : 0);
+    // QOUT: the row maxima of each wave column, [WAVES_N][BM] floats
+    constexpr int QA_BASE = SPARE_BASE + (W_WAVES < NWAVES ? WLOADS * 1024 : 0);
+    constexpr int LDS_BYTES = QA_BASE + (QOUT ? WAVES_N * BM * 4 : 0);
     // A wave's 16-wide n subtiles all lie in one 128-row weight block when its
     // n range is 128-aligned inside a 128-aligned tile: one sB per K block.
     constexpr bool kUniformSb = (BN % 128 == 0 || 128 % BN == 0) && (128 % TN == 0 || TN % 128 == 0)
@@ -292,6 +300,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     constexpr int MX_XS_WAVES = BM / 64, MX_WS_WAVES = (BN + 63) / 64;
     static_assert(!kMx || (MODE == kDense && MX_XS_WAVES + MX_WS_WAVES <= NWAVES),
                   "MX: dense only, one scale load per wave");
+    static_assert(!QOUT || (MODE == kDense && !kMx && TN == 64 && BN % 128 == 0),
+                  "quantized output: dense, 128-column groups of two 64-column waves");
 
     // A ring of STAGES LDS buffers: the loads of K blocks kb+1 .. kb+STAGES-1
     // fly while block kb is used.
@@ -900,8 +910,49 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         // the loads issued past the last block were discarded; let them retire
         wait_vmcnt<0>();
 
-        // ---------------- epilogue: BF16 (RNE), predicated stores ----------------
         const int g4 = 4 * g;
+        if constexpr (QOUT) {
+            // ---------------- epilogue: E4M3 + 1x128 scales along N ----------------
+            // A 128-column group of a row spans this wave's 64 columns and
+            // those of its neighbour wn^1.  Row maximum over the wave's
+            // columns: 16 values per lane, then across the 4 lanes of the
+            // row (lanes l, l^16, l^32, l^48); the two waves of a group meet
+            // in LDS.  Scale and codes as the 1x128 quantizer defines them,
+            // applied to the FP32 accumulator.
+            float* qa = reinterpret_cast<float*>(smem + QA_BASE);
+            float own[FI];
+#pragma unroll
+            for (int i = 0; i < FI; ++i) {
+                float a = 0.f;
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                    for (int r2 = 0; r2 < 4; ++r2) a = fmaxf(a, fabsf(acc[i][j][r2]));
+                a = fmaxf(a, __shfl_xor(a, 16));
+                a = fmaxf(a, __shfl_xor(a, 32));
+                own[i] = a;
+                if (g == 0) qa[wn * BM + wm * TM + 16 * i + (lane & 15)] = a;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < FI; ++i) {
+                const int mloc = wm * TM + 16 * i + (lane & 15);
+                const int64_t m = row0 + mloc;
+                if (mloc >= rows_valid) continue;
+                const float s = group_scale(fmaxf(own[i], qa[(wn ^ 1) * BM + mloc]), kPow2);
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) {
+                    const int64_t n = n0 + wn * TN + 16 * j + g4;   // N % 128 == 0: n < N covers n+3
+                    if (n < N)
+                        *reinterpret_cast<uint32_t*>(p.yq + m * N + n) =
+                            cvt_e4m3x4(acc[i][j][0] / s, acc[i][j][1] / s, acc[i][j][2] / s, acc[i][j][3] / s);
+                }
+                const int64_t nw = n0 + wn * TN;
+                if (g == 0 && (wn & 1) == 0 && nw < N) p.sy[(nw >> 7) * p.M + m] = s;
+            }
+            continue;
+        }
+        // ---------------- epilogue: BF16 (RNE), predicated stores ----------------
 #pragma unroll
         for (int i = 0; i < FI; ++i) {
             const int mloc = wm * TM + 16 * i + (lane & 15);

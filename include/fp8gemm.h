@@ -113,6 +113,23 @@ fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq,
                        int64_t K, uint32_t flags, void* stream);
 
 /*
+ * Dense NT GEMM whose output is quantized for the next GEMM in the epilogue
+ * ([DG] "为什么只做 NT 布局": DeepGEMM leaves the activation quantization to
+ * the caller, to be fused into the kernel that produces the activations).
+ * Y is computed as by fp8_gemm_nt and, instead of BF16, written as the 1x128
+ * activation quantizer would write it, from the FP32 accumulator:
+ *   yq  u8   (M,N)         E4M3 codes, E4M3(acc / s)
+ *   sy  fp32 [N/128][M]    s = fl32(max(amax, 1e-4)/448) over the 128
+ *                          columns of the group (rounded up to 2^k with
+ *                          FP8_FLAG_UE8M0, which also marks the input scales)
+ * so (yq, sy) is the (xq, sa) of a following fp8_gemm_nt with K = N.
+ * N % 128 == 0; flags as for fp8_gemm_nt.
+ */
+fp8_status fp8_gemm_nt_qout(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                            const float* sb, uint8_t* yq, float* sy, int64_t M,
+                            int64_t N, int64_t K, uint32_t flags, void* stream);
+
+/*
  * Grouped GEMM, contiguous layout ([DG] "分组 GEMM 的两种布局": the tokens of
  * each expert form one segment along M, N and K are shared by all experts,
  * each segment is aligned to the M block reported by

@@ -99,6 +99,18 @@ def test_grouped_validation(L):
     assert m(A, A, A, A, A, A, 0, 256, 128, 256, 0, None) == OK
 
 
+def test_qout_validation(L):
+    g = L.fp8_gemm_nt_qout
+    if not _gpu_visible():   # valid arguments: on a GPU this would launch on fake addresses
+        assert g(A, A, A, A, A, A, 4, 256, 128, 0, None) in (NODEV, OK, LAUNCH)
+    assert g(A, A, A, A, A, A, 4, 200, 128, 0, None) == SHAPE      # N % 128
+    assert g(A, A, A, A, A, A, 4, 256, 100, 0, None) == SHAPE
+    assert g(A, A, A, A, None, A, 4, 256, 128, 0, None) == INVALID
+    assert g(A, A, A, A, A, MIS, 4, 256, 128, 0, None) == ALIGN
+    assert g(A, A, A, A, A, A, 4, 256, 128, 8, None) == INVALID
+    assert g(A, A, A, A, A, A, 0, 256, 128, 0, None) == OK
+
+
 def test_mx_validation(L):
     q = L.fp8_quant_mx
     assert q(None, 4, 128, A, A, None) == INVALID
