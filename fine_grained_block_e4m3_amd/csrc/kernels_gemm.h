@@ -92,7 +92,8 @@ struct GemmParams {
     int64_t K;
     int64_t max_m;              // masked only
     int32_t E;
-    int32_t m_tiles;            // dense/contiguous: ceil(M/BM); masked: ceil(max_m/BM)
+    int64_t m_lo;               // dense/contiguous: tiles cover rows [m_lo, m_lo + m_tiles*BM)
+    int32_t m_tiles;            // dense/contiguous: ceil((rows to cover)/BM); masked: ceil(max_m/BM)
     int32_t n_tiles;            // ceil(N/BN)
     int32_t group_m;            // raster group height in tiles
 };
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             row_end = (int64_t)e * p.max_m + valid;
         } else {
             raster(t, p.m_tiles, p.n_tiles, p.group_m, mt, nt);
-            row0 = (int64_t)mt * BM;
+            row0 = p.m_lo + (int64_t)mt * BM;
             row_end = p.M;
             if constexpr (MODE == kContiguous) {
                 // expert of this aligned block: its first row naming one in [0, E)

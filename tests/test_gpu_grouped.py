@@ -87,6 +87,23 @@ def test_contiguous_routing(counts, precise):
 
 
 @pytest.mark.parametrize("precise", PATHS)
+def test_contiguous_tail_blocks_in_a_second_launch(precise):
+    """18 row blocks x 16 column tiles of 128x256 = 288 tiles: on 256 CUs one
+    full round, then the last 2 row blocks (part of expert 3 and its padding
+    rows) run as a second launch of 128x64 tiles."""
+    counts = [500, 600, 700, 300]
+    wl = workloads.contiguous(E=4, tokens=sum(counts), N=4096, K=256, seed=77,
+                              counts=np.array(counts))
+    assert wl.M == 18 * 128
+    xq, sa, wq, sb, flags = quant(wl)
+    ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E)
+    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, flags, precise)
+    bound = None if precise else grouped_bound(xq, sa, wq, sb, ref,
+                                               np.where(written, wl.m_indices, -1), wl.E, False)
+    check_rows(y, ref, written, "contiguous tail launch", bound)
+
+
+@pytest.mark.parametrize("precise", PATHS)
 def test_contiguous_dirichlet_and_bad_indices(precise):
     wl = workloads.contiguous(E=8, tokens=1500, N=384, K=256, seed=41)
     idx = wl.m_indices.copy()
