@@ -10,6 +10,7 @@
 #include <mutex>
 
 #include "../../include/fp8gemm.h"
+#include "kernels_decode.h"
 #include "kernels_gemm.h"
 #include "kernels_quant.h"
 
@@ -73,12 +74,40 @@ fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream, int64_t 
     return launch_status();
 }
 
+// Decode-sized dense GEMM (M <= 32): one workgroup per 16*NW output columns
+// and all M rows, one wave per 16 columns; MSUB = ceil(M/16) row subtiles.
+template <int NW, int NS, bool POW2>
+fp8_status launch_decode(const fp8k::GemmParams& p, hipStream_t stream) {
+    const int64_t tiles = (p.N + 16 * NW - 1) / (16 * NW);
+    if (tiles <= 0) return FP8_OK;
+    const dim3 grid((unsigned)tiles), block(64 * NW);
+    switch ((p.M + 15) / 16) {
+        case 1: hipLaunchKernelGGL((fp8k::decode_kernel<1, NW, NS, POW2>), grid, block, 0, stream,
+                                   p.xq, p.sa, p.wq, p.sb, p.y, p); break;
+        case 2: hipLaunchKernelGGL((fp8k::decode_kernel<2, NW, NS, POW2>), grid, block, 0, stream,
+                                   p.xq, p.sa, p.wq, p.sb, p.y, p); break;
+        default: return FP8_ERR_UNSUPPORTED;
+    }
+    return launch_status();
+}
+
 // Instances.  Compute-bound shapes use 8 waves (2 per SIMD) so that one wave's
 // promotion FMAs run while the other wave's MFMAs occupy the matrix core.
 template <int MODE, int PATH>
 fp8_status dispatch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream) {
     if constexpr (MODE == fp8k::kDense) {
-        if (p.M <= 64) return launch_gemm<64, 96, 2, 2, MODE, PATH, 3>(p, cus, stream);
+        if (p.M <= 64) {
+            // M <= 32 on the FP8 MFMA paths: the decode kernel (96 columns per
+            // workgroup).  Above 32 rows every wave of the decode kernel
+            // re-reads an X block larger than its W block from LDS and the
+            // 64x96 tile of the main kernel is faster (N 24576, K 1536: M 16
+            // 7.3 vs 10.3 us, M 32 8.8 vs 10.3, M 48 10.0 vs 10.3, M 64 12.2
+            // vs 10.3).  A 32-column decode workgroup (more of them, several
+            // per CU) measured slower on every shape tried.
+            if constexpr (PATH == fp8k::kPathFp8 || PATH == fp8k::kPathFp8Pow2)
+                if (p.M <= 32) return launch_decode<6, 5, PATH == fp8k::kPathFp8Pow2>(p, stream);
+            return launch_gemm<64, 96, 2, 2, MODE, PATH, 3>(p, cus, stream);
+        }
         constexpr bool kF16 = PATH == fp8k::kPathF16 || PATH == fp8k::kPathF16Pow2;
         const int64_t huge = ((p.M + 255) / 256) * ((p.N + 255) / 256);
         if constexpr (!kF16) {

@@ -208,6 +208,39 @@ def test_224_wide_tile_instance_ragged_sampled(ue8m0):
     assert_close_or_bounded(y[mi, ni], ref, bound, "256x224 tiles, ragged edges")
 
 
+@pytest.mark.parametrize("ue8m0", [False, True])
+@pytest.mark.parametrize("M,N,K", [(1, 48, 128), (16, 1000, 384), (17, 777, 640), (32, 130, 1536),
+                                   (24, 4096, 896), (32, 3072, 1536), (30, 50, 128), (20, 2, 256),
+                                   (32, 200, 7168), (8, 500, 2176), (32, 24576, 256), (9, 24700, 640),
+                                   (33, 130, 1536), (64, 200, 896)])
+def test_decode_instance(M, N, K, ue8m0):
+    """M <= 32 takes the decode kernel (one wave per 16 W rows over all of K,
+    X and the scales in chunks of four K blocks): one and two 16-row subtiles
+    of X, a single K block, partial last chunks (K = 384, 640, 896, 2176),
+    many chunks (7168), a grid of more than one workgroup per CU with a
+    ragged last tile (N 24700), N edges inside a tile, waves wholly past N and
+    tiles straddling a weight block; M = 33 and 64 take the 64x96 tile of the
+    main kernel.  Every element."""
+    flags = oracle.FLAG_UE8M0 if ue8m0 else 0
+    wl = workloads.dense(M, N, K, seed=M * 31 + N + K, outlier_frac=0.01, outlier_mult=50.0)
+    xq, sa = oracle.quant_1x128(wl.x, flags)
+    wq, sb = oracle.quant_128x128(wl.w, flags)
+    ref = oracle.gemm_nt(xq, sa, wq, sb, flags)
+    y = run_gemm(xq, sa, wq, sb, ue8m0=ue8m0)
+    say(f"stats {check(y, xq, sa, wq, sb, ref, False, ue8m0=ue8m0, what=f'decode {M}x{N}x{K}')}")
+
+
+def test_decode_instance_deterministic():
+    wl = workloads.dense(64, 4800, 1536, seed=5, outlier_frac=0.01, outlier_mult=50.0)
+    xq, sa = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    a = [dev(t) for t in (xq, sa, wq, sb)]
+    say("decode determinism x10")
+    first = bf16_bits(fp8.gemm_nt(*a))
+    for _ in range(9):
+        assert np.array_equal(bf16_bits(fp8.gemm_nt(*a)), first)
+
+
 @pytest.mark.parametrize("precise", PATHS)
 def test_deterministic_repeats(precise):
     wl = workloads.dense(300, 512, 1024, seed=77, outlier_frac=0.01, outlier_mult=50.0)
