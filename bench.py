@@ -190,6 +190,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--shape", type=str, default=None,
+                    help="M,N,K: a dense workload of that shape instead of --config, drawn like "
+                         "configuration 3 (X ~ N(0,1), W ~ N(0, 0.02^2)); for decode-sized M")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--mx", action="store_true",
@@ -222,8 +225,22 @@ def main():
     torch.cuda.set_device(dev)
     fp8.load_library()
 
-    log(f"generating workload {args.config}: {workloads.CONFIG_NAMES[args.config]}")
-    wl = workloads.config(args.config)
+    if args.shape:
+        try:
+            sM, sN, sK = (int(v) for v in args.shape.split(","))
+        except ValueError:
+            print("--shape takes M,N,K", file=sys.stderr)
+            sys.exit(2)
+        if min(sM, sN, sK) < 1 or sK % 128:
+            print("--shape: M, N, K >= 1 and K a multiple of 128", file=sys.stderr)
+            sys.exit(2)
+        log(f"generating dense workload {sM}x{sN}x{sK}")
+        wl = workloads.dense(sM, sN, sK, seed=3, w_std=0.02, name=f"dense_{sM}x{sN}x{sK}")
+        traffic_key = f"shape_{sM}x{sN}x{sK}"
+    else:
+        log(f"generating workload {args.config}: {workloads.CONFIG_NAMES[args.config]}")
+        wl = workloads.config(args.config)
+        traffic_key = f"cfg{args.config}"
     ue8m0 = wl.ue8m0
     if (args.mx or args.w4) and wl.kind != "dense":
         print("--mx / --w4: dense workloads only (configs 1-3)", file=sys.stderr)
@@ -349,7 +366,7 @@ def main():
     compute_bound = wl.kind == "contiguous" or (wl.kind == "dense" and flops / nbytes > 629)
     sha = kernel_source_sha()
     variant = "w4_" if args.w4 else ("mx_" if args.mx else "")
-    traffic = load_traffic(f"gemm_{variant}cfg{args.config}", sha)
+    traffic = load_traffic(f"gemm_{variant}{traffic_key}", sha)
     if compute_bound:
         achieved = flops / gemm_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS,
