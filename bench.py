@@ -39,13 +39,19 @@ def log(*a):
 
 
 def kernel_source_sha() -> str:
-    """Hash of the HIP sources: counters taken for other sources are stale."""
+    """Hash of the HIP sources, comments and blank space left out (they do not
+    change the compiled kernels): counters taken for other sources are stale."""
+    import re
     csrc = os.path.join(ROOT, "fine_grained_block_e4m3_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".h", ".hip")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                src = f.read()
+            src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+            src = re.sub(r"//[^\n]*", " ", src)
+            src = " ".join(src.split())
+            h.update(name.encode() + b"\0" + src.encode())
     return h.hexdigest()[:16]
 
 

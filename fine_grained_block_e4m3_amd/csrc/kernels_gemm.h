@@ -19,6 +19,10 @@
 //     of column l%16, so a lane owns one m and four consecutive n: one sA
 //     value per subtile, and a 16-wide subtile always lies inside one
 //     128-row block of W, so sB is uniform over the wave per subtile.
+//   * Per K block a wave keeps the fragments of one operand resident in
+//     registers and streams the other through, one 16-row subtile at a time:
+//     X streams for most instances, W for the 256x224 one (it has more W
+//     subtiles per wave than X subtiles).
 //   * FP8_FLAG_UE8M0 (power-of-two scales): the scales are fed to
 //     v_mfma_scale_f32_16x16x128_f8f6f4 as E8M0 operands and the whole K
 //     loop accumulates inside the matrix core -- no VALU promotion.
@@ -37,6 +41,11 @@
 //     VALU promotes the partials of column j-1, so matrix core and VALU work
 //     side by side (DeepGEMM page, "主循环骨架": promotion on the CUDA cores
 //     overlaps the tensor-core work).
+//   * Other paths of the same kernel (template PATH): FP16 products for the
+//     exact-partial option, MXFP8 with 1x32 E8M0 scales on both operands and
+//     MXFP4 (E2M1) weights; QOUT writes the output as E4M3 with 1x128 scales
+//     instead of BF16.  Decode-sized GEMMs with M <= 32 run a kernel of their
+//     own (kernels_decode.h).
 //   * Persistent grid: each workgroup walks tiles with stride gridDim.x
 //     (DeepGEMM page, "线程组织": persistent launch with an in-kernel block
 //     scheduler; "统一块调度器与 rasterization": grouped raster order so tiles
