@@ -156,3 +156,59 @@ def test_gemm_mx_end_to_end_from_fp32():
     assert np.array_equal(host(wq), rw) and np.array_equal(unpack_scales(host(eb)), reb)
     ref = oracle.gemm_mx(rx, rea, rw, reb)
     assert_close_or_bounded(bf16_bits(y), ref, mx_mfma_error_bound(rx, rea, rw, reb, ref), "mx e2e")
+
+
+def _sampled_bound(xq, ea, wq, eb, mi, ni, ref, decx, decw):
+    """mx_mfma_error_bound on sampled elements (K-long rows of the sampled m and n only)."""
+    K = xq.shape[1]
+    xd = np.abs(decx(xq[mi])) * np.repeat(np.ldexp(1.0, ea[mi].astype(np.int64) - 127), 32, axis=1)
+    wd = np.abs(decw(wq[ni])) * np.repeat(np.ldexp(1.0, eb[ni].astype(np.int64) - 127), 32, axis=1)
+    g8 = lambda a: a.reshape(a.shape[0], K // 8, 8).max(axis=2)
+    return 2.0 ** -8 * np.abs(ref) + 1.01 * 2.0 ** -10 * np.sum(g8(xd) * g8(wd), axis=1) \
+        + 2.0 ** -16 * np.sum(xd * wd, axis=1)
+
+
+def sample_with_edges(M, N, seed, n=4000):
+    rng = np.random.default_rng(seed)
+    mi = np.concatenate([rng.integers(0, M, n), np.zeros(256, int), np.full(256, M - 1), rng.integers(0, M, 512)])
+    ni = np.concatenate([rng.integers(0, N, n), rng.integers(0, N, 512), np.zeros(256, int), np.full(256, N - 1)])
+    return mi, ni
+
+
+@pytest.mark.slow
+def test_mx_full_size_config3_every_element():
+    """The MXFP8 variant of the decode workload (64x24576x1536), as bench.py --mx
+    times it: GPU quantizers bit-exact, GEMM within the bound on every element."""
+    wl = workloads.config(3)
+    say("mx config 3: quantizers")
+    xq, ea = fp8.quant_mx(dev(wl.x))
+    wq, eb = fp8.quant_mx(dev(wl.w))
+    rx, rea = oracle.quant_mx(wl.x)
+    rw, reb = oracle.quant_mx(wl.w)
+    assert np.array_equal(host(xq), rx) and np.array_equal(unpack_scales(host(ea)), rea)
+    assert np.array_equal(host(wq), rw) and np.array_equal(unpack_scales(host(eb)), reb)
+    y = run_mx(rx, rea, rw, reb)
+    say("mx config 3: oracle GEMM")
+    ref = oracle.gemm_mx(rx, rea, rw, reb)
+    assert_close_or_bounded(y, ref, mx_mfma_error_bound(rx, rea, rw, reb, ref), "mx config 3")
+
+
+@pytest.mark.slow
+def test_mx_full_size_config2_sampled():
+    """The MXFP8 variant of the prefill workload (4096x7168x7168), the 256x224
+    instance that bench.py --mx times: quantizers bit-exact, GEMM on 5000
+    sampled elements including the first and last rows and columns."""
+    wl = workloads.config(2)
+    say("mx config 2: oracle quantizers")
+    rx, rea = oracle.quant_mx(wl.x)
+    rw, reb = oracle.quant_mx(wl.w)
+    xq, ea = fp8.quant_mx(dev(wl.x))
+    wq, eb = fp8.quant_mx(dev(wl.w))
+    assert np.array_equal(host(xq), rx) and np.array_equal(unpack_scales(host(ea)), rea)
+    assert np.array_equal(host(wq), rw) and np.array_equal(unpack_scales(host(eb)), reb)
+    y = run_mx(rx, rea, rw, reb)
+    M, N = y.shape
+    mi, ni = sample_with_edges(M, N, 11)
+    ref = oracle.gemm_mx_elems(rx, rea, rw, reb, mi, ni)
+    bound = _sampled_bound(rx, rea, rw, reb, mi, ni, ref, lambda q: DEC[q], lambda q: DEC[q])
+    assert_close_or_bounded(y[mi, ni], ref, bound, "mx config 2 sampled")

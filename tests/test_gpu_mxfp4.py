@@ -135,3 +135,44 @@ def test_gemm_mx_w4_end_to_end_from_fp32():
     assert np.array_equal(host(wq), rw) and np.array_equal(unpack_scales(host(eb)), reb)
     ref = oracle.gemm_mx_w4(rx, rea, rw, reb)
     assert_close_or_bounded(bf16_bits(y), ref, w4_bound(rx, rea, rw, reb, ref), "w4 e2e")
+
+
+@pytest.mark.slow
+def test_w4_full_size_config3_every_element():
+    """MXFP8 activations x MXFP4 weights on the decode workload (64x24576x1536),
+    as bench.py --w4 times it: GPU quantizers bit-exact, GEMM within the bound
+    on every element."""
+    wl = workloads.config(3)
+    say("w4 config 3: quantizers")
+    xq, ea = fp8.quant_mx(dev(wl.x))
+    wq, eb = fp8.quant_mxfp4(dev(wl.w))
+    rx, rea = oracle.quant_mx(wl.x)
+    rw, reb = oracle.quant_mxfp4(wl.w)
+    assert np.array_equal(host(xq), rx) and np.array_equal(unpack_scales(host(ea)), rea)
+    assert np.array_equal(host(wq), rw) and np.array_equal(unpack_scales(host(eb)), reb)
+    y = run_w4(rx, rea, rw, reb)
+    say("w4 config 3: oracle GEMM")
+    ref = oracle.gemm_mx_w4(rx, rea, rw, reb)
+    assert_close_or_bounded(y, ref, w4_bound(rx, rea, rw, reb, ref), "w4 config 3")
+
+
+@pytest.mark.slow
+def test_w4_full_size_config2_sampled():
+    """MXFP8 x MXFP4 on the prefill workload (4096x7168x7168), the 256x224
+    instance bench.py --w4 times: quantizers bit-exact, GEMM on 5000 sampled
+    elements including the first and last rows and columns."""
+    from test_gpu_mx import _sampled_bound, sample_with_edges
+    wl = workloads.config(2)
+    say("w4 config 2: oracle quantizers")
+    rx, rea = oracle.quant_mx(wl.x)
+    rw, reb = oracle.quant_mxfp4(wl.w)
+    xq, ea = fp8.quant_mx(dev(wl.x))
+    wq, eb = fp8.quant_mxfp4(dev(wl.w))
+    assert np.array_equal(host(xq), rx) and np.array_equal(unpack_scales(host(ea)), rea)
+    assert np.array_equal(host(wq), rw) and np.array_equal(unpack_scales(host(eb)), reb)
+    y = run_w4(rx, rea, rw, reb)
+    M, N = y.shape
+    mi, ni = sample_with_edges(M, N, 13)
+    ref = oracle.gemm_mx_w4_elems(rx, rea, rw, reb, mi, ni)
+    bound = _sampled_bound(rx, rea, rw, reb, mi, ni, ref, lambda q: DEC8[q], lambda q: DEC4[unpack_nibbles(q)])
+    assert_close_or_bounded(y[mi, ni], ref, bound, "w4 config 2 sampled")
