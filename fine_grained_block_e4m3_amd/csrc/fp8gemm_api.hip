@@ -91,21 +91,38 @@ fp8_status launch_decode(const fp8k::GemmParams& p, hipStream_t stream) {
     return launch_status();
 }
 
+// Decode-sized dense GEMM with 32 < M <= 48 and K <= kDecodeKxMaxK: X resident
+// in LDS, waves splitting K.
+template <bool POW2>
+fp8_status launch_decode_kx(const fp8k::GemmParams& p, hipStream_t stream) {
+    const int64_t tiles = (p.N + 95) / 96;
+    if (tiles <= 0) return FP8_OK;
+    hipLaunchKernelGGL((fp8k::decode_kx_kernel<3, POW2>), dim3((unsigned)tiles), dim3(512), 0, stream,
+                       p.xq, p.sa, p.wq, p.sb, p.y, p);
+    return launch_status();
+}
+
 // Instances.  Compute-bound shapes use 8 waves (2 per SIMD) so that one wave's
 // promotion FMAs run while the other wave's MFMAs occupy the matrix core.
 template <int MODE, int PATH>
 fp8_status dispatch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream) {
     if constexpr (MODE == fp8k::kDense) {
         if (p.M <= 64) {
-            // M <= 32 on the FP8 MFMA paths: the decode kernel (96 columns per
-            // workgroup).  Above 32 rows every wave of the decode kernel
-            // re-reads an X block larger than its W block from LDS and the
-            // 64x96 tile of the main kernel is faster (N 24576, K 1536: M 16
-            // 7.3 vs 10.3 us, M 32 8.8 vs 10.3, M 48 10.0 vs 10.3, M 64 12.2
-            // vs 10.3).  A 32-column decode workgroup (more of them, several
-            // per CU) measured slower on every shape tried.
-            if constexpr (PATH == fp8k::kPathFp8 || PATH == fp8k::kPathFp8Pow2)
+            // FP8 MFMA paths.  M <= 32: the decode kernel (96 columns per
+            // workgroup, one wave per 16 W rows).  Above 32 rows each of its
+            // waves re-reads an X block larger than its W block from LDS;
+            // 33..48 rows with K <= 1664 take the X-resident decode kernel
+            // (waves splitting K), and the rest the 64x96 tile of the main
+            // kernel.  Kernel trace, N 24576, K 1536: M 16 7.3 vs 10.3 us
+            // (64x96), M 32 8.8 vs 10.3, M 48 9.6 (X-resident) vs 10.4, M 64
+            // 10.7 (X-resident) and 12.2 (decode) vs 10.0-10.4.  A 32-column
+            // decode workgroup (more of them, several per CU) measured slower
+            // on every shape tried.
+            if constexpr (PATH == fp8k::kPathFp8 || PATH == fp8k::kPathFp8Pow2) {
                 if (p.M <= 32) return launch_decode<6, 5, PATH == fp8k::kPathFp8Pow2>(p, stream);
+                if (p.M <= 48 && p.K <= fp8k::kDecodeKxMaxK)
+                    return launch_decode_kx<PATH == fp8k::kPathFp8Pow2>(p, stream);
+            }
             return launch_gemm<64, 96, 2, 2, MODE, PATH, 3>(p, cus, stream);
         }
         constexpr bool kF16 = PATH == fp8k::kPathF16 || PATH == fp8k::kPathF16Pow2;

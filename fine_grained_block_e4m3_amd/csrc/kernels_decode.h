@@ -209,13 +209,17 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
         // (c = 0) or before the KBC W blocks of the previous chunk's positions
         if (c == 0) wait_vmcnt<2 * D>();
         else wait_vmcnt<2 * KBC>();
-        lds_barrier();                                 // chunk c published, buffer of chunk c-1 free
+        // chunk c published; this wave's reads of chunk c-1 complete before
+        // the barrier, after which its buffer is refilled
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         issue_chunk(c + 1);
         static_for<KBC>([&](auto pc) {
             constexpr int pos = decltype(pc)::value;
             const int q = c * KBC + pos;               // sequence position
-            // position q+D reuses the ring slot of position q-1: its reads stay above
-            asm volatile("" ::: "memory");
+            // position q+D reuses the ring slot of position q-1: this wave's
+            // reads of it must have completed (the compiler may sink their
+            // MFMAs, and with them the wait for the reads, below this point)
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             issue_w(q + D);
             // loads issued after position q's W block: the next D W blocks,
             // and chunk c+1 when position q's block was issued before it
@@ -244,6 +248,225 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
                 if (n + 2 < N) yrow[n + 2] = (uint16_t)(hi & 0xFFFF);
                 if (n + 3 < N) yrow[n + 3] = (uint16_t)(hi >> 16);
             }
+        }
+    }
+}
+
+}  // namespace fp8k
+
+namespace fp8k {
+
+// Decode GEMM for 32 < M <= 48 and K <= kDecodeKxMaxK: the same per-wave W
+// streams of full 128-byte rows, but X stays in LDS for the whole of K and
+// the waves split K.  A workgroup owns 96 W rows and all M rows of X; its 8
+// waves are 2 column groups of 48 rows (3 subtiles) times 4 K groups, each K
+// group a contiguous range of K blocks.  A wave reads the X fragments of a K
+// block once and uses them for its 3 subtiles, so an X block is read from LDS
+// by 2 waves instead of 6 (with M = 48 the X block is as large as 3 W
+// subtiles); the K groups' FP32 partial sums meet in LDS at the end.  (With
+// M = 64 and so a 64-row X in LDS, the W ring can hold only two subtile
+// stages per wave and the W stream alone takes as long as the 64x96 tile of
+// the main kernel: the dispatch keeps that tile there.)
+// W comes through a private ring of 3 subtile stages per wave (one subtile of
+// one K block, 2 KB, per stage; two stages ahead).  X, its scales and the
+// weight scales arrive once, at the start, loaded by all waves together.
+constexpr int kDecodeKxMaxK = 1664;
+// LDS row stride of an X block kc bytes wide: kc rounded to an odd multiple
+// of 128 bytes (with the chunk swizzle, fragment reads of 16 rows then hit
+// distinct bank groups).
+__host__ __device__ constexpr int decode_stride(int kc) { return (kc & 255) ? kc : kc + 128; }
+
+template <int MSUB>
+struct DecodeKxLayout {
+    static constexpr int NW = 8, NWN = 2, NWK = 4, SN = 3, NS = 3;
+    static constexpr int MR = 16 * MSUB;
+    static constexpr int XSTRIDE_MAX = 1664;            // decode_stride(kDecodeKxMaxK)
+    static constexpr int KB_MAX = kDecodeKxMaxK / 128;
+    static constexpr int X0 = 0;
+    static constexpr int SA0 = MR * XSTRIDE_MAX;        // sA [KB][MR] floats
+    // (whole 256-byte wave loads: the last one may run past KB*MR floats)
+    static constexpr int SB0 = SA0 + (KB_MAX * MR * 4 + 255) / 256 * 256;   // sB [2][KB] floats, one wave load
+    static constexpr int W0 = SB0 + 256;                // W rings [wave][stage] 2 KB
+    static constexpr int SPARE = W0 + NW * NS * 2048;
+    static constexpr int BYTES = SPARE + 1024;
+    static constexpr int RED = NW * SN * MSUB * 1024;   // partial sums at the end (over everything)
+    static constexpr int LDS = BYTES > RED ? BYTES : RED;
+    static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(2 * KB_MAX <= 64, "one wave load holds the sB of two weight blocks");
+};
+
+template <int MSUB, bool POW2>
+__global__ __launch_bounds__(512, 1) void decode_kx_kernel(
+    const uint8_t* __restrict__ xq_, const float* __restrict__ sa_, const uint8_t* __restrict__ wq_,
+    const float* __restrict__ sb_, uint16_t* __restrict__ y_, GemmParams p) {
+    using L = DecodeKxLayout<MSUB>;
+    constexpr int NW = L::NW, NWN = L::NWN, NWK = L::NWK, SN = L::SN, NS = L::NS;
+    constexpr int TN = 16 * SN * NWN;
+    constexpr int PAIRS = SN * MSUB;
+    static_assert(NS == SN, "ring slot = subtile index");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::LDS];
+
+    const int lane = threadIdx.x & 63;
+    const int w = uniform(threadIdx.x >> 6);
+    const int wn = w % NWN, wk = w / NWN;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int KB = (int)(K >> 7);
+    const int xstride = decode_stride((int)K);
+    const int64_t n0 = (int64_t)blockIdx.x * TN;
+    const int64_t nw = n0 + 16 * SN * wn;              // this wave's first column
+    const int kb_lo = wk * KB / NWK, kb_hi = (wk + 1) * KB / NWK;
+    const int Q = (kb_hi - kb_lo) * SN;                // this wave's stages: (K block, subtile)
+    const uint32_t lds0 = lds_addr(smem);
+
+    const int64_t rows_w = N - n0 < TN ? N - n0 : TN;
+    const i32x4 wr = make_rsrc(wq_ + n0 * K, (uint32_t)(rows_w * K));
+    const i32x4 xr = make_rsrc(xq_, (uint32_t)(M * K));
+    const i32x4 sar = make_rsrc(sa_, (uint32_t)(KB * M * 4));
+    const int64_t nb0 = n0 >> 7, nb1 = (n0 + rows_w - 1) >> 7;
+    const i32x4 sbr = make_rsrc(sb_ + nb0 * KB, (uint32_t)((nb1 - nb0 + 1) * KB * 4));
+    const i32x4 none = make_rsrc(wq_, 0u);
+    constexpr uint32_t kFar = 0x7FFFFFF0u;
+
+    // ---- W stage q = (K block kb_lo + q/SN, subtile q%SN), ring slot q%SN ----
+    uint32_t wsrc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + (lane >> 3);
+        wsrc[h] = (uint32_t)((nw - n0 + r) * K) + 16 * ((lane & 7) ^ lds_swz(r));
+    }
+    const uint32_t wring = lds0 + L::W0 + (uint32_t)w * NS * 2048;
+    auto issue_w = [&](int q, auto sc) {               // sc: q % SN as a constant
+        constexpr int s = decltype(sc)::value;
+        const bool in = q < Q;
+        const int kb = kb_lo + q / SN;
+        const i32x4 rs = in ? wr : none;
+        const uint32_t off = (uint32_t)(16 * s) * (uint32_t)K + (uint32_t)(in ? kb : 0) * 128;
+        dma_lds16_one<0>(wring + s * 2048, wsrc[0] + off, rs, 0);
+        dma_lds16_one<0>(wring + s * 2048 + 1024, wsrc[1] + off, rs, 0);
+    };
+
+    // ---- prologue: W stages 0 and 1, then X, sA, sB (all waves share them) ----
+    issue_w(0, std::integral_constant<int, 0>{});
+    issue_w(1, std::integral_constant<int, 1>{});
+    {
+        const int nxl = L::MR * xstride / 1024;         // 1 KB loads of X
+        const int nsa = (KB * L::MR * 4 + 255) / 256;   // dword loads of sA
+        const int ntot = nxl + nsa + 1;
+        for (int i = w; i < ntot; i += NW) {            // wave-uniform
+            if (i < nxl) {
+                const int d = 1024 * i + 16 * lane;
+                const int r = d / xstride, j = (d - r * xstride) >> 4;
+                const int c = j ^ lds_swz(r);
+                const uint32_t src = (16 * j < K) ? (uint32_t)(r * K + 16 * c) : kFar;
+                dma_lds16_one<0>(lds0 + L::X0 + 1024 * i, src, xr, 0);
+            } else if (i < nxl + nsa) {
+                const int f = 64 * (i - nxl) + lane;    // float f of [KB][MR]
+                const int kb = f / L::MR, m = f - kb * L::MR;
+                const uint32_t src = (kb < KB && m < M) ? (uint32_t)((kb * M + m) * 4) : kFar;
+                dma_lds4(lds0 + L::SA0 + 256 * (i - nxl), src, sar, 0);
+            } else {
+                // lane b*KB + kb: sB of weight block nb0 + b, K block kb
+                const int b = lane / KB, kb = lane - b * KB;
+                const uint32_t src = (b < 2) ? (uint32_t)((b * KB + kb) * 4) : kFar;
+                dma_lds4(lds0 + L::SB0, src, sbr, 0);
+            }
+        }
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+
+    // ---- fragment reads ----
+    const int sw = lds_swz(r16);
+    const uint32_t wfa = (uint32_t)r16 * 128 + 16 * (g ^ sw), wfb = (uint32_t)r16 * 128 + 16 * ((4 + g) ^ sw);
+    const uint32_t xfa = (uint32_t)r16 * xstride + 16 * (g ^ sw);
+    const uint32_t xfb = (uint32_t)r16 * xstride + 16 * ((4 + g) ^ sw);
+    auto rd16 = [&](uint32_t off) -> i32x4 { return *reinterpret_cast<const i32x4*>(smem + off); };
+    int sbl[SN];                                       // weight block of each subtile in the sB table
+#pragma unroll
+    for (int s = 0; s < SN; ++s) {
+        const int64_t ns = nw + 16 * s < N ? nw + 16 * s : N - 1;
+        sbl[s] = (int)((ns >> 7) - nb0);
+    }
+    const float* sbt = reinterpret_cast<const float*>(smem + L::SB0);
+    const float* sat = reinterpret_cast<const float*>(smem + L::SA0);
+
+    f32x4 acc[SN][MSUB];
+#pragma unroll
+    for (int s = 0; s < SN; ++s)
+#pragma unroll
+        for (int ms = 0; ms < MSUB; ++ms) acc[s][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- K loop: per K block, its SN stages; stage q+2 issued before stage q is used ----
+    for (int kb = kb_lo; kb < kb_hi; ++kb) {
+        i32x8 xf[MSUB];
+        float sav[MSUB];
+        const uint32_t xs = L::X0 + 128 * kb;
+#pragma unroll
+        for (int ms = 0; ms < MSUB; ++ms) {
+            const i32x4 xa = rd16(xs + ms * 16 * xstride + xfa), xb = rd16(xs + ms * 16 * xstride + xfb);
+            xf[ms] = i32x8{xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+            sav[ms] = sat[kb * L::MR + 16 * ms + r16];
+        }
+        static_for<SN>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            const int q = (kb - kb_lo) * SN + s;
+            // stage q+2 reuses the ring slot of stage q-1: this wave's reads of
+            // it must have completed (the compiler may sink their MFMAs, and
+            // with them the wait for the reads, below this point)
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            issue_w(q + 2, std::integral_constant<int, (s + 2) % SN>{});
+            wait_vmcnt<4>();                           // stage q: only stages q+1, q+2 may be in flight
+            asm volatile("" ::: "memory");
+            const i32x4 wa = rd16(L::W0 + (uint32_t)w * NS * 2048 + s * 2048 + wfa);
+            const i32x4 wb = rd16(L::W0 + (uint32_t)w * NS * 2048 + s * 2048 + wfb);
+            const i32x8 wf = i32x8{wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+            const float sbv = sbt[sbl[s] * KB + kb];
+#pragma unroll
+            for (int ms = 0; ms < MSUB; ++ms) {
+                if constexpr (POW2) {
+                    acc[s][ms] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        wf, xf[ms], acc[s][ms], 0, 0, 0, e8m0_of(sbv), 0, e8m0_of(sav[ms]));
+                } else {
+                    const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        wf, xf[ms], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                    const float sc2 = sav[ms] * sbv;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[s][ms][r] = __builtin_fmaf(sc2, part[r], acc[s][ms][r]);
+                }
+            }
+        });
+    }
+    wait_vmcnt<0>();
+
+    // ---- cross-wave sum in LDS (over everything), then BF16 stores ----
+    __syncthreads();
+    f32x4* red = reinterpret_cast<f32x4*>(smem);        // [wave][subtile pair][lane]
+#pragma unroll
+    for (int q = 0; q < PAIRS; ++q) red[(w * PAIRS + q) * 64 + lane] = acc[q / MSUB][q % MSUB];
+    __syncthreads();
+    for (int t = w; t < NWN * PAIRS; t += NW) {
+        const int cg = t / PAIRS, q = t % PAIRS;       // column group, its subtile pair
+        f32x4 v = red[(cg * PAIRS + q) * 64 + lane];   // K group 0 (wave cg)
+#pragma unroll
+        for (int k2 = 1; k2 < NWK; ++k2) {
+            const f32x4 u = red[((k2 * NWN + cg) * PAIRS + q) * 64 + lane];
+            v = f32x4{v[0] + u[0], v[1] + u[1], v[2] + u[2], v[3] + u[3]};
+        }
+        const int s = q / MSUB, ms = q % MSUB;
+        const int64_t m = 16 * ms + r16;
+        const int64_t n = n0 + 16 * SN * cg + 16 * s + 4 * g;
+        if (m >= M || n >= N) continue;
+        uint16_t* yrow = y_ + m * N;
+        const uint32_t lo = pack_bf16x2(v[0], v[1]);
+        const uint32_t hi = pack_bf16x2(v[2], v[3]);
+        if ((N & 3) == 0 && n + 3 < N) {
+            *reinterpret_cast<uint2*>(yrow + n) = make_uint2(lo, hi);
+        } else {
+            yrow[n] = (uint16_t)(lo & 0xFFFF);
+            if (n + 1 < N) yrow[n + 1] = (uint16_t)(lo >> 16);
+            if (n + 2 < N) yrow[n + 2] = (uint16_t)(hi & 0xFFFF);
+            if (n + 3 < N) yrow[n + 3] = (uint16_t)(hi >> 16);
         }
     }
 }

@@ -212,15 +212,19 @@ def test_224_wide_tile_instance_ragged_sampled(ue8m0):
 @pytest.mark.parametrize("M,N,K", [(1, 48, 128), (16, 1000, 384), (17, 777, 640), (32, 130, 1536),
                                    (24, 4096, 896), (32, 3072, 1536), (30, 50, 128), (20, 2, 256),
                                    (32, 200, 7168), (8, 500, 2176), (32, 24576, 256), (9, 24700, 640),
-                                   (33, 130, 1536), (64, 200, 896)])
+                                   (33, 130, 1536), (64, 200, 896), (48, 24576, 256), (48, 1000, 1664),
+                                   (40, 300, 128), (36, 97, 1408), (48, 200, 1792), (45, 4000, 1152),
+                                   (64, 300, 1536)])
 def test_decode_instance(M, N, K, ue8m0):
     """M <= 32 takes the decode kernel (one wave per 16 W rows over all of K,
     X and the scales in chunks of four K blocks): one and two 16-row subtiles
     of X, a single K block, partial last chunks (K = 384, 640, 896, 2176),
     many chunks (7168), a grid of more than one workgroup per CU with a
     ragged last tile (N 24700), N edges inside a tile, waves wholly past N and
-    tiles straddling a weight block; M = 33 and 64 take the 64x96 tile of the
-    main kernel.  Every element."""
+    tiles straddling a weight block.  33 <= M <= 48 with K <= 1664 takes the
+    X-resident decode kernel (K groups of waves, a single K block, fewer
+    blocks than K groups, the largest K, ragged N); K = 1792 and M = 64 take
+    the 64x96 tile of the main kernel.  Every element."""
     flags = oracle.FLAG_UE8M0 if ue8m0 else 0
     wl = workloads.dense(M, N, K, seed=M * 31 + N + K, outlier_frac=0.01, outlier_mult=50.0)
     xq, sa = oracle.quant_1x128(wl.x, flags)
