@@ -76,19 +76,51 @@ fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream, int64_t 
 
 // Decode-sized dense GEMM (M <= 32): one workgroup per 16*NW output columns
 // and all M rows, one wave per 16 columns; MSUB = ceil(M/16) row subtiles.
+// With fewer column tiles than compute units the K chunks are split over up
+// to 8 workgroups per tile (one workgroup per CU in all): they write FP32
+// partial sums to a stream-ordered workspace and a second kernel adds them in
+// split order and rounds to BF16.  If the workspace cannot be allocated the
+// GEMM runs unsplit.
 template <int NW, int NS, bool POW2>
-fp8_status launch_decode(const fp8k::GemmParams& p, hipStream_t stream) {
+fp8_status launch_decode(const fp8k::GemmParams& p0, int cus, hipStream_t stream) {
+    fp8k::GemmParams p = p0;
     const int64_t tiles = (p.N + 16 * NW - 1) / (16 * NW);
     if (tiles <= 0) return FP8_OK;
-    const dim3 grid((unsigned)tiles), block(64 * NW);
+    const int64_t nct = (p.K / 128 + 3) / 4;          // K chunks of 4 blocks
+    int64_t splits = tiles < cus ? cus / tiles : 1;
+    if (splits > nct) splits = nct;
+    if (splits > 8) splits = 8;
+    if (splits < 1) splits = 1;
+    void* ws = nullptr;
+    if (splits > 1) {
+        if (hipMallocAsync(&ws, (size_t)(splits * p.M * p.N) * sizeof(float), stream) != hipSuccess) {
+            (void)hipGetLastError();
+            ws = nullptr;
+            splits = 1;
+        }
+    }
+    p.part = static_cast<float*>(ws);
+    const dim3 grid((unsigned)tiles, (unsigned)splits), block(64 * NW);
     switch ((p.M + 15) / 16) {
         case 1: hipLaunchKernelGGL((fp8k::decode_kernel<1, NW, NS, POW2>), grid, block, 0, stream,
                                    p.xq, p.sa, p.wq, p.sb, p.y, p); break;
         case 2: hipLaunchKernelGGL((fp8k::decode_kernel<2, NW, NS, POW2>), grid, block, 0, stream,
                                    p.xq, p.sa, p.wq, p.sb, p.y, p); break;
-        default: return FP8_ERR_UNSUPPORTED;
+        default:
+            if (ws) (void)hipFreeAsync(ws, stream);
+            return FP8_ERR_UNSUPPORTED;
     }
-    return launch_status();
+    fp8_status st = launch_status();
+    if (ws) {
+        if (st == FP8_OK) {
+            const int64_t mn = p.M * p.N;
+            hipLaunchKernelGGL(fp8k::decode_split_reduce, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, stream,
+                               static_cast<const float*>(ws), (int)splits, mn, p.y);
+            st = launch_status();
+        }
+        if (hipFreeAsync(ws, stream) != hipSuccess && st == FP8_OK) st = FP8_ERR_LAUNCH;
+    }
+    return st;
 }
 
 // Decode-sized dense GEMM with 32 < M <= 48 and K <= kDecodeKxMaxK: X resident
@@ -119,7 +151,7 @@ fp8_status dispatch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream)
             // decode workgroup (more of them, several per CU) measured slower
             // on every shape tried.
             if constexpr (PATH == fp8k::kPathFp8 || PATH == fp8k::kPathFp8Pow2) {
-                if (p.M <= 32) return launch_decode<6, 5, PATH == fp8k::kPathFp8Pow2>(p, stream);
+                if (p.M <= 32) return launch_decode<6, 5, PATH == fp8k::kPathFp8Pow2>(p, cus, stream);
                 if (p.M <= 48 && p.K <= fp8k::kDecodeKxMaxK)
                     return launch_decode_kx<PATH == fp8k::kPathFp8Pow2>(p, stream);
             }

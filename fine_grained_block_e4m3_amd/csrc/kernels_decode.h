@@ -86,12 +86,12 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
     const int r16 = lane & 15, g = lane >> 4;
     const int64_t M = p.M, N = p.N, K = p.K;
     const int KB = (int)(K >> 7);
-    const int NC = (KB + KBC - 1) / KBC;
+    // Split K (grid.y > 1, for few column tiles): this workgroup takes the
+    // chunks [cs0, cs0 + NC) of the K range and writes FP32 partial sums.
+    const int NCT = (KB + KBC - 1) / KBC;
+    const int cs0 = (int)(blockIdx.y * NCT / gridDim.y);
+    const int NC = (int)((blockIdx.y + 1) * NCT / gridDim.y) - cs0;
     const int64_t n0 = (int64_t)blockIdx.x * TN;
-    // Workgroups walk the K chunks in rotated orders (sequence chunk c is data
-    // chunk (c + rot) mod NC), so that at any moment they read different parts
-    // of X rather than all the same lines.
-    const int rot = (int)(blockIdx.x % (unsigned)NC);
     const int64_t nw = n0 + 16 * w;                   // this wave's first column
     const uint32_t lds0 = lds_addr(smem);
 
@@ -119,8 +119,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
     auto seq_kb = [&](int q) -> int {
         const int c = q / KBC;
         if (c >= NC) return KB;
-        const int cd = c + rot < NC ? c + rot : c + rot - NC;
-        return cd * KBC + (q - c * KBC);
+        return (cs0 + c) * KBC + (q - c * KBC);
     };
     auto issue_w = [&](int q) {
         const int kb = seq_kb(q);
@@ -135,7 +134,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
     auto issue_chunk = [&](int c) {
         const bool in = c < NC;
         const int buf = c & 1;
-        const int cd = c + rot < NC ? c + rot : c + rot - NC;   // data chunk
+        const int cd = cs0 + c;                        // data chunk
         const int k0 = cd * KBC * 128, kb0 = cd * KBC;
 #pragma unroll
         for (int t = 0; t < NPW; ++t) {
@@ -230,9 +229,25 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
     }
     wait_vmcnt<0>();
 
-    // ---- BF16 stores: lane holds n = nw + 4g + r, m = 16 ms + r16 ----
+    // ---- stores: lane holds n = nw + 4g + r, m = 16 ms + r16 ----
     const int64_t n = nw + 4 * g;
-    if (n < N) {
+    if (n < N && p.part) {
+        // FP32 partial sums of this K range, [split][M][N]
+        float* base = p.part + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+        for (int ms = 0; ms < MSUB; ++ms) {
+            const int64_t m = 16 * ms + r16;
+            if (m >= M) continue;
+            float* prow = base + m * N;
+            if ((N & 3) == 0 && n + 3 < N) {
+                *reinterpret_cast<f32x4*>(prow + n) = acc[ms];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N) prow[n + r] = acc[ms][r];
+            }
+        }
+    } else if (n < N) {
 #pragma unroll
         for (int ms = 0; ms < MSUB; ++ms) {
             const int64_t m = 16 * ms + r16;
@@ -255,6 +270,17 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(
 }  // namespace fp8k
 
 namespace fp8k {
+
+// Split-K reduction of the decode GEMM: Y = BF16(sum over the splits, in
+// split order, of the FP32 partial sums [S][M][N]).
+__global__ __launch_bounds__(256) void decode_split_reduce(const float* __restrict__ part, int S, int64_t MN,
+                                                           uint16_t* __restrict__ y) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= MN) return;
+    float v = part[i];
+    for (int s = 1; s < S; ++s) v += part[s * MN + i];
+    y[i] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFF);
+}
 
 // Decode GEMM for 32 < M <= 48 and K <= kDecodeKxMaxK: the same per-wave W
 // streams of full 128-byte rows, but X stays in LDS for the whole of K and

@@ -105,6 +105,7 @@ struct GemmParams {
     int32_t m_tiles;            // dense/contiguous: ceil((rows to cover)/BM); masked: ceil(max_m/BM)
     int32_t n_tiles;            // ceil(N/BN)
     int32_t group_m;            // raster group height in tiles
+    float* part;                // decode split-K: FP32 partial sums [splits][M][N] (else null)
 };
 
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"

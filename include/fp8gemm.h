@@ -107,6 +107,12 @@ fp8_status fp8_quant_128x128(const float* w, int64_t N, int64_t K, uint8_t* wq,
  *   Y[m][n] = sum_kb sa[kb][m] * sb[n/128][kb] * sum_{k in kb} xq[m][k]*wq[n][k]
  *   xq u8 (M,K), sa fp32 [K/128][M], wq u8 (N,K), sb fp32 [ceil(N/128)][K/128],
  *   y  bf16 bits (M,N).
+ * Memory: with M <= 32 and N below 96 times the device's compute units, K is
+ * split over several workgroups, whose FP32 partial sums (at most 8*M*N*4
+ * bytes) live in a workspace taken from the stream-ordered allocator on
+ * `stream` and released on it before the call returns; if none can be had
+ * the GEMM runs unsplit (same result up to FP32 summation order).  Every
+ * other case uses the caller's buffers only.
  */
 fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq,
                        const float* sb, uint16_t* y, int64_t M, int64_t N,

@@ -219,9 +219,11 @@ def test_decode_instance(M, N, K, ue8m0):
     """M <= 32 takes the decode kernel (one wave per 16 W rows over all of K,
     X and the scales in chunks of four K blocks): one and two 16-row subtiles
     of X, a single K block, partial last chunks (K = 384, 640, 896, 2176),
-    many chunks (7168), a grid of more than one workgroup per CU with a
-    ragged last tile (N 24700), N edges inside a tile, waves wholly past N and
-    tiles straddling a weight block.  33 <= M <= 48 with K <= 1664 takes the
+    many chunks (7168), K split over 2 to 8 workgroups per column tile when
+    the tiles are fewer than the CUs (uneven chunk ranges at K = 2176), a grid
+    of more than one workgroup per CU with a ragged last tile (N 24700), N
+    edges inside a tile, waves wholly past N and tiles straddling a weight
+    block.  33 <= M <= 48 with K <= 1664 takes the
     X-resident decode kernel (K groups of waves, a single K block, fewer
     blocks than K groups, the largest K, ragged N); K = 1792 and M = 64 take
     the 64x96 tile of the main kernel.  Every element."""
@@ -235,7 +237,9 @@ def test_decode_instance(M, N, K, ue8m0):
 
 
 def test_decode_instance_deterministic():
-    wl = workloads.dense(64, 4800, 1536, seed=5, outlier_frac=0.01, outlier_mult=50.0)
+    """Repeated calls agree bit for bit, also when K is split over workgroups
+    (here 50 column tiles, 8 splits): the partial sums are added in split order."""
+    wl = workloads.dense(32, 4800, 7168, seed=5, outlier_frac=0.01, outlier_mult=50.0)
     xq, sa = oracle.quant_1x128(wl.x)
     wq, sb = oracle.quant_128x128(wl.w)
     a = [dev(t) for t in (xq, sa, wq, sb)]
