@@ -1,5 +1,6 @@
-// kernels_decode.h -- block-scaled E4M3 NT GEMM for decode-sized M (M <= 64)
-// on gfx950.
+// kernels_decode.h -- block-scaled E4M3 NT GEMM for decode-sized M on gfx950:
+// decode_kernel (M <= 32, optionally split over K) with its split-K reduction,
+// and decode_kx_kernel (32 < M <= 48, X resident in LDS).
 //
 // Same result as gemm_kernel: Y[m][n] = sum_kb sa[kb][m] * sb[n/128][kb] *
 // P_kb[m][n], each 128-K block partial P_kb formed by one FP8 MFMA and
@@ -41,6 +42,10 @@
 //     never straddles a 128-row weight block).
 //   * Power-of-two scales (UE8M0): they are the E8M0 operands of the scaled
 //     MFMA and K accumulates inside the matrix core.
+//   * Split K (grid.y > 1, chosen by the host when the column tiles are fewer
+//     than the CUs): workgroup (t, s) takes a contiguous range of the K chunks
+//     and writes FP32 partial sums [s][M][N]; decode_split_reduce adds them in
+//     split order and rounds to BF16.
 #pragma once
 
 #include "device_common.h"
