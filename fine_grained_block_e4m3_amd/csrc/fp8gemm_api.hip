@@ -7,7 +7,9 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "../../include/fp8gemm.h"
 #include "kernels_decode.h"
@@ -78,9 +80,44 @@ fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream, int64_t 
 // and all M rows, one wave per 16 columns; MSUB = ceil(M/16) row subtiles.
 // With fewer column tiles than compute units the K chunks are split over up
 // to 8 workgroups per tile (one workgroup per CU in all): they write FP32
-// partial sums to a stream-ordered workspace and a second kernel adds them in
-// split order and rounds to BF16.  If the workspace cannot be allocated the
-// GEMM runs unsplit.
+// partial sums to the stream's split workspace and a second kernel adds them
+// in split order and rounds to BF16.  Without a workspace the GEMM runs
+// unsplit.
+// Split-K workspace of the decode GEMM: one buffer per (device, stream),
+// sized for the largest split the device takes (8 splits x 32 rows x fewer
+// than 96*CUs columns of FP32), allocated on first use and kept until the
+// process ends.  Calls on one stream are ordered, so they can share it; other
+// streams have their own.  Nothing is allocated while the stream is being
+// captured into a graph (the GEMM then runs unsplit).
+std::mutex g_split_mu;
+std::map<std::pair<int, hipStream_t>, void*> g_split_ws;
+
+size_t split_ws_bytes(int cus) { return (size_t)8 * 32 * 96 * (size_t)cus * sizeof(float); }
+
+void* split_workspace(int cus, hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_split_mu);
+    const auto key = std::make_pair(dev, stream);
+    const auto it = g_split_ws.find(key);
+    if (it != g_split_ws.end()) return it->second;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void* ws = nullptr;
+    if (hipMalloc(&ws, split_ws_bytes(cus)) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    g_split_ws[key] = ws;
+    return ws;
+}
+
 template <int NW, int NS, bool POW2>
 fp8_status launch_decode(const fp8k::GemmParams& p0, int cus, hipStream_t stream) {
     fp8k::GemmParams p = p0;
@@ -93,11 +130,10 @@ fp8_status launch_decode(const fp8k::GemmParams& p0, int cus, hipStream_t stream
     if (splits < 1) splits = 1;
     void* ws = nullptr;
     if (splits > 1) {
-        if (hipMallocAsync(&ws, (size_t)(splits * p.M * p.N) * sizeof(float), stream) != hipSuccess) {
-            (void)hipGetLastError();
-            ws = nullptr;
-            splits = 1;
-        }
+        // splits <= 8, M <= 32, N < 96 * cus: the buffer always holds them
+        ws = (size_t)(splits * p.M * p.N) * sizeof(float) <= split_ws_bytes(cus) ? split_workspace(cus, stream)
+                                                                                : nullptr;
+        if (!ws) splits = 1;
     }
     p.part = static_cast<float*>(ws);
     const dim3 grid((unsigned)tiles, (unsigned)splits), block(64 * NW);
@@ -106,19 +142,14 @@ fp8_status launch_decode(const fp8k::GemmParams& p0, int cus, hipStream_t stream
                                    p.xq, p.sa, p.wq, p.sb, p.y, p); break;
         case 2: hipLaunchKernelGGL((fp8k::decode_kernel<2, NW, NS, POW2>), grid, block, 0, stream,
                                    p.xq, p.sa, p.wq, p.sb, p.y, p); break;
-        default:
-            if (ws) (void)hipFreeAsync(ws, stream);
-            return FP8_ERR_UNSUPPORTED;
+        default: return FP8_ERR_UNSUPPORTED;
     }
     fp8_status st = launch_status();
-    if (ws) {
-        if (st == FP8_OK) {
-            const int64_t mn = p.M * p.N;
-            hipLaunchKernelGGL(fp8k::decode_split_reduce, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, stream,
-                               static_cast<const float*>(ws), (int)splits, mn, p.y);
-            st = launch_status();
-        }
-        if (hipFreeAsync(ws, stream) != hipSuccess && st == FP8_OK) st = FP8_ERR_LAUNCH;
+    if (ws && st == FP8_OK) {
+        const int64_t mn = p.M * p.N;
+        hipLaunchKernelGGL(fp8k::decode_split_reduce, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<const float*>(ws), (int)splits, mn, p.y);
+        st = launch_status();
     }
     return st;
 }

@@ -108,11 +108,14 @@ fp8_status fp8_quant_128x128(const float* w, int64_t N, int64_t K, uint8_t* wq,
  *   xq u8 (M,K), sa fp32 [K/128][M], wq u8 (N,K), sb fp32 [ceil(N/128)][K/128],
  *   y  bf16 bits (M,N).
  * Memory: with M <= 32 and N below 96 times the device's compute units, K is
- * split over several workgroups, whose FP32 partial sums (at most 8*M*N*4
- * bytes) live in a workspace taken from the stream-ordered allocator on
- * `stream` and released on it before the call returns; if none can be had
- * the GEMM runs unsplit (same result up to FP32 summation order).  Every
- * other case uses the caller's buffers only.
+ * split over several workgroups, whose FP32 partial sums live in a workspace
+ * the library keeps per (device, stream): 8*32*96*CUs*4 bytes (about 25 MB
+ * on MI355X), allocated by the first such call on that stream and held until
+ * the process ends.  Calls on one stream share it in stream order; a graph
+ * replayed on another stream while that stream runs such a call would race
+ * on it.  No allocation happens while the stream is being captured; without
+ * a workspace the GEMM runs unsplit (same result up to FP32 summation
+ * order).  Every other case uses the caller's buffers only.
  */
 fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq,
                        const float* sb, uint16_t* y, int64_t M, int64_t N,
