@@ -11,10 +11,8 @@ overwritten before its block has been read.
 """
 import pytest
 
-KBC = 4  # K blocks per X chunk
-
-
-def replay(KB, D, NPW):
+def replay(KB, D, NPW, KBC=4):
+    """KBC: K blocks per X chunk."""
     NC = (KB + KBC - 1) // KBC
     issued = []
     ring_owner = {}
@@ -47,18 +45,18 @@ def replay(KB, D, NPW):
             wait(2 * D + (NPW if pos < D else 0), [("w", q), ("x", c)])
 
 
+@pytest.mark.parametrize("KBC", [4, 8])
 @pytest.mark.parametrize("D", [1, 2, 3, 4])
 @pytest.mark.parametrize("NPW", [1, 2, 3, 6, 8, 12])
-def test_decode_wait_counts(D, NPW):
+def test_decode_wait_counts(D, NPW, KBC):
     for KB in range(1, 40):
-        replay(KB, D, NPW)
+        replay(KB, D, NPW, KBC)
 
 
 def test_decode_wait_counts_catch_a_short_count():
     """A count one too large (waiting for one load too few) must be caught."""
     with pytest.raises(AssertionError):
         KB, D, NPW = 8, 4, 2
-        NC = (KB + KBC - 1) // KBC
         issued = [("x", 0)] * NPW + [("w", j) for j in range(D) for _ in range(2)]
         n = 2 * D + 1
         done = issued[: len(issued) - n]

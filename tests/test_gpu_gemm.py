@@ -275,3 +275,55 @@ def test_full_size_dense_configs_every_element(cfg, precise):
     ref = oracle.gemm_nt(xq, sa, wq, sb)
     stats = assert_close(y, ref, f"config {cfg}")
     say(f"config {cfg} error stats: {stats}")
+
+
+def _split_operands(seed, M=16, N=2112, K=7168):
+    """A decode shape with few column tiles (K split over workgroups)."""
+    wl = workloads.dense(M, N, K, seed=seed, outlier_frac=0.01, outlier_mult=50.0)
+    xq, sa = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    return [dev(t) for t in (xq, sa, wq, sb)]
+
+
+def test_split_decode_on_concurrent_streams():
+    """Split-K decode GEMMs on two streams at once (each stream has its own
+    partial-sum workspace) give the results of the same calls on the default
+    stream, bit for bit."""
+    ops = [_split_operands(41), _split_operands(42)]
+    say("split decode: default stream")
+    ref = [bf16_bits(fp8.gemm_nt(*o)) for o in ops]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty((16, 2112), dtype=torch.bfloat16, device="cuda") for _ in ops]
+    torch.cuda.synchronize()
+    say("split decode: two streams, 10 rounds")
+    for _ in range(10):
+        for o, s, y in zip(ops, streams, outs):
+            with torch.cuda.stream(s):
+                fp8.gemm_nt(*o, out=y)
+        torch.cuda.synchronize()
+        for r, y in zip(ref, outs):
+            assert np.array_equal(bf16_bits(y), r)
+
+
+def test_split_decode_graph_replays():
+    """A split-K decode GEMM captured in a graph on a stream whose workspace
+    exists (a call on it before the capture): every replay, with eager work and
+    synchronizations between replays, equals the eager result bit for bit."""
+    o = _split_operands(43)
+    s = torch.cuda.Stream()
+    y = torch.empty((16, 2112), dtype=torch.bfloat16, device="cuda")
+    with torch.cuda.stream(s):
+        fp8.gemm_nt(*o, out=y)              # the stream's workspace is allocated here
+    torch.cuda.synchronize()
+    eager = bf16_bits(y)
+    g = torch.cuda.CUDAGraph()
+    say("split decode: capture")
+    with torch.cuda.graph(g, stream=s):
+        fp8.gemm_nt(*o, out=y)
+    other = _split_operands(44)
+    for i in range(4):
+        y.zero_()
+        g.replay()
+        fp8.gemm_nt(*other)                 # eager work on the default stream between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(y), eager), f"replay {i}"
