@@ -451,18 +451,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         int64_t row_end;    // rows [row0, row_end) may be read and written
         int expert = 0;
         if constexpr (MODE == kMasked) {
+            // An expert with nmt m-tiles owns logical tiles
+            // [base*n_tiles, (base+nmt)*n_tiles), walked m-fastest: the m-tiles
+            // that read the same W columns are neighbours, so they run together
+            // on one XCD and the second read of W hits its L2.
             const int mt_t = t / p.n_tiles;
-            nt = t - mt_t * p.n_tiles;
-            int base = 0, e = 0, valid = 0;
+            int base = 0, e = 0, valid = 0, nmt = 1;
             for (; e < p.E; ++e) {
                 valid = masked_m_[e];
                 valid = valid < 0 ? 0 : (valid > p.max_m ? (int)p.max_m : valid);
-                const int nmt = (valid + BM - 1) / BM;
+                nmt = (valid + BM - 1) / BM;
                 if (mt_t < base + nmt) break;
                 base += nmt;
             }
             expert = e;
-            mt = mt_t - base;
+            const int local = t - base * p.n_tiles;
+            nt = local / nmt;
+            mt = local - nt * nmt;
             row0 = (int64_t)e * p.max_m + (int64_t)mt * BM;
             row_end = (int64_t)e * p.max_m + valid;
         } else {
