@@ -116,6 +116,24 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _out(t, name: str, dtype: torch.dtype, shape, like: torch.Tensor) -> torch.Tensor:
+    """A caller's output buffer: the kernels write exactly this shape, so any
+    other shape, type, layout or device is refused before a launch."""
+    _need(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {like.device}")
+    return t
+
+
+def _same_device(*ts: torch.Tensor) -> None:
+    d = ts[0].device
+    for t in ts[1:]:
+        if t.device != d:
+            raise ValueError(f"operands on different devices: {d} and {t.device}")
+
+
 def _ptr(t: torch.Tensor):
     return ctypes.c_void_p(t.data_ptr())
 
@@ -137,7 +155,8 @@ def quant_1x128(x: torch.Tensor, ue8m0: bool = False, out=None):
         xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
         sa = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
     else:
-        xq, sa = out
+        xq = _out(out[0], "out[0]", torch.uint8, (M, K), x)
+        sa = _out(out[1], "out[1]", torch.float32, (K // 128, M), x)
     _check("fp8_quant_1x128", L.fp8_quant_1x128(_ptr(x), M, K, _ptr(xq), _ptr(sa),
                                                 _flags(ue8m0), _stream(x)))
     return xq, sa
@@ -152,7 +171,8 @@ def quant_128x128(w: torch.Tensor, ue8m0: bool = False, out=None):
         wq = torch.empty((N, K), dtype=torch.uint8, device=w.device)
         sb = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=w.device)
     else:
-        wq, sb = out
+        wq = _out(out[0], "out[0]", torch.uint8, (N, K), w)
+        sb = _out(out[1], "out[1]", torch.float32, ((N + 127) // 128, K // 128), w)
     _check("fp8_quant_128x128", L.fp8_quant_128x128(_ptr(w), N, K, _ptr(wq), _ptr(sb),
                                                     _flags(ue8m0), _stream(w)))
     return wq, sb
@@ -169,7 +189,9 @@ def gemm_nt(xq, sa, wq, sb, ue8m0: bool = False, precise: bool = False, out=None
     N = wq.shape[0]
     if wq.shape[1] != K or sa.shape != (K // 128, M) or sb.shape != ((N + 127) // 128, K // 128):
         raise ValueError("gemm_nt: inconsistent operand shapes")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _same_device(xq, sa, wq, sb)
+    y = _out(out, "out", torch.bfloat16, (M, N), xq) if out is not None \
+        else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     _check("fp8_gemm_nt", L.fp8_gemm_nt(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(y),
                                         M, N, K, _flags(ue8m0, precise), _stream(xq)))
     return y
@@ -187,11 +209,13 @@ def gemm_nt_qout(xq, sa, wq, sb, ue8m0: bool = False, precise: bool = False, out
     N = wq.shape[0]
     if wq.shape[1] != K or sa.shape != (K // 128, M) or sb.shape != ((N + 127) // 128, K // 128):
         raise ValueError("gemm_nt_qout: inconsistent operand shapes")
+    _same_device(xq, sa, wq, sb)
     if out is None:
         yq = torch.empty((M, N), dtype=torch.uint8, device=xq.device)
         sy = torch.empty((N // 128, M), dtype=torch.float32, device=xq.device)
     else:
-        yq, sy = out
+        yq = _out(out[0], "out[0]", torch.uint8, (M, N), xq)
+        sy = _out(out[1], "out[1]", torch.float32, (N // 128, M), xq)
     _check("fp8_gemm_nt_qout", L.fp8_gemm_nt_qout(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(yq),
                                                   _ptr(sy), M, N, K, _flags(ue8m0, precise),
                                                   _stream(xq)))
@@ -212,7 +236,9 @@ def grouped_gemm_contiguous(xq, sa, wq, sb, m_indices, ue8m0: bool = False, prec
     if wq.shape[2] != K or sa.shape != (K // 128, M) or sb.shape != (E, N // 128, K // 128) \
             or m_indices.shape[0] != M:
         raise ValueError("grouped_gemm_contiguous: inconsistent operand shapes")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _same_device(xq, sa, wq, sb, m_indices)
+    y = _out(out, "out", torch.bfloat16, (M, N), xq) if out is not None \
+        else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     _check("fp8_grouped_gemm_contiguous",
            L.fp8_grouped_gemm_contiguous(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(m_indices),
                                          _ptr(y), M, N, K, E, _flags(ue8m0, precise), _stream(xq)))
@@ -234,8 +260,9 @@ def grouped_gemm_masked(xq, sa, wq, sb, masked_m, ue8m0: bool = False, precise: 
     if wq.shape != (E, N, K) or sa.shape != (K // 128, E * max_m) \
             or sb.shape != (E, N // 128, K // 128) or masked_m.shape[0] != E:
         raise ValueError("grouped_gemm_masked: inconsistent operand shapes")
-    y = out if out is not None else torch.empty((E, max_m, N), dtype=torch.bfloat16,
-                                                device=xq.device)
+    _same_device(xq, sa, wq, sb, masked_m)
+    y = _out(out, "out", torch.bfloat16, (E, max_m, N), xq) if out is not None \
+        else torch.empty((E, max_m, N), dtype=torch.bfloat16, device=xq.device)
     _check("fp8_grouped_gemm_masked",
            L.fp8_grouped_gemm_masked(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(masked_m),
                                      _ptr(y), E, max_m, N, K, _flags(ue8m0, precise), _stream(xq)))
@@ -253,7 +280,8 @@ def quant_mx(x: torch.Tensor, out=None):
         q = torch.empty((R, K), dtype=torch.uint8, device=x.device)
         e = torch.empty((K // 128, R), dtype=torch.int32, device=x.device)
     else:
-        q, e = out
+        q = _out(out[0], "out[0]", torch.uint8, (R, K), x)
+        e = _out(out[1], "out[1]", torch.int32, (K // 128, R), x)
     _check("fp8_quant_mx", L.fp8_quant_mx(_ptr(x), R, K, _ptr(q), _ptr(e), _stream(x)))
     return q, e
 
@@ -270,7 +298,9 @@ def gemm_nt_mx(xq, ea, wq, eb, out=None) -> torch.Tensor:
     N = wq.shape[0]
     if wq.shape[1] != K or ea.shape != (K // 128, M) or eb.shape != (K // 128, N):
         raise ValueError("gemm_nt_mx: inconsistent operand shapes")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _same_device(xq, ea, wq, eb)
+    y = _out(out, "out", torch.bfloat16, (M, N), xq) if out is not None \
+        else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     _check("fp8_gemm_nt_mx", L.fp8_gemm_nt_mx(_ptr(xq), _ptr(ea), _ptr(wq), _ptr(eb), _ptr(y),
                                               M, N, K, 0, _stream(xq)))
     return y
@@ -286,7 +316,8 @@ def quant_mxfp4(w: torch.Tensor, out=None):
         q = torch.empty((R, K // 2), dtype=torch.uint8, device=w.device)
         e = torch.empty((K // 128, R), dtype=torch.int32, device=w.device)
     else:
-        q, e = out
+        q = _out(out[0], "out[0]", torch.uint8, (R, K // 2), w)
+        e = _out(out[1], "out[1]", torch.int32, (K // 128, R), w)
     _check("fp8_quant_mxfp4", L.fp8_quant_mxfp4(_ptr(w), R, K, _ptr(q), _ptr(e), _stream(w)))
     return q, e
 
@@ -302,7 +333,9 @@ def gemm_nt_mx_w4(xq, ea, wq, eb, out=None) -> torch.Tensor:
     N = wq.shape[0]
     if wq.shape[1] * 2 != K or ea.shape != (K // 128, M) or eb.shape != (K // 128, N):
         raise ValueError("gemm_nt_mx_w4: inconsistent operand shapes")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _same_device(xq, ea, wq, eb)
+    y = _out(out, "out", torch.bfloat16, (M, N), xq) if out is not None \
+        else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     _check("fp8_gemm_nt_mx_w4", L.fp8_gemm_nt_mx_w4(_ptr(xq), _ptr(ea), _ptr(wq), _ptr(eb), _ptr(y),
                                                     M, N, K, 0, _stream(xq)))
     return y

@@ -88,7 +88,10 @@ fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream, int64_t 
 // than 96*CUs columns of FP32), allocated on first use and kept until the
 // process ends.  Calls on one stream are ordered, so they can share it; other
 // streams have their own.  Nothing is allocated while the stream is being
-// captured into a graph (the GEMM then runs unsplit).
+// captured into a graph, nor past kMaxSplitWorkspaces buffers in the process
+// (a caller that makes a new stream per call would otherwise add one per
+// stream): the GEMM then runs unsplit.
+constexpr size_t kMaxSplitWorkspaces = 16;
 std::mutex g_split_mu;
 std::map<std::pair<int, hipStream_t>, void*> g_split_ws;
 
@@ -104,6 +107,7 @@ void* split_workspace(int cus, hipStream_t stream) {
     const auto key = std::make_pair(dev, stream);
     const auto it = g_split_ws.find(key);
     if (it != g_split_ws.end()) return it->second;
+    if (g_split_ws.size() >= kMaxSplitWorkspaces) return nullptr;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
         (void)hipGetLastError();

@@ -113,9 +113,10 @@ fp8_status fp8_quant_128x128(const float* w, int64_t N, int64_t K, uint8_t* wq,
  * on MI355X), allocated by the first such call on that stream and held until
  * the process ends.  Calls on one stream share it in stream order; a graph
  * replayed on another stream while that stream runs such a call would race
- * on it.  No allocation happens while the stream is being captured; without
- * a workspace the GEMM runs unsplit (same result up to FP32 summation
- * order).  Every other case uses the caller's buffers only.
+ * on it.  No allocation happens while the stream is being captured, nor once
+ * the process holds 16 such workspaces (one per stream: about 400 MB in
+ * all); without a workspace the GEMM runs unsplit (same result up to FP32
+ * summation order).  Every other case uses the caller's buffers only.
  */
 fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq,
                        const float* sb, uint16_t* y, int64_t M, int64_t N,

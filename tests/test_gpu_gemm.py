@@ -305,6 +305,31 @@ def test_split_decode_on_concurrent_streams():
             assert np.array_equal(bf16_bits(y), r)
 
 
+def test_split_decode_on_many_streams():
+    """More streams than the library keeps split workspaces for (16 per
+    process): every call still matches the oracle, the ones past the limit
+    running unsplit, and repeating the round on the same streams gives the
+    same bits."""
+    wl = workloads.dense(16, 2112, 7168, seed=45, outlier_frac=0.01, outlier_mult=50.0)
+    xq, sa = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    ref = oracle.gemm_nt(xq, sa, wq, sb)
+    a = [dev(t) for t in (xq, sa, wq, sb)]
+    streams = [torch.cuda.Stream() for _ in range(20)]
+    outs = [torch.empty((16, 2112), dtype=torch.bfloat16, device="cuda") for _ in streams]
+    say("split decode: 20 streams, 2 rounds")
+    bits = []
+    for _ in range(2):
+        for s, y in zip(streams, outs):
+            with torch.cuda.stream(s):
+                fp8.gemm_nt(*a, out=y)
+        torch.cuda.synchronize()
+        bits.append([bf16_bits(y) for y in outs])
+    for i, y in enumerate(bits[0]):
+        check(y, xq, sa, wq, sb, ref, False, what=f"stream {i}")
+        assert np.array_equal(y, bits[1][i]), f"stream {i}: second round differs"
+
+
 def test_split_decode_graph_replays():
     """A split-K decode GEMM captured in a graph on a stream whose workspace
     exists (a call on it before the capture): every replay, with eager work and
