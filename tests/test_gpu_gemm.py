@@ -214,7 +214,8 @@ def test_224_wide_tile_instance_ragged_sampled(ue8m0):
                                    (32, 200, 7168), (8, 500, 2176), (32, 24576, 256), (9, 24700, 640),
                                    (33, 130, 1536), (64, 200, 896), (48, 24576, 256), (48, 1000, 1664),
                                    (40, 300, 128), (36, 97, 1408), (48, 200, 1792), (45, 4000, 1152),
-                                   (64, 300, 1536)])
+                                   (64, 300, 1536), (50, 97, 128), (57, 1000, 640), (64, 24700, 1152),
+                                   (49, 130, 1536), (64, 96, 256), (64, 300, 1792)])
 def test_decode_instance(M, N, K, ue8m0):
     """M <= 32 takes the decode kernel (one wave per 16 W rows over all of K,
     X and the scales in chunks of four K blocks): one and two 16-row subtiles
@@ -225,8 +226,9 @@ def test_decode_instance(M, N, K, ue8m0):
     edges inside a tile, waves wholly past N and tiles straddling a weight
     block.  33 <= M <= 48 with K <= 1664 takes the
     X-resident decode kernel (K groups of waves, a single K block, fewer
-    blocks than K groups, the largest K, ragged N); K = 1792 and M = 64 take
-    the 64x96 tile of the main kernel.  Every element."""
+    blocks than K groups, the largest K, ragged N); 49 <= M <= 64 takes the
+    64x96 tile of the main kernel (one K block, ragged N, an N edge inside a
+    tile, a single tile), as do K = 1792 and above.  Every element."""
     flags = oracle.FLAG_UE8M0 if ue8m0 else 0
     wl = workloads.dense(M, N, K, seed=M * 31 + N + K, outlier_frac=0.01, outlier_mult=50.0)
     xq, sa = oracle.quant_1x128(wl.x, flags)
