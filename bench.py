@@ -369,7 +369,9 @@ def main():
 
     flops, nbytes, rows = algorithmic_counts_mx(wl, args.w4) if mx else algorithmic_counts(wl)
     gemm_s = per_kernel_ms["gemm"] / 1e3
-    compute_bound = wl.kind == "contiguous" or (wl.kind == "dense" and flops / nbytes > 629)
+    # ridge point of the roofline: peak FLOP/s over peak HBM bytes/s (625 FLOP/B)
+    ridge = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    compute_bound = wl.kind == "contiguous" or (wl.kind == "dense" and flops / nbytes > ridge)
     sha = kernel_source_sha()
     variant = "w4_" if args.w4 else ("mx_" if args.mx else "")
     traffic = load_traffic(f"gemm_{variant}{traffic_key}", sha)
