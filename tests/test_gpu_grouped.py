@@ -151,6 +151,23 @@ def test_masked_counts(ue8m0, max_m, precise):
     check_rows(y, ref, written, f"masked max_m={max_m}", bound)
 
 
+@pytest.mark.parametrize("ue8m0", [True, False])
+def test_masked_tile_order(ue8m0):
+    """Experts with one, two and three 128-row m-tiles (and none) times three
+    256-column n-tiles, the last one ragged: the tile order walks each
+    expert's m-tiles fastest within each n-tile; every valid row of every
+    column is written once and nothing else."""
+    mm = np.array([300, 129, 0, 257, 64], np.int32)
+    E, max_m, N, K = len(mm), 300, 640, 256
+    wl = workloads.masked(E, max_m, N, K, seed=11, ue8m0=ue8m0, masked_m=mm)
+    xq, sa, wq, sb, flags = quant(wl)
+    ref, written = oracle.grouped_masked(xq, sa, wq, sb, mm, E, max_m, flags)
+    y = run_masked(xq, sa, wq, sb, mm, E, max_m, flags, False)
+    row_expert = np.where(written, np.arange(E * max_m) // max_m, -1)
+    bound = grouped_bound(xq, sa, wq, sb, ref, row_expert, E, ue8m0)
+    check_rows(y, ref, written, "masked tile order", bound)
+
+
 def test_masked_rows_past_count_never_read():
     """Rows past the count may hold NaN codes and NaN scales: the output must
     not change."""
