@@ -1,5 +1,6 @@
 """Accumulation precision of the FP8 matrix instruction and the promotion
-interval, measured through the public entry points.
+interval (how many K blocks may be summed before scaling), measured through
+the public entry points.
 
 DeepGEMM page, section "细粒度缩放在 GEMM 层面引爆的两个问题": the FP8 tensor
 cores of H800 accumulate with limited precision, which is why partials are
