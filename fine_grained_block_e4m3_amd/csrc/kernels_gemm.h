@@ -683,22 +683,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         // 0 .. JB-1 take the first weight block's products (JB = 0 otherwise).
         auto kloop = [&](auto jbc) {
         constexpr int JB = decltype(jbc)::value;
-        // Prologue: block 0 in full; then blocks 1 .. STAGES-2 in full and the
-        // first two window positions of block STAGES-1; then the reads of
-        // block 0 that the pipeline expects.
+        // Prologue: blocks 0 .. STAGES-2 in full, all in flight together; once
+        // block 0 has landed (for every wave), the first two window positions
+        // of block STAGES-1; then the reads of block 0 that the pipeline
+        // expects.
         wait_vmcnt<0>();
         lds_barrier();   // all waves are done with the previous tile's buffers
-        {
-            const StageLoads L0 = stage_loads(0, std::integral_constant<int, 0>{});
-            static_for<NPIECE>([&](auto pc) { issue_piece(L0, pc); });
-        }
-        wait_vmcnt<0>();
-        lds_barrier();
-        static_for<STAGES - 2>([&](auto sc) {
-            constexpr int b = decltype(sc)::value + 1;
+        static_for<STAGES - 1>([&](auto sc) {
+            constexpr int b = decltype(sc)::value;
             const StageLoads Lb = stage_loads(b, std::integral_constant<int, b>{});
             static_for<NPIECE>([&](auto pc) { issue_piece(Lb, pc); });
         });
+        wait_vmcnt<(STAGES - 2) * NPIECE>();   // block 0: blocks 1 .. STAGES-2 may fly
+        lds_barrier();
         {
             const StageLoads Ll = stage_loads(STAGES - 1, std::integral_constant<int, STAGES - 1>{});
             issue_window(Ll, std::integral_constant<int, 0>{});
