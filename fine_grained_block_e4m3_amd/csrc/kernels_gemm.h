@@ -133,6 +133,13 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
                  uniform((int)bytes), 0x00020000};
 }
 
+// A read-only, wave-uniform int32 (here a per-expert count) through the
+// scalar cache: an s_load waited on with lgkmcnt, so that it does not wait
+// for this wave's outstanding vector loads and stores.
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int i) {
+    return ((const __attribute__((address_space(4))) int32_t*)(p))[i];
+}
+
 // Byte address of an LDS location (the value M0 takes for an LDS DMA).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(FP8K_LDS const void*)p;
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     if constexpr (MODE == kMasked) {
         int acc = 0;
         for (int e = 0; e < p.E; ++e) {
-            int v = masked_m_[e];
+            int v = ld_uniform(masked_m_, e);
             v = v < 0 ? 0 : (v > p.max_m ? (int)p.max_m : v);
             acc += (v + BM - 1) / BM;
         }
@@ -458,7 +465,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             const int mt_t = t / p.n_tiles;
             int base = 0, e = 0, valid = 0, nmt = 1;
             for (; e < p.E; ++e) {
-                valid = masked_m_[e];
+                valid = ld_uniform(masked_m_, e);
                 valid = valid < 0 ? 0 : (valid > p.max_m ? (int)p.max_m : valid);
                 nmt = (valid + BM - 1) / BM;
                 if (mt_t < base + nmt) break;
@@ -687,8 +694,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         // block 0 has landed (for every wave), the first two window positions
         // of block STAGES-1; then the reads of block 0 that the pipeline
         // expects.
-        wait_vmcnt<0>();
-        lds_barrier();   // all waves are done with the previous tile's buffers
+        // All waves are done with the previous tile's buffers.  No wait for the
+        // vector-memory counter here: it also counts the previous tile's output
+        // stores, and the waits below are counts of this wave's loads issued
+        // after the one waited for, which loads complete in order.  Each wave
+        // refills only its own rows of a buffer, after its own earlier loads
+        // into them (the discarded ones past the previous tile's last block).
+        lds_barrier();
         static_for<STAGES - 1>([&](auto sc) {
             constexpr int b = decltype(sc)::value;
             const StageLoads Lb = stage_loads(b, std::integral_constant<int, b>{});
@@ -920,8 +932,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         } else {
             kloop(std::integral_constant<int, 0>{});
         }
-        // the loads issued past the last block were discarded; let them retire
-        wait_vmcnt<0>();
+        // (the loads issued past the last block were discarded; they retire in
+        // order before the next tile's loads, and the kernel's end waits for them)
 
         const int g4 = 4 * g;
         if constexpr (QOUT) {
