@@ -209,3 +209,27 @@ def test_full_size_masked_config5_every_element(precise):
     say("config 5: oracle grouped GEMM")
     ref, written = oracle.grouped_masked(xq, sa, wq, sb, wl.masked_m, E, max_m, flags)
     check_rows(y, ref, written, "config 5")
+
+
+def test_nothing_to_compute():
+    """Calls with no valid row launch nothing or exit at once and write
+    nothing: every masked count zero (or negative), every contiguous row
+    index padding or out of range, and a dense call with M = 0."""
+    E, max_m, N, K = 3, 128, 256, 256
+    mm = np.array([0, -5, 0], np.int32)
+    wl = workloads.masked(E, max_m, N, K, seed=21, masked_m=mm)
+    xq, sa, wq, sb, flags = quant(wl)
+    y = run_masked(xq, sa, wq, sb, mm, E, max_m, flags, False)
+    assert np.all(y == SENTINEL)
+    idx = np.array([-1] * 128 + [E] * 128 + [-7] * 128, np.int32)
+    wl = workloads.dense(len(idx), N * E, K, seed=22)
+    xq, sa = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    y = run_contiguous(xq, sa, wq, sb, idx, E, 0, False)
+    assert np.all(y == SENTINEL)
+    say("dense M = 0")
+    z = fp8.gemm_nt(torch.empty((0, K), dtype=torch.uint8, device="cuda"),
+                    torch.empty((K // 128, 0), dtype=torch.float32, device="cuda"),
+                    dev(wq[:N]), dev(sb[:N // 128]))
+    torch.cuda.synchronize()
+    assert tuple(z.shape) == (0, N)
