@@ -287,6 +287,28 @@ def _split_operands(seed, M=16, N=2112, K=7168):
     return [dev(t) for t in (xq, sa, wq, sb)]
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("M", [16, 100])
+def test_largest_k(M):
+    """K = 2^22, the largest K the library takes (its per-lane tile offsets
+    are 32-bit): random finite codes and power-of-two scales.  M = 16 takes
+    the decode kernel with K split over workgroups, M = 100 a main-kernel
+    tile.  The first 32 columns are checked against the oracle on every row,
+    with the FP8-MFMA bound."""
+    N, K = 256, 1 << 22
+    rng = np.random.default_rng(M)
+    say(f"largest K: M={M} codes")
+    xq = workloads.random_codes(rng, (M, K))
+    wq = workloads.random_codes(rng, (N, K))
+    sa = workloads.random_pow2(rng, (K // 128, M), -8, 0)
+    sb = workloads.random_pow2(rng, (N // 128, K // 128), -8, 0)
+    y = run_gemm(xq, sa, wq, sb, guard=256)
+    say("largest K: oracle on 32 columns")
+    ref = oracle.gemm_nt(xq, sa, wq[:32], sb[:1])
+    bound = fp8_mfma_error_bound(xq, sa, wq[:32], sb[:1], ref)
+    say(f"stats {assert_close_or_bounded(y[:, :32], ref, bound, f'K=2^22 M={M}')}")
+
+
 def test_split_decode_on_concurrent_streams():
     """Split-K decode GEMMs on two streams at once (each stream has its own
     partial-sum workspace) give the results of the same calls on the default
