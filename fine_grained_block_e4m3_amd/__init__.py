@@ -22,7 +22,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8gemm.so")
 
 FLAG_UE8M0 = 1
-FLAG_PRECISE = 2
+FLAG_FAST_ACCUM = 2
+PLAN_MX = 0x100
+PLAN_QOUT = 0x200
+LAYOUT = {"dense": 0, "contiguous": 1, "masked": 2}
 
 STATUS = {
     0: "FP8_OK",
@@ -39,6 +42,9 @@ SYMBOLS = (
     "fp8_quant_1x128",
     "fp8_quant_128x128",
     "fp8_gemm_nt",
+    "fp8_gemm_nt_ws",
+    "fp8_gemm_workspace_size",
+    "fp8_gemm_plan",
     "fp8_gemm_nt_qout",
     "fp8_grouped_gemm_contiguous",
     "fp8_grouped_gemm_masked",
@@ -49,6 +55,18 @@ SYMBOLS = (
     "fp8_get_mk_alignment_for_contiguous_layout",
     "fp8_status_string",
 )
+
+
+class GemmPlan(ctypes.Structure):
+    """fp8_gemm_plan_t: the kernel instances a GEMM call launches."""
+    _fields_ = [("exact", ctypes.c_int32), ("kernel", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("waves", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("tiles", ctypes.c_int64), ("main_rows", ctypes.c_int64), ("tail_tile_m", ctypes.c_int32),
+                ("tail_tile_n", ctypes.c_int32), ("tail_tiles", ctypes.c_int64), ("k_splits", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class Fp8GemmError(RuntimeError):
@@ -74,6 +92,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fp8_quant_1x128.argtypes = [P, I64, I64, P, P, U32, P]
     L.fp8_quant_128x128.argtypes = [P, I64, I64, P, P, U32, P]
     L.fp8_gemm_nt.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
+    L.fp8_gemm_nt_ws.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P, ctypes.c_size_t, P]
+    L.fp8_gemm_workspace_size.argtypes = [I64, I64, I64, U32]
+    L.fp8_gemm_workspace_size.restype = ctypes.c_size_t
+    L.fp8_gemm_plan.argtypes = [I32, I64, I64, I64, U32, I32, ctypes.c_size_t, ctypes.POINTER(GemmPlan)]
     L.fp8_gemm_nt_qout.argtypes = [P, P, P, P, P, P, I64, I64, I64, U32, P]
     L.fp8_grouped_gemm_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I32, U32, P]
     L.fp8_grouped_gemm_masked.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, U32, P]
@@ -81,7 +103,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fp8_gemm_nt_mx.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
     L.fp8_quant_mxfp4.argtypes = [P, I64, I64, P, P, P]
     L.fp8_gemm_nt_mx_w4.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
-    for fn in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_gemm_nt", "fp8_gemm_nt_qout",
+    for fn in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_gemm_nt", "fp8_gemm_nt_ws", "fp8_gemm_plan",
+               "fp8_gemm_nt_qout",
                "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked", "fp8_quant_mx",
                "fp8_gemm_nt_mx", "fp8_quant_mxfp4", "fp8_gemm_nt_mx_w4"):
         getattr(L, fn).restype = ctypes.c_int
@@ -138,8 +161,22 @@ def _ptr(t: torch.Tensor):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _flags(ue8m0: bool, precise: bool = False) -> int:
-    return (FLAG_UE8M0 if ue8m0 else 0) | (FLAG_PRECISE if precise else 0)
+def _flags(ue8m0: bool, fast_accum: bool = False) -> int:
+    return (FLAG_UE8M0 if ue8m0 else 0) | (FLAG_FAST_ACCUM if fast_accum else 0)
+
+
+def gemm_plan(layout: str, M: int, N: int, K: int, ue8m0: bool = False, fast_accum: bool = False,
+              mx: bool = False, qout: bool = False, compute_units: int = 256,
+              workspace_bytes: int = 0) -> dict:
+    """The kernel instances a GEMM call of this shape launches (host-side
+    arithmetic only; no GPU needed).  layout: dense, contiguous or masked
+    (max_m as M)."""
+    L = load_library()
+    flags = _flags(ue8m0, fast_accum) | (PLAN_MX if mx else 0) | (PLAN_QOUT if qout else 0)
+    plan = GemmPlan()
+    _check("fp8_gemm_plan", L.fp8_gemm_plan(LAYOUT[layout], M, N, K, flags, compute_units, workspace_bytes,
+                                            ctypes.byref(plan)))
+    return plan.as_dict()
 
 
 def get_mk_alignment_for_contiguous_layout() -> int:
@@ -178,8 +215,13 @@ def quant_128x128(w: torch.Tensor, ue8m0: bool = False, out=None):
     return wq, sb
 
 
-def gemm_nt(xq, sa, wq, sb, ue8m0: bool = False, precise: bool = False, out=None) -> torch.Tensor:
-    """Y (M, N) bf16 = block-scaled X * W^T."""
+def gemm_nt(xq, sa, wq, sb, ue8m0: bool = False, fast_accum: bool = False, out=None,
+            workspace=None) -> torch.Tensor:
+    """Y (M, N) bf16 = block-scaled X * W^T.  fast_accum: block partials from
+    the FP8 matrix instruction (see FP8_FLAG_FAST_ACCUM).  With fast_accum and
+    a decode-sized M the library splits K when given a workspace: a uint8
+    device tensor of at least fp8_gemm_workspace_size() bytes, allocated here
+    through torch when not passed."""
     L = load_library()
     _need(xq, "xq", torch.uint8, 2)
     _need(wq, "wq", torch.uint8, 2)
@@ -192,12 +234,23 @@ def gemm_nt(xq, sa, wq, sb, ue8m0: bool = False, precise: bool = False, out=None
     _same_device(xq, sa, wq, sb)
     y = _out(out, "out", torch.bfloat16, (M, N), xq) if out is not None \
         else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
-    _check("fp8_gemm_nt", L.fp8_gemm_nt(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(y),
-                                        M, N, K, _flags(ue8m0, precise), _stream(xq)))
+    flags = _flags(ue8m0, fast_accum)
+    if workspace is None and M and N and K:
+        nbytes = int(L.fp8_gemm_workspace_size(M, N, K, flags))
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=xq.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+        _same_device(xq, workspace)
+        ws, ws_bytes = _ptr(workspace), workspace.numel()
+    else:
+        ws, ws_bytes = None, 0
+    _check("fp8_gemm_nt_ws", L.fp8_gemm_nt_ws(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(y),
+                                              M, N, K, flags, ws, ws_bytes, _stream(xq)))
     return y
 
 
-def gemm_nt_qout(xq, sa, wq, sb, ue8m0: bool = False, precise: bool = False, out=None):
+def gemm_nt_qout(xq, sa, wq, sb, ue8m0: bool = False, fast_accum: bool = False, out=None):
     """Block-scaled X * W^T written quantized for the next GEMM: (yq uint8
     (M, N) E4M3 codes, sy fp32 (N/128, M) 1x128 scales); N % 128 == 0."""
     L = load_library()
@@ -217,12 +270,12 @@ def gemm_nt_qout(xq, sa, wq, sb, ue8m0: bool = False, precise: bool = False, out
         yq = _out(out[0], "out[0]", torch.uint8, (M, N), xq)
         sy = _out(out[1], "out[1]", torch.float32, (N // 128, M), xq)
     _check("fp8_gemm_nt_qout", L.fp8_gemm_nt_qout(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(yq),
-                                                  _ptr(sy), M, N, K, _flags(ue8m0, precise),
+                                                  _ptr(sy), M, N, K, _flags(ue8m0, fast_accum),
                                                   _stream(xq)))
     return yq, sy
 
 
-def grouped_gemm_contiguous(xq, sa, wq, sb, m_indices, ue8m0: bool = False, precise: bool = False,
+def grouped_gemm_contiguous(xq, sa, wq, sb, m_indices, ue8m0: bool = False, fast_accum: bool = False,
                             out=None) -> torch.Tensor:
     """xq (M, K), sa (K/128, M), wq (E, N, K), sb (E, N/128, K/128), m_indices int32 (M)."""
     L = load_library()
@@ -241,11 +294,11 @@ def grouped_gemm_contiguous(xq, sa, wq, sb, m_indices, ue8m0: bool = False, prec
         else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     _check("fp8_grouped_gemm_contiguous",
            L.fp8_grouped_gemm_contiguous(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(m_indices),
-                                         _ptr(y), M, N, K, E, _flags(ue8m0, precise), _stream(xq)))
+                                         _ptr(y), M, N, K, E, _flags(ue8m0, fast_accum), _stream(xq)))
     return y
 
 
-def grouped_gemm_masked(xq, sa, wq, sb, masked_m, ue8m0: bool = False, precise: bool = False,
+def grouped_gemm_masked(xq, sa, wq, sb, masked_m, ue8m0: bool = False, fast_accum: bool = False,
                         out=None) -> torch.Tensor:
     """xq (E, max_m, K), sa (K/128, E*max_m), wq (E, N, K), sb (E, N/128, K/128),
     masked_m int32 (E).  Returns y (E, max_m, N) bf16 (rows past masked_m untouched)."""
@@ -265,7 +318,7 @@ def grouped_gemm_masked(xq, sa, wq, sb, masked_m, ue8m0: bool = False, precise: 
         else torch.empty((E, max_m, N), dtype=torch.bfloat16, device=xq.device)
     _check("fp8_grouped_gemm_masked",
            L.fp8_grouped_gemm_masked(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(masked_m),
-                                     _ptr(y), E, max_m, N, K, _flags(ue8m0, precise), _stream(xq)))
+                                     _ptr(y), E, max_m, N, K, _flags(ue8m0, fast_accum), _stream(xq)))
     return y
 
 

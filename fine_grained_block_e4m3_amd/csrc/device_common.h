@@ -11,11 +11,15 @@ typedef int   i32x2 __attribute__((ext_vector_type(2)));
 typedef int   i32x4 __attribute__((ext_vector_type(4)));
 typedef int   i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 #define FP8K_LDS __attribute__((address_space(3)))
+// Lambdas of the kernels are always inlined: an out-of-line call would pass
+// wave-uniform values (LDS addresses, buffer resources) in VGPRs.
+#define FP8K_INLINE __attribute__((always_inline))
 
 // Wave-uniform value (moves it to a scalar register).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -64,12 +68,6 @@ __device__ __forceinline__ float group_scale(float amax, bool pow2) {
 // a power of two.
 __device__ __forceinline__ int e8m0_of(float s) {
     return (int)((__float_as_uint(s) >> 23) & 0xFFu);
-}
-
-// Power-of-two part of an FP32 scale: 2^(e-127) for its biased exponent e
-// (the value a UE8M0 scale byte stands for).
-__device__ __forceinline__ float pow2_part(float s) {
-    return __uint_as_float(__float_as_uint(s) & 0x7F800000u);
 }
 
 // Eight E4M3 bytes (w0 bytes 0..3, then w1 bytes 0..3) widened to FP16 with

@@ -6,13 +6,14 @@
 // allocated, freed or synchronized here.
 #include <hip/hip_runtime.h>
 
+#include <stdint.h>
+
 #include <atomic>
-#include <map>
 #include <mutex>
-#include <utility>
 
 #include "../../include/fp8gemm.h"
 #include "kernels_decode.h"
+#include "kernels_exact.h"
 #include "kernels_gemm.h"
 #include "kernels_quant.h"
 
@@ -20,7 +21,7 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;     // rows/cols fit int32 tile math
 constexpr int kMaxDevices = 64;
-constexpr uint32_t kGemmFlags = FP8_FLAG_UE8M0 | FP8_FLAG_PRECISE;
+constexpr uint32_t kGemmFlags = FP8_FLAG_UE8M0 | FP8_FLAG_FAST_ACCUM;
 // Per-lane operand offsets inside a tile are 32-bit: 256 rows * K < 2^31.
 constexpr int64_t kMaxGemmK = (int64_t)1 << 22;
 
@@ -58,89 +59,233 @@ fp8_status launch_status() {
 // ---------------------------------------------------------------------------
 // GEMM instances.  Naming: BM x BN workgroup tile, WAVES_M x WAVES_N waves.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int MODE, int PATH, int STAGES = 2, int GROUP_M = 4,
-          bool QOUT = false>
-fp8_status launch_gemm(fp8k::GemmParams p, int cus, hipStream_t stream, int64_t m_hi = -1) {
-    // dense/contiguous: tiles over rows [p.m_lo, m_hi) (all rows by default)
+// A persistent launch of `kern` over the tiles of BM x BN: one workgroup per
+// compute unit, at most one per tile.  Dense/contiguous: tiles over rows
+// [p.m_lo, m_hi) (all rows by default).
+template <int BM, int BN, int MODE, typename Kernel>
+fp8_status launch_tiles(Kernel kern, int threads, fp8k::GemmParams p, int group_m, int cus,
+                        hipStream_t stream, int64_t m_hi) {
     if (m_hi < 0) m_hi = p.M;
     p.m_tiles = (int)((MODE == fp8k::kMasked ? p.max_m : m_hi - p.m_lo) + BM - 1) / BM;
     p.n_tiles = (int)((p.N + BN - 1) / BN);
-    p.group_m = GROUP_M;
+    p.group_m = group_m;
     int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
     if (MODE == fp8k::kMasked) tiles *= p.E;   // upper bound; the kernel counts the real ones
     int grid = (int)(tiles < cus ? tiles : cus);
     if (grid <= 0) return FP8_OK;
-    hipLaunchKernelGGL((fp8k::gemm_kernel<BM, BN, WM, WN, MODE, PATH, STAGES, QOUT>), dim3(grid),
-                       dim3(64 * WM * WN), 0, stream, p.xq, p.sa, p.wq, p.sb, p.y, p.m_indices,
-                       p.masked_m, p);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, stream, p.xq, p.sa, p.wq, p.sb, p.y,
+                       p.m_indices, p.masked_m, p);
     return launch_status();
 }
 
-// Decode-sized dense GEMM (M <= 32): one workgroup per 16*NW output columns
-// and all M rows, one wave per 16 columns; MSUB = ceil(M/16) row subtiles.
-// With fewer column tiles than compute units the K chunks are split over up
-// to 8 workgroups per tile (one workgroup per CU in all): they write FP32
-// partial sums to the stream's split workspace and a second kernel adds them
-// in split order and rounds to BF16.  Without a workspace the GEMM runs
-// unsplit.
-// Split-K workspace of the decode GEMM: one buffer per (device, stream),
-// sized for the largest split the device takes (8 splits x 32 rows x fewer
-// than 96*CUs columns of FP32), allocated on first use and kept until the
-// process ends.  Calls on one stream are ordered, so they can share it; other
-// streams have their own.  Nothing is allocated while the stream is being
-// captured into a graph, nor past kMaxSplitWorkspaces buffers in the process
-// (a caller that makes a new stream per call would otherwise add one per
-// stream): the GEMM then runs unsplit.
-constexpr size_t kMaxSplitWorkspaces = 16;
-std::mutex g_split_mu;
-std::map<std::pair<int, hipStream_t>, void*> g_split_ws;
-
-size_t split_ws_bytes(int cus) { return (size_t)8 * 32 * 96 * (size_t)cus * sizeof(float); }
-
-void* split_workspace(int cus, hipStream_t stream) {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    std::lock_guard<std::mutex> lock(g_split_mu);
-    const auto key = std::make_pair(dev, stream);
-    const auto it = g_split_ws.find(key);
-    if (it != g_split_ws.end()) return it->second;
-    if (g_split_ws.size() >= kMaxSplitWorkspaces) return nullptr;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    void* ws = nullptr;
-    if (hipMalloc(&ws, split_ws_bytes(cus)) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    g_split_ws[key] = ws;
-    return ws;
+// The FP8-instruction kernel (FP8_FLAG_FAST_ACCUM and the MX paths).
+template <int BM, int BN, int WM, int WN, int MODE, int PATH, int STAGES = 2, int GROUP_M = 4,
+          bool QOUT = false>
+fp8_status launch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream, int64_t m_hi = -1) {
+    return launch_tiles<BM, BN, MODE>(fp8k::gemm_kernel<BM, BN, WM, WN, MODE, PATH, STAGES, QOUT>, 64 * WM * WN,
+                                      p, GROUP_M, cus, stream, m_hi);
 }
 
-template <int NW, int NS, bool POW2>
-fp8_status launch_decode(const fp8k::GemmParams& p0, int cus, hipStream_t stream) {
-    fp8k::GemmParams p = p0;
-    const int64_t tiles = (p.N + 16 * NW - 1) / (16 * NW);
-    if (tiles <= 0) return FP8_OK;
-    const int64_t nct = (p.K / 128 + 3) / 4;          // K chunks of 4 blocks
+// The exact-partial kernel (the default path).
+template <int BM, int BN, int WM, int WN, int MODE, bool POW2, int STAGES, bool QOUT = false>
+fp8_status launch_exact(const fp8k::GemmParams& p, int cus, hipStream_t stream, int64_t m_hi = -1) {
+    return launch_tiles<BM, BN, MODE>(fp8k::gemm_exact_kernel<BM, BN, WM, WN, MODE, POW2, STAGES, QOUT>,
+                                      64 * WM * WN, p, 4, cus, stream, m_hi);
+}
+
+// ---------------------------------------------------------------------------
+// Instance choice.  Pure integer arithmetic on the shape and the compute-unit
+// count, so that fp8_gemm_plan can report it and tests can check it on the
+// host; the launches below follow the plan.
+// ---------------------------------------------------------------------------
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+enum Inst : int {
+    // FP8-instruction kernel (FP8_FLAG_FAST_ACCUM, MX paths)
+    kFastDecode, kFastDecodeKx, kFast64x96, kFast256x224, kFast256x256, kFast256x128, kFast128x128,
+    kFast128x256, kFast128x64,
+    // exact-partial kernel (default)
+    kExact64x96, kExact256x256, kExact128x256, kExact128x128, kExactQ256x256, kExactQ128x256,
+};
+
+struct InstInfo { int bm, bn, waves, kernel, exact; };
+InstInfo inst_info(Inst i) {
+    switch (i) {
+        case kFastDecode: return {32, 96, 6, 1, 0};
+        case kFastDecodeKx: return {48, 96, 8, 2, 0};
+        case kFast64x96: return {64, 96, 4, 0, 0};
+        case kFast256x224: return {256, 224, 8, 0, 0};
+        case kFast256x256: return {256, 256, 8, 0, 0};
+        case kFast256x128: return {256, 128, 8, 0, 0};
+        case kFast128x128: return {128, 128, 4, 0, 0};
+        case kFast128x256: return {128, 256, 8, 0, 0};
+        case kFast128x64: return {128, 64, 8, 0, 0};
+        case kExact64x96: return {64, 96, 6, 0, 1};
+        case kExact256x256: return {256, 256, 8, 0, 1};
+        case kExact128x256: return {128, 256, 8, 0, 1};
+        case kExact128x128: return {128, 128, 4, 0, 1};
+        case kExactQ256x256: return {256, 256, 8, 0, 1};
+        case kExactQ128x256: return {128, 256, 4, 0, 1};
+    }
+    return {0, 0, 0, 0, 0};
+}
+
+// Decode split-K: workgroups along K per 96-column tile of the M <= 32 decode
+// kernel (FP8 instruction path), when the column tiles are fewer than the
+// compute units and the caller's workspace holds the partial sums.
+constexpr int kDecodeTileN = 96;
+size_t decode_ws_bytes(int64_t splits, int64_t M, int64_t N) { return (size_t)(splits * M * N) * sizeof(float); }
+int64_t decode_splits(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
+    const int64_t tiles = cdiv(N, kDecodeTileN);
+    const int64_t nct = cdiv(K / 128, 4);          // K chunks of 4 blocks
     int64_t splits = tiles < cus ? cus / tiles : 1;
     if (splits > nct) splits = nct;
     if (splits > 8) splits = 8;
     if (splits < 1) splits = 1;
-    void* ws = nullptr;
-    if (splits > 1) {
-        // splits <= 8, M <= 32, N < 96 * cus: the buffer always holds them
-        ws = (size_t)(splits * p.M * p.N) * sizeof(float) <= split_ws_bytes(cus) ? split_workspace(cus, stream)
-                                                                                : nullptr;
-        if (!ws) splits = 1;
+    if (splits > 1 && decode_ws_bytes(splits, M, N) > ws_bytes) splits = 1;
+    return splits;
+}
+
+struct Plan {
+    Inst main;
+    int64_t main_rows;      // contiguous: the main launch covers rows [0, main_rows)
+    Inst tail;              // contiguous: the launch over [main_rows, M), if main_rows < M
+    int64_t k_splits;       // decode kernel
+};
+
+// The FP8-instruction paths.  Compute-bound shapes use 8 waves (2 per SIMD)
+// so that one wave's promotion FMAs run while the other wave's MFMAs occupy
+// the matrix core.
+Plan plan_fast(int mode, int64_t M, int64_t N, int64_t K, bool mx, bool qout, int cus, size_t ws_bytes) {
+    Plan pl{kFast128x128, M, kFast128x128, 1};
+    if (mode == fp8k::kDense) {
+        if (qout) {
+            // quantized output: 128-column output groups need a tile width of
+            // 128 or 256 with 64-column waves
+            if (cdiv(M, 256) * cdiv(N, 256) >= cus) pl.main = kFast256x256;
+            else if (cdiv(M, 256) * cdiv(N, 128) >= 2 * cus) pl.main = kFast256x128;
+            else pl.main = kFast128x128;
+            return pl;
+        }
+        if (M <= 64) {
+            // M <= 32: the decode kernel (96 columns per workgroup, one wave
+            // per 16 W rows).  Above 32 rows each of its waves re-reads an X
+            // block larger than its W block from LDS; 33..48 rows with
+            // K <= 1664 take the X-resident decode kernel (waves splitting K),
+            // and the rest the 64x96 tile of the main kernel.  Kernel trace,
+            // N 24576, K 1536: M 16 7.3 vs 10.3 us (64x96), M 32 8.8 vs 10.3,
+            // M 48 9.6 (X-resident) vs 10.4, M 64 10.7 (X-resident) and 12.2
+            // (decode) vs 10.0-10.4.  A 32-column decode workgroup (more of
+            // them, several per CU) measured slower on every shape tried.
+            if (!mx && M <= 32) {
+                pl.main = kFastDecode;
+                pl.k_splits = decode_splits(M, N, K, cus, ws_bytes);
+            } else if (!mx && M <= 48 && K <= fp8k::kDecodeKxMaxK) {
+                pl.main = kFastDecodeKx;
+            } else {
+                pl.main = kFast64x96;
+            }
+            return pl;
+        }
+        const int64_t huge = cdiv(M, 256) * cdiv(N, 256);
+        if (huge >= cus) {
+            // 256x224 when it takes fewer waves' worth of tile area (e.g.
+            // N = 7168: 32 tiles of 224 per row fill two whole waves where
+            // 28 tiles of 256 leave the second one a quarter empty; the
+            // DeepGEMM page, section "非对齐块大小", makes the same trade
+            // with 112-column blocks)
+            const int64_t t224 = cdiv(M, 256) * cdiv(N, 224);
+            const int64_t cost256 = cdiv(huge, cus) * 256;
+            const int64_t cost224 = cdiv(t224, cus) * 224;
+            pl.main = cost224 < cost256 ? kFast256x224 : kFast256x256;
+        } else if (cdiv(M, 256) * cdiv(N, 128) >= 2 * cus) {
+            pl.main = kFast256x128;
+        } else {
+            pl.main = kFast128x128;
+        }
+    } else if (mode == fp8k::kContiguous) {
+        // The M tile must equal the layout alignment (128): one expert per
+        // tile.  When the last round of 128x256 tiles would leave over half of
+        // the CUs idle, the full rounds' 128-row blocks run as one launch and
+        // the remaining blocks as a second one with 128x64 tiles (8 waves of
+        // 32x32), four times as many (8 experts x 8192 tokens, N 4096: 1088
+        // tiles = 4.25 rounds -> 4 full rounds + 256 tiles of 128x64;
+        // measured 343 -> 327 us).
+        pl.main = kFast128x256;
+        const int64_t mt = cdiv(M, 128), nt = cdiv(N, 256);
+        const int64_t full = mt * nt / cus, last = mt * nt - full * cus;
+        const int64_t m_main = full * cus / nt;   // 128-row blocks of the full rounds
+        if (full >= 1 && 2 * last < cus && m_main < mt) {
+            pl.main_rows = m_main * 128;
+            pl.tail = kFast128x64;
+        }
+    } else {
+        // Masked: 128-row tiles pad each expert's rows less than 256-row ones,
+        // and 256 columns per tile halve the re-reads of the expert's X rows
+        // (measured 94 -> 82 us on 16 experts x 256 rows, N 7168, K 2048).
+        pl.main = kFast128x256;
     }
+    return pl;
+}
+
+// The exact-partial path (FP16 matrix instruction on E4M3 operands widened
+// exactly).  Waves hold 64x128 (or 64x64) of 32x32 subtiles.
+Plan plan_exact(int mode, int64_t M, int64_t N, bool qout, int cus) {
+    Plan pl{kExact128x128, M, kExact128x128, 1};
+    if (mode == fp8k::kDense) {
+        if (qout) {
+            // a 1x128 output group per wave: 128-column waves
+            pl.main = cdiv(M, 256) * cdiv(N, 256) >= cus ? kExactQ256x256 : kExactQ128x256;
+        } else if (M <= 64) {
+            pl.main = kExact64x96;
+        } else if (cdiv(M, 256) * cdiv(N, 256) >= cus) {
+            pl.main = kExact256x256;
+        } else if (cdiv(M, 128) * cdiv(N, 256) >= cus) {
+            pl.main = kExact128x256;
+        } else {
+            pl.main = kExact128x128;
+        }
+    } else if (mode == fp8k::kContiguous) {
+        // 128-row tiles (the layout alignment); the blocks past the last full
+        // round of 128x256 tiles run as 128x128 tiles when that round would
+        // leave over half of the CUs idle
+        pl.main = kExact128x256;
+        const int64_t mt = cdiv(M, 128), nt = cdiv(N, 256);
+        const int64_t full = mt * nt / cus, last = mt * nt - full * cus;
+        const int64_t m_main = full * cus / nt;
+        if (full >= 1 && 2 * last < cus && m_main < mt) {
+            pl.main_rows = m_main * 128;
+            pl.tail = kExact128x128;
+        }
+    } else {
+        pl.main = kExact128x256;
+    }
+    return pl;
+}
+
+Plan make_plan(int mode, int64_t M, int64_t N, int64_t K, uint32_t flags, bool mx, bool qout, int cus,
+               size_t ws_bytes) {
+    return (mx || (flags & FP8_FLAG_FAST_ACCUM)) ? plan_fast(mode, M, N, K, mx, qout, cus, ws_bytes)
+                                                 : plan_exact(mode, M, N, qout, cus);
+}
+
+// ---------------------------------------------------------------------------
+// Launches.
+// ---------------------------------------------------------------------------
+// Decode-sized dense GEMM (M <= 32): one workgroup per 16*NW output columns
+// and all M rows, one wave per 16 columns; MSUB = ceil(M/16) row subtiles.
+// With splits > 1 the K chunks are split over that many workgroups per tile:
+// they write FP32 partial sums to the caller's workspace and a second kernel
+// adds them in split order and rounds to BF16.
+template <int NW, int NS, bool POW2>
+fp8_status launch_decode(const fp8k::GemmParams& p0, int64_t splits, void* ws, hipStream_t stream) {
+    static_assert(16 * NW == kDecodeTileN, "decode tile width");
+    fp8k::GemmParams p = p0;
+    const int64_t tiles = cdiv(p.N, 16 * NW);
+    if (tiles <= 0) return FP8_OK;
+    if (splits <= 1) ws = nullptr;
     p.part = static_cast<float*>(ws);
-    const dim3 grid((unsigned)tiles, (unsigned)splits), block(64 * NW);
+    const dim3 grid((unsigned)tiles, (unsigned)(ws ? splits : 1)), block(64 * NW);
     switch ((p.M + 15) / 16) {
         case 1: hipLaunchKernelGGL((fp8k::decode_kernel<1, NW, NS, POW2>), grid, block, 0, stream,
                                    p.xq, p.sa, p.wq, p.sb, p.y, p); break;
@@ -151,7 +296,7 @@ fp8_status launch_decode(const fp8k::GemmParams& p0, int cus, hipStream_t stream
     fp8_status st = launch_status();
     if (ws && st == FP8_OK) {
         const int64_t mn = p.M * p.N;
-        hipLaunchKernelGGL(fp8k::decode_split_reduce, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, stream,
+        hipLaunchKernelGGL(fp8k::decode_split_reduce, dim3((unsigned)cdiv(mn, 256)), dim3(256), 0, stream,
                            static_cast<const float*>(ws), (int)splits, mn, p.y);
         st = launch_status();
     }
@@ -162,135 +307,119 @@ fp8_status launch_decode(const fp8k::GemmParams& p0, int cus, hipStream_t stream
 // in LDS, waves splitting K.
 template <bool POW2>
 fp8_status launch_decode_kx(const fp8k::GemmParams& p, hipStream_t stream) {
-    const int64_t tiles = (p.N + 95) / 96;
+    const int64_t tiles = cdiv(p.N, 96);
     if (tiles <= 0) return FP8_OK;
     hipLaunchKernelGGL((fp8k::decode_kx_kernel<3, POW2>), dim3((unsigned)tiles), dim3(512), 0, stream,
                        p.xq, p.sa, p.wq, p.sb, p.y, p);
     return launch_status();
 }
 
-// Instances.  Compute-bound shapes use 8 waves (2 per SIMD) so that one wave's
-// promotion FMAs run while the other wave's MFMAs occupy the matrix core.
+// One launch of instance `i` (m_hi: dense/contiguous rows [p.m_lo, m_hi)).
 template <int MODE, int PATH>
-fp8_status dispatch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream) {
+fp8_status launch_fast(Inst i, const fp8k::GemmParams& p, int64_t splits, void* ws, int cus, hipStream_t stream,
+                       int64_t m_hi, bool qout) {
+    constexpr bool kPow2 = PATH == fp8k::kPathFp8Pow2;
+    constexpr bool kBlock = PATH == fp8k::kPathFp8 || PATH == fp8k::kPathFp8Pow2;
     if constexpr (MODE == fp8k::kDense) {
-        if (p.M <= 64) {
-            // FP8 MFMA paths.  M <= 32: the decode kernel (96 columns per
-            // workgroup, one wave per 16 W rows).  Above 32 rows each of its
-            // waves re-reads an X block larger than its W block from LDS;
-            // 33..48 rows with K <= 1664 take the X-resident decode kernel
-            // (waves splitting K), and the rest the 64x96 tile of the main
-            // kernel.  Kernel trace, N 24576, K 1536: M 16 7.3 vs 10.3 us
-            // (64x96), M 32 8.8 vs 10.3, M 48 9.6 (X-resident) vs 10.4, M 64
-            // 10.7 (X-resident) and 12.2 (decode) vs 10.0-10.4.  A 32-column
-            // decode workgroup (more of them, several per CU) measured slower
-            // on every shape tried.
-            if constexpr (PATH == fp8k::kPathFp8 || PATH == fp8k::kPathFp8Pow2) {
-                if (p.M <= 32) return launch_decode<6, 5, PATH == fp8k::kPathFp8Pow2>(p, cus, stream);
-                if (p.M <= 48 && p.K <= fp8k::kDecodeKxMaxK)
-                    return launch_decode_kx<PATH == fp8k::kPathFp8Pow2>(p, stream);
+        if constexpr (kBlock) {
+            if (qout) {
+                switch (i) {
+                    case kFast256x256: return launch_gemm<256, 256, 2, 4, MODE, PATH, 2, 4, true>(p, cus, stream);
+                    case kFast256x128: return launch_gemm<256, 128, 4, 2, MODE, PATH, 3, 4, true>(p, cus, stream);
+                    case kFast128x128: return launch_gemm<128, 128, 2, 2, MODE, PATH, 4, 4, true>(p, cus, stream);
+                    default: return FP8_ERR_UNSUPPORTED;
+                }
             }
-            return launch_gemm<64, 96, 2, 2, MODE, PATH, 3>(p, cus, stream);
+            if (i == kFastDecode) return launch_decode<6, 5, kPow2>(p, splits, ws, stream);
+            if (i == kFastDecodeKx) return launch_decode_kx<kPow2>(p, stream);
         }
-        constexpr bool kF16 = PATH == fp8k::kPathF16 || PATH == fp8k::kPathF16Pow2;
-        const int64_t huge = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-        if constexpr (!kF16) {
-            if (huge >= cus) {
-                // 256x224 when it takes fewer waves' worth of tile area (e.g.
-                // N = 7168: 32 tiles of 224 per row fill two whole waves where
-                // 28 tiles of 256 leave the second one a quarter empty)
-                const int64_t t224 = ((p.M + 255) / 256) * ((p.N + 223) / 224);
-                const int64_t cost256 = ((huge + cus - 1) / cus) * 256;
-                const int64_t cost224 = ((t224 + cus - 1) / cus) * 224;
-                if (cost224 < cost256) return launch_gemm<256, 224, 4, 2, MODE, PATH>(p, cus, stream);
-                return launch_gemm<256, 256, 2, 4, MODE, PATH>(p, cus, stream);
-            }
+        switch (i) {
+            case kFast64x96: return launch_gemm<64, 96, 2, 2, MODE, PATH, 3>(p, cus, stream);
+            case kFast256x224: return launch_gemm<256, 224, 4, 2, MODE, PATH>(p, cus, stream);
+            case kFast256x256: return launch_gemm<256, 256, 2, 4, MODE, PATH>(p, cus, stream);
+            case kFast256x128: return launch_gemm<256, 128, 4, 2, MODE, PATH, 3>(p, cus, stream);
+            case kFast128x128: return launch_gemm<128, 128, 2, 2, MODE, PATH, 4>(p, cus, stream);
+            default: return FP8_ERR_UNSUPPORTED;
         }
-        const int64_t big = ((p.M + 255) / 256) * ((p.N + 127) / 128);
-        if (big >= 2 * cus || (kF16 && huge >= cus)) return launch_gemm<256, 128, 4, 2, MODE, PATH, 3>(p, cus, stream);
-        return launch_gemm<128, 128, 2, 2, MODE, PATH, 4>(p, cus, stream);
-    } else if constexpr (MODE == fp8k::kContiguous) {
-        // The M tile must equal the layout alignment (128): one expert per tile.
-        // When the last round of 128x256 tiles would leave over half of the
-        // CUs idle, the full rounds' 128-row blocks run as one launch and the
-        // remaining blocks as a second one with 128x64 tiles (8 waves of
-        // 32x32), four times as many (8 experts x 8192 tokens, N 4096: 1088
-        // tiles = 4.25 rounds -> 4 full rounds + 256 tiles of 128x64; measured
-        // 343 -> 327 us).
-        const int64_t mt = (p.M + 127) / 128, nt = (p.N + 255) / 256;
-        const int64_t full = mt * nt / cus, last = mt * nt - full * cus;
-        const int64_t m_main = full * cus / nt;   // 128-row blocks of the full rounds
-        if (full >= 1 && 2 * last < cus && m_main < mt) {
-            fp8_status st = launch_gemm<128, 256, 2, 4, MODE, PATH, 3>(p, cus, stream, m_main * 128);
-            if (st != FP8_OK) return st;
-            fp8k::GemmParams t = p;
-            t.m_lo = m_main * 128;
-            return launch_gemm<128, 64, 4, 2, MODE, PATH, 4>(t, cus, stream);
+    } else if constexpr (kBlock) {
+        switch (i) {
+            case kFast128x256: return launch_gemm<128, 256, 2, 4, MODE, PATH, 3>(p, cus, stream, m_hi);
+            case kFast128x64:
+                if constexpr (MODE == fp8k::kContiguous) return launch_gemm<128, 64, 4, 2, MODE, PATH, 4>(p, cus, stream, m_hi);
+                else return FP8_ERR_UNSUPPORTED;
+            default: return FP8_ERR_UNSUPPORTED;
         }
-        return launch_gemm<128, 256, 2, 4, MODE, PATH, 3>(p, cus, stream);
     } else {
-        // Masked: 128-row tiles pad each expert's rows less than 256-row ones,
-        // and 256 columns per tile halve the re-reads of the expert's X rows
-        // (measured 94 -> 82 us on 16 experts x 256 rows, N 7168, K 2048).
-        return launch_gemm<128, 256, 2, 4, MODE, PATH, 3>(p, cus, stream);
+        return FP8_ERR_UNSUPPORTED;
     }
 }
 
-// Quantized-output instances: 128-column output groups need a tile width of
-// 128 or 256 with 64-column waves (no 256x224, no 64x96).
-template <int PATH>
-fp8_status dispatch_qout(const fp8k::GemmParams& p, int cus, hipStream_t stream) {
-    constexpr bool kF16 = PATH == fp8k::kPathF16 || PATH == fp8k::kPathF16Pow2;
-    const int64_t huge = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-    if constexpr (!kF16)
-        if (huge >= cus) return launch_gemm<256, 256, 2, 4, fp8k::kDense, PATH, 2, 4, true>(p, cus, stream);
-    const int64_t big = ((p.M + 255) / 256) * ((p.N + 127) / 128);
-    if (big >= 2 * cus || (kF16 && huge >= cus))
-        return launch_gemm<256, 128, 4, 2, fp8k::kDense, PATH, 3, 4, true>(p, cus, stream);
-    return launch_gemm<128, 128, 2, 2, fp8k::kDense, PATH, 4, 4, true>(p, cus, stream);
+template <int MODE, bool POW2>
+fp8_status launch_exact_inst(Inst i, const fp8k::GemmParams& p, int cus, hipStream_t stream, int64_t m_hi) {
+    if constexpr (MODE == fp8k::kDense) {
+        switch (i) {
+            case kExact64x96: return launch_exact<64, 96, 2, 3, MODE, POW2, 3>(p, cus, stream);
+            case kExact256x256: return launch_exact<256, 256, 4, 2, MODE, POW2, 2>(p, cus, stream);
+            case kExact128x256: return launch_exact<128, 256, 2, 4, MODE, POW2, 3>(p, cus, stream);
+            case kExact128x128: return launch_exact<128, 128, 2, 2, MODE, POW2, 4>(p, cus, stream);
+            case kExactQ256x256: return launch_exact<256, 256, 4, 2, MODE, POW2, 2, true>(p, cus, stream);
+            case kExactQ128x256: return launch_exact<128, 256, 2, 2, MODE, POW2, 3, true>(p, cus, stream);
+            default: return FP8_ERR_UNSUPPORTED;
+        }
+    } else {
+        switch (i) {
+            case kExact128x256: return launch_exact<128, 256, 2, 4, MODE, POW2, 3>(p, cus, stream, m_hi);
+            case kExact128x128:
+                if constexpr (MODE == fp8k::kContiguous) return launch_exact<128, 128, 2, 2, MODE, POW2, 4>(p, cus, stream, m_hi);
+                else return FP8_ERR_UNSUPPORTED;
+            default: return FP8_ERR_UNSUPPORTED;
+        }
+    }
 }
 
-fp8_status run_gemm_qout(const fp8k::GemmParams& p, uint32_t flags, hipStream_t stream) {
-    int cus = 0;
-    fp8_status st = current_device_cus(&cus);
-    if (st != FP8_OK) return st;
-    const bool pow2 = flags & FP8_FLAG_UE8M0, precise = flags & FP8_FLAG_PRECISE;
-    if (precise)
-        return pow2 ? dispatch_qout<fp8k::kPathF16Pow2>(p, cus, stream)
-                    : dispatch_qout<fp8k::kPathF16>(p, cus, stream);
-    return pow2 ? dispatch_qout<fp8k::kPathFp8Pow2>(p, cus, stream)
-                : dispatch_qout<fp8k::kPathFp8>(p, cus, stream);
+// Runs a plan: the main launch, then (contiguous) the tail launch.
+template <int MODE, int PATH>
+fp8_status run_plan(const Plan& pl, bool exact, const fp8k::GemmParams& p, void* ws, int cus,
+                    hipStream_t stream, bool qout) {
+    constexpr bool kPow2 = PATH == fp8k::kPathFp8Pow2;
+    auto one = [&](Inst i, const fp8k::GemmParams& q, int64_t m_hi) {
+        return exact ? launch_exact_inst<MODE, kPow2>(i, q, cus, stream, m_hi)
+                     : launch_fast<MODE, PATH>(i, q, pl.k_splits, ws, cus, stream, m_hi, qout);
+    };
+    if (MODE == fp8k::kContiguous && pl.main_rows < p.M) {
+        fp8_status st = one(pl.main, p, pl.main_rows);
+        if (st != FP8_OK) return st;
+        fp8k::GemmParams t = p;
+        t.m_lo = pl.main_rows;
+        return one(pl.tail, t, -1);
+    }
+    return one(pl.main, p, -1);
 }
 
+// Block-scaled GEMM call of layout MODE: plan, then launch.
 template <int MODE>
-fp8_status run_gemm(const fp8k::GemmParams& p, uint32_t flags, hipStream_t stream) {
+fp8_status run_gemm(const fp8k::GemmParams& p, uint32_t flags, void* ws, size_t ws_bytes, hipStream_t stream,
+                    bool qout = false) {
     int cus = 0;
     fp8_status st = current_device_cus(&cus);
     if (st != FP8_OK) return st;
-    const bool pow2 = flags & FP8_FLAG_UE8M0, precise = flags & FP8_FLAG_PRECISE;
-    if (precise)
-        return pow2 ? dispatch_gemm<MODE, fp8k::kPathF16Pow2>(p, cus, stream)
-                    : dispatch_gemm<MODE, fp8k::kPathF16>(p, cus, stream);
-    return pow2 ? dispatch_gemm<MODE, fp8k::kPathFp8Pow2>(p, cus, stream)
-                : dispatch_gemm<MODE, fp8k::kPathFp8>(p, cus, stream);
+    const Plan pl = make_plan(MODE, p.M, p.N, p.K, flags, false, qout, cus, ws_bytes);
+    const bool exact = !(flags & FP8_FLAG_FAST_ACCUM);
+    return (flags & FP8_FLAG_UE8M0) ? run_plan<MODE, fp8k::kPathFp8Pow2>(pl, exact, p, ws, cus, stream, qout)
+                                    : run_plan<MODE, fp8k::kPathFp8>(pl, exact, p, ws, cus, stream, qout);
 }
 
 bool dims_ok(int64_t a) { return a >= 0 && a < kMaxDim; }
 
-// MXFP8: the dense instance table with the MX path (scales as per-lane E8M0
-// operands, no promotion).
+// MXFP8 / MXFP4 weights: the dense FP8-instruction instances with the MX path
+// (scales as per-lane E8M0 operands, no promotion).
+template <int PATH>
 fp8_status run_gemm_mx(const fp8k::GemmParams& p, hipStream_t stream) {
     int cus = 0;
     fp8_status st = current_device_cus(&cus);
     if (st != FP8_OK) return st;
-    return dispatch_gemm<fp8k::kDense, fp8k::kPathMx>(p, cus, stream);
-}
-
-fp8_status run_gemm_mx_w4(const fp8k::GemmParams& p, hipStream_t stream) {
-    int cus = 0;
-    fp8_status st = current_device_cus(&cus);
-    if (st != FP8_OK) return st;
-    return dispatch_gemm<fp8k::kDense, fp8k::kPathMxW4>(p, cus, stream);
+    const Plan pl = make_plan(fp8k::kDense, p.M, p.N, p.K, 0, true, false, cus, 0);
+    return launch_fast<fp8k::kDense, PATH>(pl.main, p, 1, nullptr, cus, stream, -1, false);
 }
 
 }  // namespace
@@ -391,7 +520,7 @@ fp8_status fp8_gemm_nt_mx(const uint8_t* xq, const uint32_t* ea, const uint8_t* 
     p.sa = reinterpret_cast<const float*>(ea);   // packed scale tables, read as such by the MX path
     p.sb = reinterpret_cast<const float*>(eb);
     p.M = M; p.N = N; p.K = K; p.E = 1;
-    return run_gemm_mx(p, (hipStream_t)stream);
+    return run_gemm_mx<fp8k::kPathMx>(p, (hipStream_t)stream);
 }
 
 fp8_status fp8_quant_mxfp4(const float* x, int64_t R, int64_t K, uint8_t* q, uint32_t* e, void* stream) {
@@ -426,25 +555,78 @@ fp8_status fp8_gemm_nt_mx_w4(const uint8_t* xq, const uint32_t* ea, const uint8_
     p.sa = reinterpret_cast<const float*>(ea);
     p.sb = reinterpret_cast<const float*>(eb);
     p.M = M; p.N = N; p.K = K; p.E = 1;
-    return run_gemm_mx_w4(p, (hipStream_t)stream);
+    return run_gemm_mx<fp8k::kPathMxW4>(p, (hipStream_t)stream);
 }
 
-fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sb,
-                       uint16_t* y, int64_t M, int64_t N, int64_t K, uint32_t flags,
-                       void* stream) {
+fp8_status fp8_gemm_nt_ws(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sb,
+                          uint16_t* y, int64_t M, int64_t N, int64_t K, uint32_t flags, void* workspace,
+                          size_t workspace_bytes, void* stream) {
     if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K) || (flags & ~kGemmFlags))
         return FP8_ERR_INVALID_ARG;
     if (K % 128) return FP8_ERR_SHAPE;
     if (K > kMaxGemmK) return FP8_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return FP8_OK;
     if (K == 0) return FP8_ERR_SHAPE;
-    if (!xq || !sa || !wq || !sb || !y) return FP8_ERR_INVALID_ARG;
-    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(sa) || !aligned16(sb))
+    if (!xq || !sa || !wq || !sb || !y || (workspace_bytes && !workspace)) return FP8_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(sa) || !aligned16(sb) ||
+        !aligned16(workspace))
         return FP8_ERR_ALIGNMENT;
     fp8k::GemmParams p{};
     p.xq = xq; p.sa = sa; p.wq = wq; p.sb = sb; p.y = y;
     p.M = M; p.N = N; p.K = K; p.E = 1;
-    return run_gemm<fp8k::kDense>(p, flags, (hipStream_t)stream);
+    return run_gemm<fp8k::kDense>(p, flags, workspace, workspace ? workspace_bytes : 0, (hipStream_t)stream);
+}
+
+fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sb,
+                       uint16_t* y, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                       void* stream) {
+    return fp8_gemm_nt_ws(xq, sa, wq, sb, y, M, N, K, flags, nullptr, 0, stream);
+}
+
+size_t fp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, uint32_t flags) {
+    if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K) || (flags & ~kGemmFlags) || K % 128 || M == 0 || N == 0)
+        return 0;
+    int cus = 0;
+    if (current_device_cus(&cus) != FP8_OK) return 0;
+    const Plan pl = make_plan(fp8k::kDense, M, N, K, flags, false, false, cus, SIZE_MAX);
+    return pl.main == kFastDecode && pl.k_splits > 1 ? decode_ws_bytes(pl.k_splits, M, N) : 0;
+}
+
+fp8_status fp8_gemm_plan(int32_t layout, int64_t M, int64_t N, int64_t K, uint32_t flags, int32_t compute_units,
+                         size_t workspace_bytes, fp8_gemm_plan_t* plan) {
+    const uint32_t known = kGemmFlags | FP8_PLAN_MX | FP8_PLAN_QOUT;
+    if (!plan || layout < 0 || layout > 2 || !dims_ok(M) || !dims_ok(N) || !dims_ok(K) || compute_units <= 0 ||
+        (flags & ~known))
+        return FP8_ERR_INVALID_ARG;
+    if (K % 128) return FP8_ERR_SHAPE;
+    const bool mx = flags & FP8_PLAN_MX, qout = flags & FP8_PLAN_QOUT;
+    if ((mx || qout) && layout != 0) return FP8_ERR_INVALID_ARG;
+    const Plan pl = make_plan(layout, M, N, K, flags & kGemmFlags, mx, qout, compute_units, workspace_bytes);
+    const InstInfo a = inst_info(pl.main);
+    *plan = fp8_gemm_plan_t{};
+    plan->exact = a.exact;
+    plan->kernel = a.kernel;
+    plan->tile_m = a.bm;
+    plan->tile_n = a.bn;
+    plan->waves = a.waves;
+    plan->main_rows = layout == 1 ? pl.main_rows : M;
+    plan->k_splits = (int32_t)pl.k_splits;
+    plan->workspace_bytes = pl.k_splits > 1 ? decode_ws_bytes(pl.k_splits, M, N) : 0;
+    if (a.kernel != 0) {
+        plan->tiles = cdiv(N, kDecodeTileN) * pl.k_splits;
+        plan->grid = (int32_t)plan->tiles;
+    } else {
+        const int64_t rows = layout == 1 ? pl.main_rows : M;
+        plan->tiles = cdiv(rows, a.bm) * cdiv(N, a.bn);
+        plan->grid = (int32_t)(plan->tiles < compute_units ? plan->tiles : compute_units);
+    }
+    if (layout == 1 && pl.main_rows < M) {
+        const InstInfo t = inst_info(pl.tail);
+        plan->tail_tile_m = t.bm;
+        plan->tail_tile_n = t.bn;
+        plan->tail_tiles = cdiv(M - pl.main_rows, t.bm) * cdiv(N, t.bn);
+    }
+    return FP8_OK;
 }
 
 fp8_status fp8_gemm_nt_qout(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sb,
@@ -463,7 +645,7 @@ fp8_status fp8_gemm_nt_qout(const uint8_t* xq, const float* sa, const uint8_t* w
     fp8k::GemmParams p{};
     p.xq = xq; p.sa = sa; p.wq = wq; p.sb = sb; p.yq = yq; p.sy = sy;
     p.M = M; p.N = N; p.K = K; p.E = 1;
-    return run_gemm_qout(p, flags, (hipStream_t)stream);
+    return run_gemm<fp8k::kDense>(p, flags, nullptr, 0, (hipStream_t)stream, true);
 }
 
 fp8_status fp8_grouped_gemm_contiguous(const uint8_t* xq, const float* sa, const uint8_t* wq,
@@ -483,7 +665,7 @@ fp8_status fp8_grouped_gemm_contiguous(const uint8_t* xq, const float* sa, const
     fp8k::GemmParams p{};
     p.xq = xq; p.sa = sa; p.wq = wq; p.sb = sb; p.y = y; p.m_indices = m_indices;
     p.M = M; p.N = N; p.K = K; p.E = E;
-    return run_gemm<fp8k::kContiguous>(p, flags, (hipStream_t)stream);
+    return run_gemm<fp8k::kContiguous>(p, flags, nullptr, 0, (hipStream_t)stream);
 }
 
 fp8_status fp8_grouped_gemm_masked(const uint8_t* xq, const float* sa, const uint8_t* wq,
@@ -504,7 +686,7 @@ fp8_status fp8_grouped_gemm_masked(const uint8_t* xq, const float* sa, const uin
     fp8k::GemmParams p{};
     p.xq = xq; p.sa = sa; p.wq = wq; p.sb = sb; p.y = y; p.masked_m = masked_m;
     p.M = (int64_t)E * max_m; p.N = N; p.K = K; p.E = E; p.max_m = max_m;
-    return run_gemm<fp8k::kMasked>(p, flags, (hipStream_t)stream);
+    return run_gemm<fp8k::kMasked>(p, flags, nullptr, 0, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,210 @@
+// gemm_common.h -- pieces shared by the block-scaled GEMM kernels of
+// libfp8gemm.so (gfx950): launch parameters, direct-to-LDS loads through
+// buffer resources, the LDS chunk swizzle, the tile order and the decoding of
+// a tile of the grouped layouts.
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.h"
+
+namespace fp8k {
+
+enum GemmMode : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+
+// Operand pointers (passed to the kernel as separate __restrict__ arguments):
+//   xq (M, K) codes; masked: (E*max_m, K)
+//   sa [K/128][M]; masked: [K/128][E*max_m]
+//   wq (N, K); grouped: (E, N, K)
+//   sb [ceil(N/128)][K/128]; grouped: (E, N/128, K/128)
+//   y  (M, N) BF16 bits; masked: (E*max_m, N)
+//   m_indices (contiguous): expert of each row; masked_m (masked): valid rows
+struct GemmParams {
+    const uint8_t* xq;
+    const float* sa;
+    const uint8_t* wq;
+    const float* sb;
+    uint16_t* y;
+    uint8_t* yq;                // quantized output (QOUT): E4M3 codes (M, N)
+    float* sy;                  // ... and its 1x128 scales [N/128][M]
+    const int32_t* m_indices;
+    const int32_t* masked_m;
+    int64_t M;                  // rows of X (masked: E*max_m)
+    int64_t N;                  // output columns (per expert)
+    int64_t K;
+    int64_t max_m;              // masked only
+    int32_t E;
+    int64_t m_lo;               // dense/contiguous: tiles cover rows [m_lo, m_lo + m_tiles*BM)
+    int32_t m_tiles;            // dense/contiguous: ceil((rows to cover)/BM); masked: ceil(max_m/BM)
+    int32_t n_tiles;            // ceil(N/BN)
+    int32_t group_m;            // raster group height in tiles
+    float* part;                // decode split-K: FP32 partial sums [splits][M][N] (else null)
+};
+
+// Workgroup barrier without a memory fence.  Each wave has already waited on
+// its own vector-memory counter for the LDS data it needs; the barrier only
+// orders the waves.  (The fence of __syncthreads() would also wait for the
+// younger prefetch stages still in flight.)  The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (gfx9 encoding: vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14;
+// expcnt and lgkmcnt left at their maxima, i.e. not waited on).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Raw buffer resource (V#) over [base, base + bytes), held in SGPRs: loads at
+// offsets >= bytes return zeros.  gfx9 dword3: 32-bit data format, raw
+// addressing (stride 0).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    return i32x4{uniform((int)(uint32_t)b), uniform((int)(uint32_t)(b >> 32) & 0xFFFF),
+                 uniform((int)bytes), 0x00020000};
+}
+
+// A read-only, wave-uniform int32 (here a per-expert count) through the
+// scalar cache: an s_load waited on with lgkmcnt, so that it does not wait
+// for this wave's outstanding vector loads and stores.
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int i) {
+    return ((const __attribute__((address_space(4))) int32_t*)(p))[i];
+}
+
+// Byte address of an LDS location (the value M0 takes for an LDS DMA).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(FP8K_LDS const void*)p;
+}
+
+// Wave-wide DMAs from a buffer into LDS.  The loads count on this wave's
+// vmcnt.  They are issued from asm so that the compiler does not treat them
+// as LDS stores that may alias the stage being read (it would wait for every
+// DMA in flight).  M0 is restored afterwards.
+// One wave-wide 16-byte-per-lane DMA: lane l's bytes land at
+// m0 + 1024*Q + 16*l and come from buffer offset voff + 1024*Q + soff.
+template <int Q>
+__device__ __forceinline__ void dma_lds16_one(uint32_t m0, uint32_t voff, i32x4 rsrc, int soff) {
+    int saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, %4 offen offset:%5 lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff), "i"(1024 * Q));
+}
+// One wave-wide DMA of 4 bytes per lane: lane l's dword lands at m0 + 4*l.
+__device__ __forceinline__ void dma_lds4(uint32_t m0, uint32_t voff, i32x4 rsrc, int soff) {
+    int saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dword %2, %3, %4 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff));
+}
+
+// LDS chunk swizzle: chunk c of row r lives in slot c ^ swz(r).  A fragment
+// read touches 16 consecutive rows (a 16-aligned run) at one logical chunk;
+// with swz(r) = (r mod 8) ^ ((r / 8) mod 2) those reads run at the full LDS
+// rate on gfx950 (measured; r mod 8 and (r / 2) mod 8 leave a residual
+// conflict).  Depending on r mod 16 only, it keeps every subtile of a wave at
+// a fixed offset from the first.
+__device__ __forceinline__ int lds_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Logical tile -> (m tile, n tile) in grouped raster order: group_m m-tiles
+// are walked m-fastest for each n tile before the next group of m-tiles.
+__device__ __forceinline__ void raster(int t, int m_tiles, int n_tiles, int group_m, int& mt,
+                                       int& nt) {
+    const int per_group = group_m * n_tiles;
+    const int grp = t / per_group;
+    const int first = grp * group_m;
+    const int gm = min(m_tiles - first, group_m);
+    const int r = t - grp * per_group;
+    mt = first + r % gm;
+    nt = r / gm;
+}
+
+// Number of tiles in the persistent walk.  Dense and contiguous: m_tiles x
+// n_tiles.  Masked: each expert's ceil(valid / BM) m-tiles times n_tiles,
+// from the device-side counts clamped to [0, max_m] (DeepGEMM page, section
+// "分组 GEMM 的两种布局": the masked layout skips the rows past each
+// expert's count).
+template <int MODE, int BM>
+__device__ __forceinline__ int count_tiles(const GemmParams& p, const int32_t* masked_m) {
+    if constexpr (MODE == kMasked) {
+        int acc = 0;
+        for (int e = 0; e < p.E; ++e) {
+            int v = ld_uniform(masked_m, e);
+            v = v < 0 ? 0 : (v > p.max_m ? (int)p.max_m : v);
+            acc += (v + BM - 1) / BM;
+        }
+        return acc * p.n_tiles;
+    } else {
+        return p.m_tiles * p.n_tiles;
+    }
+}
+
+// Where one logical tile of the walk lies.
+struct TileCoord {
+    int64_t row0;      // first X row of the tile
+    int64_t row_end;   // rows [row0, row_end) may be read and written
+    int64_t n0;        // first output column
+    int expert;        // grouped layouts: whose weights the tile multiplies
+};
+
+// Logical tile t -> its rows, columns and expert.  Returns false when the
+// tile has nothing to compute (contiguous: a 128-row block of padding only).
+//   dense/contiguous: grouped raster order over rows [m_lo, ...);
+//   masked: an expert with nmt m-tiles owns logical tiles
+//     [base*n_tiles, (base+nmt)*n_tiles), walked m-fastest, so that the
+//     m-tiles reading the same W columns run side by side (one XCD, one L2);
+//   contiguous: the block's expert is the first index in [0, E) among its
+//     rows, in row order (DeepGEMM page, "分组 GEMM 的两种布局": each aligned
+//     block belongs to one expert).
+template <int MODE, int BM, int BN>
+__device__ __forceinline__ bool decode_tile(int t, const GemmParams& p, const int32_t* m_indices,
+                                            const int32_t* masked_m, TileCoord& tc) {
+    int mt, nt;
+    tc.expert = 0;
+    if constexpr (MODE == kMasked) {
+        const int mt_t = t / p.n_tiles;
+        int base = 0, e = 0, valid = 0, nmt = 1;
+        for (; e < p.E; ++e) {
+            valid = ld_uniform(masked_m, e);
+            valid = valid < 0 ? 0 : (valid > p.max_m ? (int)p.max_m : valid);
+            nmt = (valid + BM - 1) / BM;
+            if (mt_t < base + nmt) break;
+            base += nmt;
+        }
+        tc.expert = e;
+        const int local = t - base * p.n_tiles;
+        nt = local / nmt;
+        mt = local - nt * nmt;
+        tc.row0 = (int64_t)e * p.max_m + (int64_t)mt * BM;
+        tc.row_end = (int64_t)e * p.max_m + valid;
+    } else {
+        raster(t, p.m_tiles, p.n_tiles, p.group_m, mt, nt);
+        tc.row0 = p.m_lo + (int64_t)mt * BM;
+        tc.row_end = p.M;
+        if constexpr (MODE == kContiguous) {
+            int e = -1;
+            for (int r = 0; r < BM && tc.row0 + r < p.M; ++r) {
+                const int v = m_indices[tc.row0 + r];
+                if (v >= 0 && v < p.E) { e = v; break; }
+            }
+            if (e < 0) return false;
+            tc.expert = e;
+        }
+    }
+    tc.n0 = (int64_t)nt * BN;
+    return true;
+}
+
+// Calls f(integral_constant<int, 0>) ... f(integral_constant<int, S-1>) in order.
+template <int S, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (S > 0) {
+        static_for<S - 1>(f);
+        f(std::integral_constant<int, S - 1>{});
+    }
+}
+
+}  // namespace fp8k

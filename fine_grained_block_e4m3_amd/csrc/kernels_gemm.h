@@ -1,4 +1,7 @@
-// kernels_gemm.h -- block-scaled E4M3 NT GEMM for gfx950 (MI355X, CDNA4).
+// kernels_gemm.h -- block-scaled E4M3 NT GEMM for gfx950 (MI355X, CDNA4)
+// through the FP8 matrix instruction: the opt-in FP8_FLAG_FAST_ACCUM path of
+// the block-scaled calls, and the MXFP8 / MXFP4-weight calls.  (The default
+// block-scaled path, with exact block partials, is kernels_exact.h.)
 //
 // Computes Y = X * W^T (BF16 out) with X (M,K) E4M3 + one FP32 scale per 1x128
 // tile of a row, W (N,K) E4M3 + one FP32 scale per 128x128 block.
@@ -41,10 +44,14 @@
 //     VALU promotes the partials of column j-1, so matrix core and VALU work
 //     side by side (DeepGEMM page, "主循环骨架": promotion on the CUDA cores
 //     overlaps the tensor-core work).
-//   * Other paths of the same kernel (template PATH): FP16 products for the
-//     exact-partial option, MXFP8 with 1x32 E8M0 scales on both operands and
-//     MXFP4 (E2M1) weights; QOUT writes the output as E4M3 with 1x128 scales
-//     instead of BF16.  Decode-sized GEMMs with M <= 32 run a kernel of their
+//   * Precision.  The FP8 instruction does not sum the 128 products of a block
+//     exactly: within each group of 8 consecutive K it truncates every product
+//     to a multiple of 2^(E-13), 2^E the group's largest product (measured on
+//     gfx950, the analog of the limited FP8 accumulation the DeepGEMM page,
+//     section "细粒度缩放在 GEMM 层面引爆的两个问题", reports for H800).
+//   * Other paths of the same kernel (template PATH): MXFP8 with 1x32 E8M0
+//     scales on both operands and MXFP4 (E2M1) weights; QOUT writes the
+//     output as E4M3 with 1x128 scales instead of BF16.  Decode-sized GEMMs with M <= 32 run a kernel of their
 //     own (kernels_decode.h).
 //   * Persistent grid: each workgroup walks tiles with stride gridDim.x
 //     (DeepGEMM page, "线程组织": persistent launch with an in-kernel block
@@ -52,21 +59,15 @@
 //     running together share operand rows in L2).
 #pragma once
 
-#include <type_traits>
-
-#include "device_common.h"
+#include "gemm_common.h"
 
 namespace fp8k {
 
-enum GemmMode : int { kDense = 0, kContiguous = 1, kMasked = 2 };
 
 // How each 128-K block partial is formed.
 //   kPathFp8       one FP8 MFMA (16x16x128) per block, VALU promotion by sA*sB
 //   kPathFp8Pow2   power-of-two scales as E8M0 operands of the scaled FP8 MFMA,
 //                  accumulated over all of K inside the matrix core
-//   kPathF16       E4M3 widened to FP16 (exact), four FP16 MFMAs (16x16x32) per
-//                  block: exact products, FP32 accumulation; VALU promotion
-//   kPathF16Pow2   as kPathF16, promotion by the power-of-two part of each scale
 //   kPathMx        MXFP8: one E8M0 byte per 1x32 group on both operands (tcgen05
 //                  page, sections 6.1 and 6.3: SV = 32, E8M0 scales), packed
 //                  4 to a dword per (K block, row) in [K/128][rows] tables.
@@ -76,155 +77,7 @@ enum GemmMode : int { kDense = 0, kContiguous = 1, kMasked = 2 };
 //                  K (tcgen05 page, sections 6.3 and the operand-major notes),
 //                  64 bytes per row and K block; the instruction's A operand
 //                  in E2M1 format.
-enum GemmPath : int { kPathFp8 = 0, kPathFp8Pow2 = 1, kPathF16 = 2, kPathF16Pow2 = 3, kPathMx = 4,
-                      kPathMxW4 = 5 };
-
-// Operand pointers (passed to the kernel as separate __restrict__ arguments):
-//   xq (M, K) codes; masked: (E*max_m, K)
-//   sa [K/128][M]; masked: [K/128][E*max_m]
-//   wq (N, K); grouped: (E, N, K)
-//   sb [ceil(N/128)][K/128]; grouped: (E, N/128, K/128)
-//   y  (M, N) BF16 bits; masked: (E*max_m, N)
-//   m_indices (contiguous): expert of each row; masked_m (masked): valid rows
-struct GemmParams {
-    const uint8_t* xq;
-    const float* sa;
-    const uint8_t* wq;
-    const float* sb;
-    uint16_t* y;
-    uint8_t* yq;                // quantized output (QOUT): E4M3 codes (M, N)
-    float* sy;                  // ... and its 1x128 scales [N/128][M]
-    const int32_t* m_indices;
-    const int32_t* masked_m;
-    int64_t M;                  // rows of X (masked: E*max_m)
-    int64_t N;                  // output columns (per expert)
-    int64_t K;
-    int64_t max_m;              // masked only
-    int32_t E;
-    int64_t m_lo;               // dense/contiguous: tiles cover rows [m_lo, m_lo + m_tiles*BM)
-    int32_t m_tiles;            // dense/contiguous: ceil((rows to cover)/BM); masked: ceil(max_m/BM)
-    int32_t n_tiles;            // ceil(N/BN)
-    int32_t group_m;            // raster group height in tiles
-    float* part;                // decode split-K: FP32 partial sums [splits][M][N] (else null)
-};
-
-// s_waitcnt immediate for "at most n vector-memory operations outstanding"
-// (gfx9 encoding: vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14;
-// expcnt and lgkmcnt left at their maxima, i.e. not waited on).
-// Workgroup barrier without a memory fence.  Each wave has already waited on
-// its own vector-memory counter for the LDS data it needs; the barrier only
-// orders the waves.  (The fence of __syncthreads() would also wait for the
-// younger prefetch stages still in flight.)  The memory clobber keeps the
-// compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Raw buffer resource (V#) over [base, base + bytes), held in SGPRs: loads at
-// offsets >= bytes return zeros.  gfx9 dword3: 32-bit data format, raw
-// addressing (stride 0).
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t b = (uint64_t)base;
-    return i32x4{uniform((int)(uint32_t)b), uniform((int)(uint32_t)(b >> 32) & 0xFFFF),
-                 uniform((int)bytes), 0x00020000};
-}
-
-// A read-only, wave-uniform int32 (here a per-expert count) through the
-// scalar cache: an s_load waited on with lgkmcnt, so that it does not wait
-// for this wave's outstanding vector loads and stores.
-__device__ __forceinline__ int ld_uniform(const int32_t* p, int i) {
-    return ((const __attribute__((address_space(4))) int32_t*)(p))[i];
-}
-
-// Byte address of an LDS location (the value M0 takes for an LDS DMA).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(FP8K_LDS const void*)p;
-}
-
-// Wave-wide DMAs from a buffer into LDS.  N loads of 16 bytes per lane:
-// load q writes lane l's bytes at LDS m0 + 1024*q + 16*l and reads them from
-// buffer offset voff[q] + 1024*q + soff (the instruction offset moves both
-// addresses, so callers pass voff[q] already reduced by 1024*q).  M0 is
-// restored afterwards.  The loads count on this wave's vmcnt.  They are issued
-// from asm so that the compiler does not treat them as LDS stores that may
-// alias the stage being read (it would wait for every DMA in flight).
-template <int N>
-__device__ __forceinline__ void dma_lds16(uint32_t m0, const uint32_t (&voff)[N], i32x4 rsrc, int soff) {
-    static_assert(N >= 1 && N <= 4, "1..4 loads per group");
-    int saved;
-    if constexpr (N == 1)
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                     "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-                     "s_mov_b32 m0, %0"
-                     : "=&s"(saved) : "s"(m0), "v"(voff[0]), "s"(rsrc), "s"(soff));
-    else if constexpr (N == 2)
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                     "buffer_load_dwordx4 %2, %4, %5 offen lds\n\t"
-                     "buffer_load_dwordx4 %3, %4, %5 offen offset:1024 lds\n\t"
-                     "s_mov_b32 m0, %0"
-                     : "=&s"(saved) : "s"(m0), "v"(voff[0]), "v"(voff[1]), "s"(rsrc), "s"(soff));
-    else if constexpr (N == 3)
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                     "buffer_load_dwordx4 %2, %5, %6 offen lds\n\t"
-                     "buffer_load_dwordx4 %3, %5, %6 offen offset:1024 lds\n\t"
-                     "buffer_load_dwordx4 %4, %5, %6 offen offset:2048 lds\n\t"
-                     "s_mov_b32 m0, %0"
-                     : "=&s"(saved)
-                     : "s"(m0), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "s"(rsrc), "s"(soff));
-    else
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                     "buffer_load_dwordx4 %2, %6, %7 offen lds\n\t"
-                     "buffer_load_dwordx4 %3, %6, %7 offen offset:1024 lds\n\t"
-                     "buffer_load_dwordx4 %4, %6, %7 offen offset:2048 lds\n\t"
-                     "buffer_load_dwordx4 %5, %6, %7 offen offset:3072 lds\n\t"
-                     "s_mov_b32 m0, %0"
-                     : "=&s"(saved)
-                     : "s"(m0), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
-                       "s"(rsrc), "s"(soff));
-}
-// One wave-wide 16-byte-per-lane DMA: lane l's bytes land at
-// m0 + 1024*Q + 16*l and come from buffer offset voff + 1024*Q + soff.
-template <int Q>
-__device__ __forceinline__ void dma_lds16_one(uint32_t m0, uint32_t voff, i32x4 rsrc, int soff) {
-    int saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "buffer_load_dwordx4 %2, %3, %4 offen offset:%5 lds\n\t"
-                 "s_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff), "i"(1024 * Q));
-}
-// One wave-wide DMA of 4 bytes per lane: lane l's dword lands at m0 + 4*l.
-__device__ __forceinline__ void dma_lds4(uint32_t m0, uint32_t voff, i32x4 rsrc, int soff) {
-    int saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "buffer_load_dword %2, %3, %4 offen lds\n\t"
-                 "s_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff));
-}
-
-// LDS chunk swizzle: chunk c of row r lives in slot c ^ swz(r).  A fragment
-// read touches 16 consecutive rows (a 16-aligned run) at one logical chunk;
-// with swz(r) = (r mod 8) ^ ((r / 8) mod 2) those reads run at the full LDS
-// rate on gfx950 (measured; r mod 8 and (r / 2) mod 8 leave a residual
-// conflict).  Depending on r mod 16 only, it keeps every subtile of a wave at
-// a fixed offset from the first.
-__device__ __forceinline__ int lds_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// Logical tile -> (m tile, n tile) in grouped raster order: group_m m-tiles
-// are walked m-fastest for each n tile before the next group of m-tiles.
-__device__ __forceinline__ void raster(int t, int m_tiles, int n_tiles, int group_m, int& mt,
-                                       int& nt) {
-    const int per_group = group_m * n_tiles;
-    const int grp = t / per_group;
-    const int first = grp * group_m;
-    const int gm = min(m_tiles - first, group_m);
-    const int r = t - grp * per_group;
-    mt = first + r % gm;
-    nt = r / gm;
-}
+enum GemmPath : int { kPathFp8 = 0, kPathFp8Pow2 = 1, kPathMx = 2, kPathMxW4 = 3 };
 
 // A 16x128 E4M3 fragment of a lane from LDS: 16 bytes at base+a0 and 16 at
 // base+a1, as four 8-byte reads.
@@ -234,15 +87,6 @@ __device__ __forceinline__ i32x8 lds_frag(const uint8_t* base, uint32_t a0, uint
     const i32x2 r = *reinterpret_cast<const i32x2*>(base + a1);
     const i32x2 t = *reinterpret_cast<const i32x2*>(base + a1 + 8);
     return i32x8{p[0], p[1], q[0], q[1], r[0], r[1], t[0], t[1]};
-}
-
-// Calls f(integral_constant<int, 0>) ... f(integral_constant<int, S-1>) in order.
-template <int S, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (S > 0) {
-        static_for<S - 1>(f);
-        f(std::integral_constant<int, S - 1>{});
-    }
 }
 
 // QOUT: the epilogue emits the output quantized for the next GEMM -- E4M3
@@ -303,8 +147,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     // E8M0 byte of this lane's 32-group
     using ScaleT = std::conditional_t<kMx, int, float>;
     constexpr bool kSplitSb = kStreamW && TN <= 128 && !kScaledMfma;
-    constexpr bool kF16 = PATH == kPathF16 || PATH == kPathF16Pow2;
-    constexpr bool kPow2 = PATH == kPathFp8Pow2 || PATH == kPathF16Pow2;
+    constexpr bool kPow2 = PATH == kPathFp8Pow2;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 subtiles");
     static_assert(BM % 64 == 0 && NSA < NWAVES, "activation scales: 64 rows per wave, one wave left for sB");
     static_assert(BN / 128 + 2 <= 64, "one scale load covers the tile's weight blocks");
@@ -333,19 +176,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     const int64_t N = p.N;
     const int g = lane >> 4;             // K group of this lane: bytes [32g, 32g+32)
 
-    // Masked layout: tiles are counted per expert from the device-side counts.
-    int total_tiles;
-    if constexpr (MODE == kMasked) {
-        int acc = 0;
-        for (int e = 0; e < p.E; ++e) {
-            int v = ld_uniform(masked_m_, e);
-            v = v < 0 ? 0 : (v > p.max_m ? (int)p.max_m : v);
-            acc += (v + BM - 1) / BM;
-        }
-        total_tiles = acc * p.n_tiles;
-    } else {
-        total_tiles = p.m_tiles * p.n_tiles;
-    }
+    const int total_tiles = count_tiles<MODE, BM>(p, masked_m_);
 
     // ---- per-lane constants, shared by every tile ----
     // DMA: a wave load fills 1 KB = 8 rows R0..R0+7 of 8-row group grp = R0/8;
@@ -453,46 +284,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         if (t >= total_tiles) continue;
 
         // ---------------- tile decode ----------------
-        int mt, nt;
-        int64_t row0;       // first X row of the tile
-        int64_t row_end;    // rows [row0, row_end) may be read and written
-        int expert = 0;
-        if constexpr (MODE == kMasked) {
-            // An expert with nmt m-tiles owns logical tiles
-            // [base*n_tiles, (base+nmt)*n_tiles), walked m-fastest: the m-tiles
-            // that read the same W columns are neighbours, so they run together
-            // on one XCD and the second read of W hits its L2.
-            const int mt_t = t / p.n_tiles;
-            int base = 0, e = 0, valid = 0, nmt = 1;
-            for (; e < p.E; ++e) {
-                valid = ld_uniform(masked_m_, e);
-                valid = valid < 0 ? 0 : (valid > p.max_m ? (int)p.max_m : valid);
-                nmt = (valid + BM - 1) / BM;
-                if (mt_t < base + nmt) break;
-                base += nmt;
-            }
-            expert = e;
-            const int local = t - base * p.n_tiles;
-            nt = local / nmt;
-            mt = local - nt * nmt;
-            row0 = (int64_t)e * p.max_m + (int64_t)mt * BM;
-            row_end = (int64_t)e * p.max_m + valid;
-        } else {
-            raster(t, p.m_tiles, p.n_tiles, p.group_m, mt, nt);
-            row0 = p.m_lo + (int64_t)mt * BM;
-            row_end = p.M;
-            if constexpr (MODE == kContiguous) {
-                // expert of this aligned block: its first row naming one in [0, E)
-                int e = -1;
-                for (int r = 0; r < BM && row0 + r < p.M; ++r) {
-                    const int v = m_indices_[row0 + r];
-                    if (v >= 0 && v < p.E) { e = v; break; }
-                }
-                if (e < 0) continue;   // only padding rows: nothing to compute
-                expert = e;
-            }
-        }
-        const int64_t n0 = (int64_t)nt * BN;
+        TileCoord tc;
+        if (!decode_tile<MODE, BM, BN>(t, p, m_indices_, masked_m_, tc)) continue;
+        const int64_t row0 = tc.row0, row_end = tc.row_end, n0 = tc.n0;
+        const int expert = tc.expert;
         const uint8_t* wq = wq_;
         const float* sb = sb_;
         if constexpr (MODE != kDense) {
@@ -747,10 +542,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         // promotion of the previous row (partials prev, row rp of the block
         // whose resident scales are rsv)
         auto promote = [&](int rp, const float (&rsv)[C]) {
-            const float stv = kPow2 ? pow2_part(st_prev) : st_prev;
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                const float sc = stv * (kPow2 ? pow2_part(rsv[c]) : rsv[c]);
+                const float sc = st_prev * rsv[c];
 #pragma unroll
                 for (int r2 = 0; r2 < 4; ++r2) accr(rp, c)[r2] = fmaf(sc, prev[c][r2], accr(rp, c)[r2]);
             }
@@ -767,14 +561,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             const StageLoads L2 = stage_loads(kb + STAGES, std::integral_constant<int, BUF>{});
             ScaleT rs_next[C];
             float sb2_next[2];
-            // resident fragments widened to FP16 once per block on the precise path
-            f16x8 resh[kF16 ? C : 1][4];
-            if constexpr (kF16) {
-#pragma unroll
-                for (int c = 0; c < C; ++c)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) resh[c][q] = e4m3x8_to_f16(res[c][2 * q], res[c][2 * q + 1]);
-            }
             // E8M0 exponents of the resident scales (scaled-MFMA path)
             int rse[C];
             if constexpr (kScaledMfma) {
@@ -834,37 +620,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                     }
                 } else {
                     f32x4 cur[C];
-                    if constexpr (kF16) {
-                        f16x8 fh[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) fh[q] = e4m3x8_to_f16(fc[2 * q], fc[2 * q + 1]);
-#pragma unroll
-                        for (int c = 0; c < C; ++c) {
-                            cur[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                if constexpr (kStreamW)
-                                    cur[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fh[q], resh[c][q], cur[c], 0, 0, 0);
-                                else
-                                    cur[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(resh[c][q], fh[q], cur[c], 0, 0, 0);
-                            }
-                        }
-                        if constexpr (r == R - 1) {
-#pragma unroll
-                            for (int c = 0; c < C; ++c) res[c] = read_res(NBUF, c);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < C; ++c) {
-                            if constexpr (kStreamW)
-                                cur[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                    fc, res[c], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                            else
-                                cur[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                    res[c], fc, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                            if constexpr (r == R - 1) res[c] = read_res(NBUF, c);
-                        }
+                    for (int c = 0; c < C; ++c) {
+                        if constexpr (kStreamW)
+                            cur[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                fc, res[c], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                        else
+                            cur[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                res[c], fc, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                        if constexpr (r == R - 1) res[c] = read_res(NBUF, c);
                     }
                     // the previous row: row r-1 of this block, or the last
                     // row of the previous block (with that block's scales)
@@ -876,8 +640,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                             for (int h = 0; h < 2; ++h)
 #pragma unroll
                                 for (int c = 0; c < C; ++c)
-                                    pr[h][c] = (kPow2 ? pow2_part(rs_cur[c]) : rs_cur[c]) *
-                                               (kPow2 ? pow2_part(sb2_cur[h]) : sb2_cur[h]);
+                                    pr[h][c] = rs_cur[c] * sb2_cur[h];
                         }
                         if constexpr (r == 0) promote_p(R - 1, plast);
                         else promote_p(r - 1, pr[r - 1 < JB ? 0 : 1]);
@@ -888,16 +651,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 #pragma unroll
                     for (int c = 0; c < C; ++c) prev[c] = cur[c];
                     st_prev = st_c;
-                    if constexpr (!kF16) {
-                        // each MFMA of this row preceded by the promotion FMAs of
-                        // the subtile whose partials its result replaces (and the
-                        // scale products)
-                        static_for<C>([&](auto qc) {
-                            constexpr int n = kSplitSb ? 4 : (decltype(qc)::value == 0 || kStreamW ? 5 : 4);
-                            __builtin_amdgcn_sched_group_barrier(0x002, n, 0);
-                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        });
-                    }
+                    // each MFMA of this row preceded by the promotion FMAs of
+                    // the subtile whose partials its result replaces (and the
+                    // scale products)
+                    static_for<C>([&](auto qc) {
+                        constexpr int n = kSplitSb ? 4 : (decltype(qc)::value == 0 || kStreamW ? 5 : 4);
+                        __builtin_amdgcn_sched_group_barrier(0x002, n, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    });
                 }
             });
             __builtin_amdgcn_sched_barrier(0);

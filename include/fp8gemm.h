@@ -39,6 +39,7 @@
  */
 #ifndef FP8GEMM_H
 #define FP8GEMM_H
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -62,19 +63,28 @@ typedef enum {
  * the matrix instruction. */
 #define FP8_FLAG_UE8M0 1u
 
-/* GEMMs only: form every 128-K block partial from products that are exact and
- * sums accumulated in FP32, by widening the E4M3 operands to FP16 (exact) and
- * using FP16 matrix instructions, at half the FP8 matrix rate.  Without this
- * flag the partials come from the FP8 matrix instruction, which on gfx950
- * truncates, within each group of 8 consecutive products, every product to a
- * multiple of 2^(E-13), 2^E being the group's largest product magnitude
- * (measured: the analog of the limited FP8 accumulation precision that the
- * DeepGEMM page, section "细粒度缩放在 GEMM 层面引爆的两个问题", reports for
- * H800 tensor cores).  Either way the partials are promoted into FP32 every
- * 128-K block.  With FP8_FLAG_UE8M0 and without this flag, the block scaling
- * runs inside the scaled FP8 matrix instruction and the K sum stays in its
- * FP32 accumulator. */
-#define FP8_FLAG_PRECISE 2u
+/* GEMMs only: form each 128-K block partial with the FP8 matrix instruction
+ * (twice the FP16 matrix rate) instead of exactly.
+ *
+ * Default (flag clear): the E4M3 operands are widened to FP16, which is exact,
+ * and multiplied by FP16 matrix instructions: every product is exact and
+ * every sum FP32-accurate, so Y is the exact block-scaled sum up to FP32
+ * accumulation and BF16 rounding, i.e. within |y - ref| <= 8e-3*|ref| +
+ * 1e-3*rms(ref) of the exact value ref barring cancellation below FP32
+ * precision ([DG] "细粒度缩放在 GEMM 层面引爆的两个问题": the promotion exists
+ * so that the sum is accumulated at full precision).
+ *
+ * FP8_FLAG_FAST_ACCUM: the FP8 instruction of gfx950 truncates, within each
+ * group of 8 consecutive K, every product toward zero to a multiple of
+ * 2^(E-13), 2^E being the group's largest product magnitude (measured; the
+ * analog of the limited FP8 accumulation precision the DeepGEMM page reports
+ * for H800 tensor cores).  Per output element the error therefore stays below
+ *   2^-10 * sum over 8-groups g of sa*sb * max_{k in g} |x[m][k]| * max_{k in g} |w[n][k]|
+ * (decoded E4M3 values, the scales of g's block) plus FP32/BF16 rounding,
+ * which can exceed the tolerance above where the sum cancels.  With
+ * FP8_FLAG_UE8M0 the block scaling then runs inside the scaled FP8
+ * instruction and the K sum stays in its FP32 accumulator. */
+#define FP8_FLAG_FAST_ACCUM 2u
 
 /*
  * Activation quantizer, 1x128 groups ([DG] "离群值如何摧毁 per-tensor 量化":
@@ -107,20 +117,34 @@ fp8_status fp8_quant_128x128(const float* w, int64_t N, int64_t K, uint8_t* wq,
  *   Y[m][n] = sum_kb sa[kb][m] * sb[n/128][kb] * sum_{k in kb} xq[m][k]*wq[n][k]
  *   xq u8 (M,K), sa fp32 [K/128][M], wq u8 (N,K), sb fp32 [ceil(N/128)][K/128],
  *   y  bf16 bits (M,N).
- * Memory: with M <= 32 and N below 96 times the device's compute units, K is
- * split over several workgroups, whose FP32 partial sums live in a workspace
- * the library keeps per (device, stream): 8*32*96*CUs*4 bytes (about 25 MB
- * on MI355X), allocated by the first such call on that stream and held until
- * the process ends.  Calls on one stream share it in stream order; a graph
- * replayed on another stream while that stream runs such a call would race
- * on it.  No allocation happens while the stream is being captured, nor once
- * the process holds 16 such workspaces (one per stream: about 400 MB in
- * all); without a workspace the GEMM runs unsplit (same result up to FP32
- * summation order).  Every other case uses the caller's buffers only.
+ * flags: FP8_FLAG_UE8M0, FP8_FLAG_FAST_ACCUM.  Uses the caller's buffers only
+ * (equivalent to fp8_gemm_nt_ws with no workspace).
  */
 fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq,
                        const float* sb, uint16_t* y, int64_t M, int64_t N,
                        int64_t K, uint32_t flags, void* stream);
+
+/*
+ * fp8_gemm_nt with a caller-owned device workspace.  With FP8_FLAG_FAST_ACCUM,
+ * M <= 32 and fewer 96-column tiles than compute units, the decode kernel
+ * splits K over up to 8 workgroups per tile when `workspace` holds their FP32
+ * partial sums, and a second kernel adds them in split order (the same result
+ * for the same split).  fp8_gemm_workspace_size() gives the bytes that enable
+ * the split for a shape on the current device (0: no split).  With a smaller
+ * or no workspace the GEMM runs unsplit.  The workspace is only read and
+ * written by this call's kernels, in stream order; calls that overlap on one
+ * workspace race.  workspace_bytes > 0 needs a non-NULL, 16-byte aligned
+ * workspace.
+ */
+fp8_status fp8_gemm_nt_ws(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                          const float* sb, uint16_t* y, int64_t M, int64_t N,
+                          int64_t K, uint32_t flags, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes with which fp8_gemm_nt_ws splits K for this shape and these
+ * flags on the current device (0 when it does not split, or on bad
+ * arguments). */
+size_t fp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, uint32_t flags);
 
 /*
  * Dense NT GEMM whose output is quantized for the next GEMM in the epilogue
@@ -202,7 +226,8 @@ fp8_status fp8_quant_mx(const float* x, int64_t R, int64_t K, uint8_t* q,
  *   4*kb + t), y bf16 bits (M,N); K % 128 == 0.  Every lane of the scaled
  *   matrix instruction holds one 32-group of its row and takes that group's
  *   byte as its scale, so the whole K sum stays in the instruction's FP32
- *   accumulator.  flags must be 0.
+ *   accumulator.  Accuracy: that of the FP8 instruction (the bound stated at
+ *   FP8_FLAG_FAST_ACCUM, with each 32-group's scales).  flags must be 0.
  */
 fp8_status fp8_gemm_nt_mx(const uint8_t* xq, const uint32_t* ea,
                           const uint8_t* wq, const uint32_t* eb, uint16_t* y,
@@ -232,12 +257,45 @@ fp8_status fp8_quant_mxfp4(const float* x, int64_t R, int64_t K, uint8_t* q,
  *   xq u8 (M,K), ea u32 [K/128][M] (fp8_quant_mx), wq u8 (N, K/2),
  *   eb u32 [K/128][N] (fp8_quant_mxfp4), y bf16 bits (M,N); K % 128 == 0.
  *   The scaled matrix instruction takes W as an E2M1 operand and each lane's
- *   group scale; the K sum stays in its FP32 accumulator.  flags must be 0.
+ *   group scale; the K sum stays in its FP32 accumulator.  Accuracy: that of
+ *   the FP8 instruction, as for fp8_gemm_nt_mx.  flags must be 0.
  */
 fp8_status fp8_gemm_nt_mx_w4(const uint8_t* xq, const uint32_t* ea,
                              const uint8_t* wq, const uint32_t* eb, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, uint32_t flags,
                              void* stream);
+
+/*
+ * The kernel instances a GEMM call would launch, computed on the host from
+ * the shape and a compute-unit count (no device needed): the persistent tile
+ * schedule of [DG] "统一块调度器与 rasterization" and the tile choice of
+ * [DG] "非对齐块大小" (pick the tile whose count fills the machine's waves
+ * best).
+ *   layout   0 dense (fp8_gemm_nt), 1 contiguous, 2 masked (max_m as M)
+ *   flags    FP8_FLAG_* of the call, plus FP8_PLAN_MX (fp8_gemm_nt_mx /
+ *            fp8_gemm_nt_mx_w4) or FP8_PLAN_QOUT (fp8_gemm_nt_qout), dense only
+ *   workspace_bytes  what an fp8_gemm_nt_ws call would pass
+ * Masked plans count every expert's max_m rows (the kernel counts the valid
+ * ones on the device).
+ */
+#define FP8_PLAN_MX 0x100u
+#define FP8_PLAN_QOUT 0x200u
+typedef struct {
+    int32_t exact;          /* 1: exact partials (FP16 instruction); 0: FP8 instruction */
+    int32_t kernel;         /* 0: tile kernel; 1: decode kernel (M <= 32); 2: X-resident decode kernel */
+    int32_t tile_m, tile_n; /* workgroup tile of the main launch (decode kernels: 96 columns) */
+    int32_t waves;          /* waves per workgroup */
+    int32_t grid;           /* workgroups of the main launch */
+    int64_t tiles;          /* tiles of the main launch (decode kernels: workgroups) */
+    int64_t main_rows;      /* rows [0, main_rows) in the main launch (contiguous); else M */
+    int32_t tail_tile_m, tail_tile_n; /* contiguous: tile of a second launch over [main_rows, M), or 0 */
+    int64_t tail_tiles;
+    int32_t k_splits;       /* decode kernel: workgroups along K per tile */
+    size_t workspace_bytes; /* workspace the split uses */
+} fp8_gemm_plan_t;
+fp8_status fp8_gemm_plan(int32_t layout, int64_t M, int64_t N, int64_t K,
+                         uint32_t flags, int32_t compute_units,
+                         size_t workspace_bytes, fp8_gemm_plan_t* plan);
 
 /* M alignment every expert segment of the contiguous layout must have
  * ([DG] "分组 GEMM 的两种布局": the alignment query).  Returns 128. */

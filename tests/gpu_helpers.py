@@ -116,8 +116,13 @@ def fp8_mfma_error_bound(xq, sa, wq, sb, ref, pow2: bool = False) -> np.ndarray:
     return 2.0 ** -8 * np.abs(ref) + 1.01 * trunc + 2.0 ** -16 * absprod
 
 
-def assert_close_or_bounded(y_bits, ref, bound, what: str = "") -> dict:
-    """Every element within the benchmark spec's tolerance or within `bound`."""
+def assert_close_or_bounded(y_bits, ref, bound, what: str = "", max_beyond_frac: float = 1e-4) -> dict:
+    """For the opt-in FP8-instruction path (FP8_FLAG_FAST_ACCUM, MX): every
+    element within the benchmark spec's tolerance or within `bound`, the bound of
+    the measured FP8-MFMA truncation model; and the elements outside the
+    tolerance (reported as beyond_strict) at most max_beyond_frac of them,
+    rounded up, so that a regression that moves many elements past the
+    tolerance fails even while they stay inside the model's bound."""
     y = bf16_to_f64(np.asarray(y_bits))
     ref = np.asarray(ref, dtype=np.float64)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
@@ -130,4 +135,8 @@ def assert_close_or_bounded(y_bits, ref, bound, what: str = "") -> dict:
         raise AssertionError(f"{what}: {int(bad.sum())} elements beyond both the tolerance and the "
                              f"FP8-MFMA model bound; first "
                              f"{[(tuple(i), float(y[tuple(i)]), float(ref[tuple(i)]), float(bound[tuple(i)])) for i in idx]}")
-    return {"n": int(ref.size), "beyond_strict": int(np.sum(err > strict))}
+    beyond = int(np.sum(err > strict))
+    ceiling = int(np.ceil(max_beyond_frac * ref.size))
+    assert beyond <= ceiling, (f"{what}: {beyond} of {ref.size} elements outside the tolerance "
+                               f"(ceiling {ceiling})")
+    return {"n": int(ref.size), "beyond_strict": beyond, "ceiling": ceiling}

@@ -11,9 +11,10 @@ FP32.  Consequences tested here:
   * promoting every 128-K block by VALU FMA and accumulating the whole K in
     the scaled instruction's accumulator give bit-identical results on
     power-of-two scales: the longer interval costs no precision;
-  * exact partials (FP8_FLAG_PRECISE) give correctly rounded BF16 for almost
-    every element, the FP8 instruction for most;
-  * a crafted 8-group shows the truncation itself."""
+  * exact partials (the default path) give correctly rounded BF16 for almost
+    every element, the FP8 instruction (FP8_FLAG_FAST_ACCUM) for most;
+  * a crafted 8-group shows the truncation itself, and that the default path
+    does not truncate."""
 import numpy as np
 import pytest
 import torch
@@ -42,13 +43,15 @@ def test_promotion_interval_128_equals_whole_k_on_pow2_scales(M, N, K, outliers)
     wq, sb = oracle.quant_128x128(wl.w, oracle.FLAG_UE8M0)
     a = [dev(t) for t in (xq, sa, wq, sb)]
     say(f"promotion interval M={M} N={N} K={K}")
-    every_block = bf16_bits(fp8.gemm_nt(*a, ue8m0=False))   # zero-C partial + FP32 FMA per 128 K
-    whole_k = bf16_bits(fp8.gemm_nt(*a, ue8m0=True))        # scaled instruction, K in its accumulator
-    precise = bf16_bits(fp8.gemm_nt(*a, precise=True))      # exact partials, FP32 promotion
+    every_block = bf16_bits(fp8.gemm_nt(*a, fast_accum=True))              # zero-C FP8 partial + FP32 FMA per 128 K
+    whole_k = bf16_bits(fp8.gemm_nt(*a, ue8m0=True, fast_accum=True))      # scaled instruction, K in its accumulator
+    precise = bf16_bits(fp8.gemm_nt(*a))                                   # default: exact partials
+    precise_pow2 = bf16_bits(fp8.gemm_nt(*a, ue8m0=True))                  # ... with exponent-shift promotion
     assert np.array_equal(every_block, whole_k)
     ref = oracle.gemm_nt(xq, sa, wq, sb, oracle.FLAG_UE8M0)
     rn = bf16_rne(ref)
     frac_precise = np.mean(bf16_to_f64(precise) == rn)
+    assert np.mean(bf16_to_f64(precise_pow2) == rn) >= 0.999
     frac_fp8 = np.mean(bf16_to_f64(every_block) == rn)
     say(f"correctly rounded: precise {frac_precise:.4f}, fp8 {frac_fp8:.4f}")
     assert frac_precise >= 0.999          # measured 0.9998-0.9999
@@ -60,7 +63,8 @@ def test_fp8_instruction_truncates_small_products_in_a_group():
     the next group holds -256.  Exact: 7 * 2^-6 = 0.109375.  In the measured
     model each product of a group is truncated toward zero to a multiple of
     2^(E-13), 2^E <= 256 being the group's largest: 2^-5 > 2^-6, so the seven
-    vanish and the FP8 paths return 0.  Exact partials keep them."""
+    vanish and the FP8-instruction paths (FP8_FLAG_FAST_ACCUM) return 0.  The
+    default path's exact partials keep them, with FP32 or power-of-two scales."""
     K = 128
     xq = np.zeros((1, K), np.uint8)
     wq = np.zeros((16, K), np.uint8)
@@ -72,6 +76,7 @@ def test_fp8_instruction_truncates_small_products_in_a_group():
     assert oracle.gemm_nt(xq, sa, wq, sb)[0, 0] == 0.109375
     a = [dev(t) for t in (xq, sa, wq, sb)]
     y = {k: bf16_to_f64(bf16_bits(fp8.gemm_nt(*a, **kw)))[0, 0]
-         for k, kw in (("fp8", {}), ("ue8m0", {"ue8m0": True}), ("precise", {"precise": True}))}
-    assert y["precise"] == 0.109375
-    assert y["fp8"] == 0.0 and y["ue8m0"] == 0.0
+         for k, kw in (("fp8", {"fast_accum": True}), ("fp8_ue8m0", {"ue8m0": True, "fast_accum": True}),
+                       ("exact", {}), ("exact_ue8m0", {"ue8m0": True}))}
+    assert y["exact"] == 0.109375 and y["exact_ue8m0"] == 0.109375
+    assert y["fp8"] == 0.0 and y["fp8_ue8m0"] == 0.0

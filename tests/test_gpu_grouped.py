@@ -1,8 +1,9 @@
 """GPU grouped (MoE) GEMMs against the oracle.  Row handling is bit-exact:
 every row the oracle leaves unwritten must keep its sentinel bits.  Values
-follow the same two-path rule as the dense tests (PRECISE: the tolerance
-everywhere; FP8 matrix instruction: the tolerance on the headline workloads,
-elsewhere the tolerance or the measured truncation-model bound)."""
+follow the same two-path rule as the dense tests (default, exact partials:
+the tolerance everywhere; FP8_FLAG_FAST_ACCUM: the tolerance on the headline
+workloads, elsewhere the tolerance or the measured truncation-model bound,
+with a ceiling on the elements outside the tolerance)."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +15,7 @@ from gpu_helpers import (SENTINEL, assert_close, assert_close_or_bounded, bf16_b
                          fp8_mfma_error_bound, say, sentinel_like)
 
 pytestmark = pytest.mark.gpu
-PATHS = [pytest.param(False, id="fp8"), pytest.param(True, id="precise")]
+PATHS = [pytest.param(False, id="exact"), pytest.param(True, id="fast")]
 
 
 def quant(wl):
@@ -24,27 +25,27 @@ def quant(wl):
     return xq, sa, wq, sb, flags
 
 
-def run_contiguous(xq, sa, wq, sb, idx, E, flags, precise):
+def run_contiguous(xq, sa, wq, sb, idx, E, flags, fast):
     M, K = xq.shape
     N = wq.shape[0] // E
-    say(f"contiguous M={M} N={N} K={K} E={E} flags={flags} precise={precise}")
+    say(f"contiguous M={M} N={N} K={K} E={E} flags={flags} fast_accum={fast}")
     y = sentinel_like((M, N))
     fp8.grouped_gemm_contiguous(dev(xq), dev(sa), dev(wq.reshape(E, N, K)),
                                 dev(sb.reshape(E, N // 128, K // 128)),
-                                dev(idx.astype(np.int32)), ue8m0=bool(flags), precise=precise,
+                                dev(idx.astype(np.int32)), ue8m0=bool(flags), fast_accum=fast,
                                 out=y)
     return bf16_bits(y)
 
 
-def run_masked(xq, sa, wq, sb, mm, E, max_m, flags, precise):
+def run_masked(xq, sa, wq, sb, mm, E, max_m, flags, fast):
     MT, K = xq.shape
     N = wq.shape[0] // E
     say(f"masked E={E} max_m={max_m} N={N} K={K} counts={list(mm)} flags={flags} "
-        f"precise={precise}")
+        f"fast_accum={fast}")
     y = sentinel_like((E, max_m, N))
     fp8.grouped_gemm_masked(dev(xq.reshape(E, max_m, K)), dev(sa), dev(wq.reshape(E, N, K)),
                             dev(sb.reshape(E, N // 128, K // 128)), dev(mm.astype(np.int32)),
-                            ue8m0=bool(flags), precise=precise, out=y)
+                            ue8m0=bool(flags), fast_accum=fast, out=y)
     return bf16_bits(y).reshape(E * max_m, N)
 
 
@@ -72,22 +73,22 @@ def check_rows(y, ref, written, what, bound=None):
         say(f"stats {assert_close_or_bounded(y[written], ref[written], bound[written], what)}")
 
 
-@pytest.mark.parametrize("precise", PATHS)
+@pytest.mark.parametrize("fast", PATHS)
 @pytest.mark.parametrize("counts", [[0, 130, 1, 169], [500, 0, 0, 0], [1, 1, 1, 1],
                                     [128, 256, 0, 7]])
-def test_contiguous_routing(counts, precise):
+def test_contiguous_routing(counts, fast):
     wl = workloads.contiguous(E=4, tokens=sum(counts), N=256, K=384, seed=sum(counts),
                               counts=np.array(counts))
     xq, sa, wq, sb, flags = quant(wl)
     ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E)
-    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, flags, precise)
-    bound = None if precise else grouped_bound(xq, sa, wq, sb, ref,
+    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, flags, fast)
+    bound = None if not fast else grouped_bound(xq, sa, wq, sb, ref,
                                                np.where(written, wl.m_indices, -1), wl.E, False)
     check_rows(y, ref, written, f"contiguous {counts}", bound)
 
 
-@pytest.mark.parametrize("precise", PATHS)
-def test_contiguous_tail_blocks_in_a_second_launch(precise):
+@pytest.mark.parametrize("fast", PATHS)
+def test_contiguous_tail_blocks_in_a_second_launch(fast):
     """18 row blocks x 16 column tiles of 128x256 = 288 tiles: on 256 CUs one
     full round, then the last 2 row blocks (part of expert 3 and its padding
     rows) run as a second launch of 128x64 tiles."""
@@ -97,14 +98,14 @@ def test_contiguous_tail_blocks_in_a_second_launch(precise):
     assert wl.M == 18 * 128
     xq, sa, wq, sb, flags = quant(wl)
     ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E)
-    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, flags, precise)
-    bound = None if precise else grouped_bound(xq, sa, wq, sb, ref,
+    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, flags, fast)
+    bound = None if not fast else grouped_bound(xq, sa, wq, sb, ref,
                                                np.where(written, wl.m_indices, -1), wl.E, False)
     check_rows(y, ref, written, "contiguous tail launch", bound)
 
 
-@pytest.mark.parametrize("precise", PATHS)
-def test_contiguous_dirichlet_and_bad_indices(precise):
+@pytest.mark.parametrize("fast", PATHS)
+def test_contiguous_dirichlet_and_bad_indices(fast):
     wl = workloads.contiguous(E=8, tokens=1500, N=384, K=256, seed=41)
     idx = wl.m_indices.copy()
     # contract violations, defined as "skip": out-of-range experts and a
@@ -115,44 +116,45 @@ def test_contiguous_dirichlet_and_bad_indices(precise):
         idx[first5[1:3]] = 6
     xq, sa, wq, sb, flags = quant(wl)
     ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, idx, wl.E)
-    y = run_contiguous(xq, sa, wq, sb, idx, wl.E, flags, precise)
-    bound = None if precise else grouped_bound(xq, sa, wq, sb, ref,
+    y = run_contiguous(xq, sa, wq, sb, idx, wl.E, flags, fast)
+    bound = None if not fast else grouped_bound(xq, sa, wq, sb, ref,
                                                np.where(written, idx, -1), wl.E, False)
     check_rows(y, ref, written, "contiguous dirichlet", bound)
 
 
-@pytest.mark.parametrize("precise", PATHS)
-def test_contiguous_ue8m0(precise):
+@pytest.mark.parametrize("fast", PATHS)
+def test_contiguous_ue8m0(fast):
     wl = workloads.contiguous(E=3, tokens=400, N=256, K=256, seed=42)
     xq, sa = oracle.quant_1x128(wl.x, oracle.FLAG_UE8M0)
     wq, sb = oracle.quant_128x128(wl.w, oracle.FLAG_UE8M0)
     ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E,
                                              oracle.FLAG_UE8M0)
-    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, oracle.FLAG_UE8M0, precise)
-    bound = None if precise else grouped_bound(xq, sa, wq, sb, ref,
+    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, oracle.FLAG_UE8M0, fast)
+    bound = None if not fast else grouped_bound(xq, sa, wq, sb, ref,
                                                np.where(written, wl.m_indices, -1), wl.E, True)
     check_rows(y, ref, written, "contiguous ue8m0", bound)
 
 
-@pytest.mark.parametrize("precise", PATHS)
+@pytest.mark.parametrize("fast", PATHS)
 @pytest.mark.parametrize("ue8m0", [True, False])
 @pytest.mark.parametrize("max_m", [200, 256, 300])
-def test_masked_counts(ue8m0, max_m, precise):
+def test_masked_counts(ue8m0, max_m, fast):
     mm = np.array([0, 1, 127, 128, 255, 256, -3, 999], np.int32)
     E = len(mm)
     wl = workloads.masked(E, max_m, 256, 384, seed=max_m, ue8m0=ue8m0, masked_m=mm)
     xq, sa, wq, sb, flags = quant(wl)
     ref, written = oracle.grouped_masked(xq, sa, wq, sb, mm, E, max_m, flags)
-    y = run_masked(xq, sa, wq, sb, mm, E, max_m, flags, precise)
+    y = run_masked(xq, sa, wq, sb, mm, E, max_m, flags, fast)
     bound = None
-    if not precise:
+    if fast:
         row_expert = np.where(written, np.arange(E * max_m) // max_m, -1)
         bound = grouped_bound(xq, sa, wq, sb, ref, row_expert, E, ue8m0)
     check_rows(y, ref, written, f"masked max_m={max_m}", bound)
 
 
+@pytest.mark.parametrize("fast", PATHS)
 @pytest.mark.parametrize("ue8m0", [True, False])
-def test_masked_tile_order(ue8m0):
+def test_masked_tile_order(ue8m0, fast):
     """Experts with one, two and three 128-row m-tiles (and none) times three
     256-column n-tiles, the last one ragged: the tile order walks each
     expert's m-tiles fastest within each n-tile; every valid row of every
@@ -162,36 +164,37 @@ def test_masked_tile_order(ue8m0):
     wl = workloads.masked(E, max_m, N, K, seed=11, ue8m0=ue8m0, masked_m=mm)
     xq, sa, wq, sb, flags = quant(wl)
     ref, written = oracle.grouped_masked(xq, sa, wq, sb, mm, E, max_m, flags)
-    y = run_masked(xq, sa, wq, sb, mm, E, max_m, flags, False)
+    y = run_masked(xq, sa, wq, sb, mm, E, max_m, flags, fast)
     row_expert = np.where(written, np.arange(E * max_m) // max_m, -1)
-    bound = grouped_bound(xq, sa, wq, sb, ref, row_expert, E, ue8m0)
+    bound = grouped_bound(xq, sa, wq, sb, ref, row_expert, E, ue8m0) if fast else None
     check_rows(y, ref, written, "masked tile order", bound)
 
 
-def test_masked_rows_past_count_never_read():
+@pytest.mark.parametrize("fast", PATHS)
+def test_masked_rows_past_count_never_read(fast):
     """Rows past the count may hold NaN codes and NaN scales: the output must
     not change."""
     E, max_m, N, K = 3, 256, 256, 256
     mm = np.array([5, 0, 200], np.int32)
     wl = workloads.masked(E, max_m, N, K, seed=3, masked_m=mm)
     xq, sa, wq, sb, flags = quant(wl)
-    y0 = run_masked(xq, sa, wq, sb, mm, E, max_m, flags, False)
+    y0 = run_masked(xq, sa, wq, sb, mm, E, max_m, flags, fast)
     xq2 = xq.copy()
     sa2 = sa.copy()
     for e in range(E):
         xq2[e * max_m + mm[e]:(e + 1) * max_m] = 0x7F      # NaN codes
         sa2[:, e * max_m + mm[e]:(e + 1) * max_m] = np.nan
-    y1 = run_masked(xq2, sa2, wq, sb, mm, E, max_m, flags, False)
+    y1 = run_masked(xq2, sa2, wq, sb, mm, E, max_m, flags, fast)
     assert np.array_equal(y0, y1)
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("precise", PATHS)
-def test_full_size_contiguous_config4_every_element(precise):
+@pytest.mark.parametrize("fast", PATHS)
+def test_full_size_contiguous_config4_every_element(fast):
     wl = workloads.config(4)
     say("config 4: oracle quantization")
     xq, sa, wq, sb, flags = quant(wl)
-    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, flags, precise)
+    y = run_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E, flags, fast)
     say("config 4: oracle grouped GEMM")
     ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, wl.m_indices, wl.E)
     assert np.array_equal(written, wl.m_indices >= 0)
@@ -199,13 +202,13 @@ def test_full_size_contiguous_config4_every_element(precise):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("precise", PATHS)
-def test_full_size_masked_config5_every_element(precise):
+@pytest.mark.parametrize("fast", PATHS)
+def test_full_size_masked_config5_every_element(fast):
     wl = workloads.config(5)
     say("config 5: oracle quantization")
     xq, sa, wq, sb, flags = quant(wl)
     E, max_m = wl.E, wl.max_m
-    y = run_masked(xq, sa, wq, sb, wl.masked_m, E, max_m, flags, precise)
+    y = run_masked(xq, sa, wq, sb, wl.masked_m, E, max_m, flags, fast)
     say("config 5: oracle grouped GEMM")
     ref, written = oracle.grouped_masked(xq, sa, wq, sb, wl.masked_m, E, max_m, flags)
     check_rows(y, ref, written, "config 5")

@@ -3,11 +3,12 @@
 
 Where the FP32 accumulator is exact (integer-valued products, power-of-two
 scales, small sums) the codes and scales must be bit-identical to the 1x128
-oracle quantizer applied to the exact product.  Elsewhere the accumulator may
-differ from the exact product by the FP8-MFMA model bound B, so each group's
-scale must lie between fl32((A-B)/448) and fl32((A+B)/448), A the exact group
-maximum, and each decoded value within half an E4M3 step of the exact one
-plus B."""
+oracle quantizer applied to the exact product, on both accumulation paths.
+Elsewhere the accumulator may differ from the exact product by a bound B --
+FP32 accumulation on the default path (exact partials), the FP8-MFMA model
+bound with FP8_FLAG_FAST_ACCUM -- so each group's scale must lie between
+fl32((A-B)/448) and fl32((A+B)/448), A the exact group maximum, and each
+decoded value within half an E4M3 step of the exact one plus B."""
 import numpy as np
 import pytest
 import torch
@@ -20,6 +21,20 @@ from gpu_helpers import bf16_bits, bf16_to_f64, dev, fp8_mfma_error_bound, host,
 pytestmark = pytest.mark.gpu
 
 DEC = oracle.e4m3_decode(np.arange(256))
+PATHS = [pytest.param(False, id="exact"), pytest.param(True, id="fast")]
+
+
+def accumulation_bound(xq, sa, wq, sb, fast, pow2):
+    """Per-element bound on |accumulator - exact product|: the FP8-MFMA model
+    (fast), or 2^-18 of the sum of |scaled products| (exact partials summed in
+    FP32: at most a few dozen roundings of 2^-24 each along K)."""
+    if fast:
+        return fp8_mfma_error_bound(xq, sa, wq, sb, np.zeros((xq.shape[0], wq.shape[0])), pow2=pow2)
+    M, K = xq.shape
+    N = wq.shape[0]
+    sx = np.repeat(sa.astype(np.float64).T, 128, axis=1)
+    sw = np.repeat(np.repeat(sb.astype(np.float64), 128, axis=0)[:N], 128, axis=1)
+    return 2.0 ** -18 * ((np.abs(DEC[xq]) * sx) @ (np.abs(DEC[wq]) * sw).T)
 
 
 def integer_case(rng, M, N, K):
@@ -31,14 +46,15 @@ def integer_case(rng, M, N, K):
     return xq, sa, wq, sb
 
 
+@pytest.mark.parametrize("fast", PATHS)
 @pytest.mark.parametrize("M,N,K,ue8m0", [(96, 256, 256, False), (300, 384, 512, False),
                                          (300, 384, 512, True), (2048, 8192, 256, False)])
-def test_qout_bitexact_when_the_accumulator_is_exact(M, N, K, ue8m0):
+def test_qout_bitexact_when_the_accumulator_is_exact(M, N, K, ue8m0, fast):
     rng = np.random.default_rng(M + N)
     xq, sa, wq, sb = integer_case(rng, M, N, K)
     flags = oracle.FLAG_UE8M0 if ue8m0 else 0
-    say(f"gemm_nt_qout M={M} N={N} K={K} ue8m0={ue8m0}")
-    yq, sy = fp8.gemm_nt_qout(dev(xq), dev(sa), dev(wq), dev(sb), ue8m0=ue8m0)
+    say(f"gemm_nt_qout M={M} N={N} K={K} ue8m0={ue8m0} fast_accum={fast}")
+    yq, sy = fp8.gemm_nt_qout(dev(xq), dev(sa), dev(wq), dev(sb), ue8m0=ue8m0, fast_accum=fast)
     torch.cuda.synchronize()
     y = oracle.gemm_nt(xq, sa, wq, sb, flags)
     assert np.all(np.abs(y) < 2 ** 24) and np.array_equal(y.astype(np.float32), y)   # exact in FP32
@@ -47,17 +63,20 @@ def test_qout_bitexact_when_the_accumulator_is_exact(M, N, K, ue8m0):
     assert np.array_equal(host(yq), q_ref)
 
 
-@pytest.mark.parametrize("M,N,K,ue8m0", [(200, 512, 1024, False), (256, 1024, 2048, True)])
-def test_qout_within_quantization_and_accumulation_bounds(M, N, K, ue8m0):
+@pytest.mark.parametrize("fast", PATHS)
+@pytest.mark.parametrize("M,N,K,ue8m0", [(200, 512, 1024, False), (256, 1024, 2048, True),
+                                         (1024, 2048, 512, False)])
+def test_qout_within_quantization_and_accumulation_bounds(M, N, K, ue8m0, fast):
     wl = workloads.dense(M, N, K, seed=M + K, outlier_frac=0.001, outlier_mult=100.0)
     flags = oracle.FLAG_UE8M0 if ue8m0 else 0
     xq, sa = oracle.quant_1x128(wl.x, flags)
     wq, sb = oracle.quant_128x128(wl.w, flags)
-    yq, sy = fp8.gemm_nt_qout(dev(xq), dev(sa), dev(wq), dev(sb), ue8m0=ue8m0)
+    say(f"gemm_nt_qout M={M} N={N} K={K} ue8m0={ue8m0} fast_accum={fast}")
+    yq, sy = fp8.gemm_nt_qout(dev(xq), dev(sa), dev(wq), dev(sb), ue8m0=ue8m0, fast_accum=fast)
     torch.cuda.synchronize()
     yq, sy = host(yq), host(sy)
     y = oracle.gemm_nt(xq, sa, wq, sb, flags)
-    b = fp8_mfma_error_bound(xq, sa, wq, sb, np.zeros_like(y), pow2=ue8m0)   # accumulation only
+    b = accumulation_bound(xq, sa, wq, sb, fast, ue8m0)
     G = N // 128
     A = np.abs(y).reshape(M, G, 128).max(axis=2)                              # exact group maxima
     Bg = b.reshape(M, G, 128).max(axis=2)
@@ -76,15 +95,17 @@ def test_qout_within_quantization_and_accumulation_bounds(M, N, K, ue8m0):
     assert np.all(np.abs(d - y) <= allowed)
 
 
-def test_qout_feeds_the_next_gemm():
+@pytest.mark.parametrize("fast", PATHS)
+def test_qout_feeds_the_next_gemm(fast):
     """X -> GEMM with quantized output -> its (yq, sy) as the next GEMM's
     activations, bit-exact end to end where every accumulator is exact."""
     rng = np.random.default_rng(5)
     M, N1, K, N2 = 128, 256, 384, 384
     xq, sa, w1, s1 = integer_case(rng, M, N1, K)
     _, _, w2, s2 = integer_case(rng, 1, N2, N1)
-    yq, sy = fp8.gemm_nt_qout(dev(xq), dev(sa), dev(w1), dev(s1))
-    y2 = fp8.gemm_nt(yq, sy, dev(w2), dev(s2))
+    say(f"chained gemm_nt_qout + gemm_nt fast_accum={fast}")
+    yq, sy = fp8.gemm_nt_qout(dev(xq), dev(sa), dev(w1), dev(s1), fast_accum=fast)
+    y2 = fp8.gemm_nt(yq, sy, dev(w2), dev(s2), fast_accum=fast)
     torch.cuda.synchronize()
     y1 = oracle.gemm_nt(xq, sa, w1, s1)
     q1, t1 = oracle.quant_1x128(y1.astype(np.float32))
