@@ -287,6 +287,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
             db[b] = 0;
         }
 
+        // operands of the current MFMA step, widened one step ahead of use
+        f16x8 hx[FI], hw[FJ];
+#pragma unroll
+        for (int a = 0; a < FI; ++a) hx[a] = e4m3x8_to_f16(rx[a][0], rx[a][1]);
+#pragma unroll
+        for (int b = 0; b < FJ; ++b) hw[b] = e4m3x8_to_f16(rw[b][0], rw[b][1]);
+
+        // Promotion into the next block's units, split over two steps so that
+        // it runs beside MFMAs: values 0..7 of subtile t right after the
+        // block's last MFMA on the following subtile, values 8..15 just before
+        // the next block's first MFMA on t.
+        auto rescale = [&](int a, int b, int v0) FP8K_INLINE {
+            const float f = fa[a] * fb[b];
+            const int d = da[a] + db[b];
+#pragma unroll
+            for (int v = v0; v < v0 + 8; ++v) {
+                if constexpr (POW2) acc[a][b][v] = __builtin_amdgcn_ldexpf(acc[a][b][v], d);
+                else acc[a][b][v] *= f;
+            }
+        };
         auto block = [&](int kb, auto bufc) FP8K_INLINE {
             constexpr int BUF = decltype(bufc)::value;
             constexpr int NBUF = (BUF + 1) % STAGES;
@@ -294,6 +314,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
             // kb+STAGES (position 0, after this block's barrier, into BUF)
             const StageLoads L1 = stage_loads(kb + STAGES - 1, (BUF + STAGES - 1) % STAGES);
             const StageLoads L2 = stage_loads(kb + STAGES, BUF);
+            const bool last = kb + 1 >= KB;
             float sa_n[FI], sb_n[FJ];
             static_for<NP>([&](auto pc) FP8K_INLINE {
                 constexpr int pr = decltype(pc)::value;
@@ -322,68 +343,79 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
                 if constexpr (pr < RB) issue_window(L1, std::integral_constant<int, pr + 1>{});
                 else issue_window(L2, std::integral_constant<int, 0>{});
 
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    f16x8 hx[FI], hw[FJ];
-#pragma unroll
-                    for (int a = 0; a < FI; ++a) hx[a] = e4m3x8_to_f16(rx[a][2 * e], rx[a][2 * e + 1]);
-#pragma unroll
-                    for (int b = 0; b < FJ; ++b) hw[b] = e4m3x8_to_f16(rw[b][2 * e], rw[b][2 * e + 1]);
+                static_for<2>([&](auto ec) FP8K_INLINE {
+                    constexpr int e = decltype(ec)::value;
+                    constexpr bool first = pr == 0 && e == 0, final = pr == NP - 1 && e == 1;
+                    // operands of the following step: the second half of this
+                    // pair's reads, or the first half of the next pair's
+                    f16x8 gx[FI], gw[FJ];
 #pragma unroll
                     for (int a = 0; a < FI; ++a)
+                        gx[a] = e == 0 ? e4m3x8_to_f16(rx[a][2], rx[a][3]) : e4m3x8_to_f16(nx[a][0], nx[a][1]);
+#pragma unroll
+                    for (int b = 0; b < FJ; ++b)
+                        gw[b] = e == 0 ? e4m3x8_to_f16(rw[b][2], rw[b][3]) : e4m3x8_to_f16(nw[b][0], nw[b][1]);
+                    if constexpr (final) {
+                        // factors into the next block's units: s_kb / s_kb+1.
+                        // A zero FP32 scale keeps the current units (factor
+                        // 1): the block it scales holds zero codes (an absmax
+                        // quantizer's all-zero group), so it adds nothing in
+                        // any units.  (Rows past the valid range read zero
+                        // scales too; they are never stored.)  After the last
+                        // block the factor is 1.  Computed branch-free (the
+                        // selects stay inside the MFMA schedule).
+#pragma unroll
+                        for (int a = 0; a < FI; ++a) {
+                            if constexpr (POW2) {
+                                int d = e8m0_of(sa_c[a]) - e8m0_of(sa_n[a]);
+                                asm volatile("" : "+v"(d));
+                                da[a] = last ? 0 : d;
+                            } else {
+                                float r = sa_c[a] * __builtin_amdgcn_rcpf(sa_n[a]);
+                                asm volatile("" : "+v"(r));
+                                fa[a] = (last || sa_n[a] == 0.f) ? 1.f : r;
+                            }
+                        }
 #pragma unroll
                         for (int b = 0; b < FJ; ++b) {
-                            if (pr == 0 && e == 0) {
-                                // promotion: into units of this block's scale product
-                                const float f = fa[a] * fb[b];
-                                const int d = da[a] + db[b];
-#pragma unroll
-                                for (int v = 0; v < 16; ++v) {
-                                    if constexpr (POW2) acc[a][b][v] = __builtin_amdgcn_ldexpf(acc[a][b][v], d);
-                                    else acc[a][b][v] *= f;
-                                }
+                            if constexpr (POW2) {
+                                int d = e8m0_of(sb_c[b]) - e8m0_of(sb_n[b]);
+                                asm volatile("" : "+v"(d));
+                                db[b] = last ? 0 : d;
+                            } else {
+                                float r = sb_c[b] * __builtin_amdgcn_rcpf(sb_n[b]);
+                                asm volatile("" : "+v"(r));
+                                fb[b] = (last || sb_n[b] == 0.f) ? 1.f : r;
                             }
-                            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hw[b], hx[a], acc[a][b], 0, 0, 0);
                         }
-                }
+                    }
+                    static_for<FI * FJ>([&](auto tc) FP8K_INLINE {
+                        constexpr int t = decltype(tc)::value, a = t / FJ, b = t % FJ;
+                        if constexpr (first) rescale(a, b, 8);
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hw[b], hx[a], acc[a][b], 0, 0, 0);
+                        if constexpr (final && t > 0) rescale((t - 1) / FJ, (t - 1) % FJ, 0);
+                    });
+                    if constexpr (final) rescale(FI - 1, FJ - 1, 0);
+                    // one MFMA, then its share of the VALU work
+                    static_for<FI * FJ>([&](auto) FP8K_INLINE {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, (first || final) ? 12 : 3, 0);
+                    });
+#pragma unroll
+                    for (int a = 0; a < FI; ++a) hx[a] = gx[a];
+#pragma unroll
+                    for (int b = 0; b < FJ; ++b) hw[b] = gw[b];
+                });
 #pragma unroll
                 for (int a = 0; a < FI; ++a) rx[a] = nx[a];
 #pragma unroll
                 for (int b = 0; b < FJ; ++b) rw[b] = nw[b];
             });
-            // factors for the next block: s_kb / s_kb+1.  A zero FP32 scale
-            // keeps the current units (factor 1): the block it scales holds
-            // zero codes (an absmax quantizer's all-zero group), so it adds
-            // nothing in any units.  (Rows past the valid range read zero
-            // scales too; they are never stored.)
+            // the next block's scales become current (a zero FP32 scale keeps the units)
 #pragma unroll
-            for (int a = 0; a < FI; ++a) {
-                if constexpr (POW2) {
-                    da[a] = e8m0_of(sa_c[a]) - e8m0_of(sa_n[a]);
-                } else {
-                    const bool z = sa_n[a] == 0.f;
-                    fa[a] = z ? 1.f : sa_c[a] * __builtin_amdgcn_rcpf(sa_n[a]);
-                    if (kb + 1 < KB && !z) sa_c[a] = sa_n[a];
-                }
-            }
+            for (int a = 0; a < FI; ++a) sa_c[a] = (last || (!POW2 && sa_n[a] == 0.f)) ? sa_c[a] : sa_n[a];
 #pragma unroll
-            for (int b = 0; b < FJ; ++b) {
-                if constexpr (POW2) {
-                    db[b] = e8m0_of(sb_c[b]) - e8m0_of(sb_n[b]);
-                } else {
-                    const bool z = sb_n[b] == 0.f;
-                    fb[b] = z ? 1.f : sb_c[b] * __builtin_amdgcn_rcpf(sb_n[b]);
-                    if (kb + 1 < KB && !z) sb_c[b] = sb_n[b];
-                }
-            }
-            if constexpr (POW2) {
-                if (kb + 1 < KB) {
-#pragma unroll
-                    for (int a = 0; a < FI; ++a) sa_c[a] = sa_n[a];
-#pragma unroll
-                    for (int b = 0; b < FJ; ++b) sb_c[b] = sb_n[b];
-                }
-            }
+            for (int b = 0; b < FJ; ++b) sb_c[b] = (last || (!POW2 && sb_n[b] == 0.f)) ? sb_c[b] : sb_n[b];
         };
         int kb = 0;
         for (; kb + STAGES <= KB; kb += STAGES)
