@@ -35,6 +35,7 @@ STATUS = {
     4: "FP8_ERR_UNSUPPORTED",
     5: "FP8_ERR_NO_DEVICE",
     6: "FP8_ERR_LAUNCH",
+    7: "FP8_ERR_SCRATCH",
 }
 
 # Exported C symbols (kept in step with include/fp8gemm.h by the tests).
@@ -43,6 +44,7 @@ SYMBOLS = (
     "fp8_quant_128x128",
     "fp8_gemm_nt",
     "fp8_gemm_nt_ws",
+    "fp8_gemm_nt_noalloc",
     "fp8_gemm_workspace_size",
     "fp8_gemm_plan",
     "fp8_gemm_nt_qout",
@@ -93,6 +95,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fp8_quant_128x128.argtypes = [P, I64, I64, P, P, U32, P]
     L.fp8_gemm_nt.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
     L.fp8_gemm_nt_ws.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P, ctypes.c_size_t, P]
+    L.fp8_gemm_nt_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
     L.fp8_gemm_workspace_size.argtypes = [I64, I64, I64, U32]
     L.fp8_gemm_workspace_size.restype = ctypes.c_size_t
     L.fp8_gemm_plan.argtypes = [I32, I64, I64, I64, U32, I32, ctypes.c_size_t, ctypes.POINTER(GemmPlan)]
@@ -103,7 +106,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fp8_gemm_nt_mx.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
     L.fp8_quant_mxfp4.argtypes = [P, I64, I64, P, P, P]
     L.fp8_gemm_nt_mx_w4.argtypes = [P, P, P, P, P, I64, I64, I64, U32, P]
-    for fn in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_gemm_nt", "fp8_gemm_nt_ws", "fp8_gemm_plan",
+    for fn in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_gemm_nt", "fp8_gemm_nt_ws", "fp8_gemm_nt_noalloc",
+               "fp8_gemm_plan",
                "fp8_gemm_nt_qout",
                "fp8_grouped_gemm_contiguous", "fp8_grouped_gemm_masked", "fp8_quant_mx",
                "fp8_gemm_nt_mx", "fp8_quant_mxfp4", "fp8_gemm_nt_mx_w4"):

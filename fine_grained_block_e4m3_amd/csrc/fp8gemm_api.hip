@@ -52,6 +52,40 @@ fp8_status current_device_cus(int* cus) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Scratch of fp8_gemm_nt_noalloc: the split-K partial sums of the decode GEMM
+// in a fixed device array instead of a workspace the caller passes.  Every
+// GPU holds its own copy (from when the library is loaded on it until the
+// process ends); every call on that GPU shares it.  4 MiB holds the largest
+// split the planner picks on a device of up to 341 compute units: splits * N
+// stays below 96 * CUs columns and M <= 32 rows of FP32.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of this device's scratch, resolved once per device (the
+// array's name is only a host-side stand-in).
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+fp8_status current_device_scratch(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return FP8_ERR_NO_DEVICE;
+    }
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) {
+        (void)hipGetLastError();
+        return FP8_ERR_NO_DEVICE;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return FP8_OK;
+}
+
 fp8_status launch_status() {
     return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH;
 }
@@ -435,6 +469,7 @@ const char* fp8_status_string(fp8_status s) {
         case FP8_ERR_UNSUPPORTED: return "unsupported configuration";
         case FP8_ERR_NO_DEVICE: return "no usable HIP device";
         case FP8_ERR_LAUNCH: return "kernel launch failed";
+        case FP8_ERR_SCRATCH: return "the problem needs more split-K scratch than fp8_gemm_nt_noalloc holds";
     }
     return "unknown status";
 }
@@ -581,6 +616,23 @@ fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq, co
                        uint16_t* y, int64_t M, int64_t N, int64_t K, uint32_t flags,
                        void* stream) {
     return fp8_gemm_nt_ws(xq, sa, wq, sb, y, M, N, K, flags, nullptr, 0, stream);
+}
+
+fp8_status fp8_gemm_nt_noalloc(const uint8_t* xq, const float* sa, const uint8_t* wq, const float* sb,
+                               uint16_t* y, int64_t M, int64_t N, int64_t K, uint32_t flags, void* stream) {
+    if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K) || (flags & ~kGemmFlags))
+        return FP8_ERR_INVALID_ARG;
+    if (K % 128) return FP8_ERR_SHAPE;
+    if (K > kMaxGemmK) return FP8_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return FP8_OK;
+    const size_t need = fp8_gemm_workspace_size(M, N, K, flags);
+    if (need > kScratchBytes) return FP8_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need) {
+        const fp8_status st = current_device_scratch(&ws);
+        if (st != FP8_OK) return st;
+    }
+    return fp8_gemm_nt_ws(xq, sa, wq, sb, y, M, N, K, flags, ws, need, stream);
 }
 
 size_t fp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, uint32_t flags) {

@@ -30,6 +30,8 @@
  *       FP8_ERR_ALIGNMENT    a pointer not 16-byte aligned
  *       FP8_ERR_NO_DEVICE    no HIP device is usable
  *       FP8_ERR_LAUNCH       the kernel launch reported an error
+ *       FP8_ERR_SCRATCH      (fp8_gemm_nt_noalloc) the problem needs more
+ *                            split-K scratch than its fixed array holds
  *     A call with an empty problem (M == 0, E == 0, N == 0 ...) returns FP8_OK
  *     and enqueues nothing.  Device-side data (expert indices, valid counts)
  *     is never reported as an error: its handling is defined per call.
@@ -53,7 +55,8 @@ typedef enum {
     FP8_ERR_ALIGNMENT = 3,
     FP8_ERR_UNSUPPORTED = 4,
     FP8_ERR_NO_DEVICE = 5,
-    FP8_ERR_LAUNCH = 6
+    FP8_ERR_LAUNCH = 6,
+    FP8_ERR_SCRATCH = 7
 } fp8_status;
 
 /* Quantizers: round each group's scale up to a power of two (UE8M0, [DG]
@@ -140,6 +143,26 @@ fp8_status fp8_gemm_nt_ws(const uint8_t* xq, const float* sa, const uint8_t* wq,
                           const float* sb, uint16_t* y, int64_t M, int64_t N,
                           int64_t K, uint32_t flags, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * fp8_gemm_nt for callers that cannot allocate (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): fp8_gemm_nt_ws with
+ * the split-K workspace taken from a fixed 4 MiB device array inside the
+ * library (one per GPU, loaded with the library, held until the process
+ * ends) instead of the caller's memory.  Calls no hipMalloc, hipFree or
+ * other allocating routine; the first call on a device looks up that
+ * device's array.  The result equals fp8_gemm_nt_ws with a workspace of
+ * fp8_gemm_workspace_size() bytes.  A shape whose split needs more than the
+ * array (none on a device of up to 341 compute units) returns
+ * FP8_ERR_SCRATCH before any launch.  Every call on one GPU shares the
+ * array: calls that overlap on one GPU (several streams, or several host
+ * threads) race on it and must be ordered by the caller.  Each split writes
+ * every partial sum it covers before the reduction reads it, so nothing
+ * needs clearing between calls.
+ */
+fp8_status fp8_gemm_nt_noalloc(const uint8_t* xq, const float* sa, const uint8_t* wq,
+                               const float* sb, uint16_t* y, int64_t M, int64_t N,
+                               int64_t K, uint32_t flags, void* stream);
 
 /* Workspace bytes with which fp8_gemm_nt_ws splits K for this shape and these
  * flags on the current device (0 when it does not split, or on bad
