@@ -12,7 +12,7 @@ import fine_grained_block_e4m3_amd as fp8
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8gemm.h")
 
-OK, INVALID, SHAPE, ALIGN, UNSUP, NODEV, LAUNCH = range(7)
+OK, INVALID, SHAPE, ALIGN, UNSUP, NODEV, LAUNCH, SCRATCH = range(8)
 P = ctypes.c_void_p
 A = P(4096)           # an aligned fake device address: never dereferenced on the host
 MIS = P(4097)
@@ -42,8 +42,8 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_constants(L):
     assert L.fp8_get_mk_alignment_for_contiguous_layout() == 128
-    for s in range(7):
-        assert L.fp8_status_string(s)
+    for s in range(8):
+        assert L.fp8_status_string(s) and L.fp8_status_string(s) != b"unknown status"
     assert L.fp8_status_string(99) == b"unknown status"
 
 
@@ -57,6 +57,7 @@ def test_gemm_validation(L):
     assert _gemm(L, M=-1) == INVALID
     assert _gemm(L, N=1 << 31) == INVALID
     assert _gemm(L, flags=4) == INVALID
+    assert _gemm(L, flags=fp8.FLAG_UE8M0 | fp8.FLAG_FAST_ACCUM, M=0) == OK
     assert _gemm(L, K=100) == SHAPE
     assert _gemm(L, K=0) == SHAPE
     assert _gemm(L, xq=MIS) == ALIGN
@@ -144,11 +145,109 @@ def test_mxfp4_validation(L):
     assert g(A, A, A, A, A, 4, 0, 128, 0, None) == OK
 
 
+def test_workspace_and_noalloc_validation(L):
+    """The workspace variant and the no-allocation variant validate like
+    fp8_gemm_nt; a workspace size needs a non-NULL, aligned workspace."""
+    for fn in (lambda **k: L.fp8_gemm_nt_ws(k.get("xq", A), A, A, A, A, k.get("M", 4), 8, k.get("K", 128),
+                                             k.get("flags", 0), k.get("ws", None), k.get("nb", 0), None),
+               lambda **k: L.fp8_gemm_nt_noalloc(k.get("xq", A), A, A, A, A, k.get("M", 4), 8, k.get("K", 128),
+                                                  k.get("flags", 0), None)):
+        assert fn(xq=None) == INVALID
+        assert fn(flags=8) == INVALID
+        assert fn(K=64) == SHAPE
+        assert fn(M=0) == OK
+    assert L.fp8_gemm_nt_ws(A, A, A, A, A, 4, 8, 128, 0, None, 64, None) == INVALID
+    assert L.fp8_gemm_nt_ws(A, A, A, A, A, 4, 8, 128, 0, MIS, 64, None) == ALIGN
+    assert L.fp8_gemm_workspace_size(4, 8, 100, 0) == 0
+
+
+def _plan(layout, M, N, K, flags=0, cus=256, ws=0):
+    plan = fp8.GemmPlan()
+    st = fp8.load_library().fp8_gemm_plan(layout, M, N, K, flags, cus, ws, ctypes.byref(plan))
+    assert st == OK, st
+    return plan
+
+
+def test_plan_pins_the_pages_unaligned_block_example(L):
+    """DeepGEMM page, section "非对齐块大小": M = 256, N = 7168 on 132 SMs gives
+    112 tiles of 128x128, one wave that leaves 20 SMs idle.  The FP8-instruction
+    planner takes exactly that tiling for this shape and that SM count."""
+    p = _plan(0, 256, 7168, 7168, fp8.FLAG_FAST_ACCUM, cus=132)
+    assert (p.tile_m, p.tile_n, p.tiles, p.grid) == (128, 128, 112, 112)
+    assert 132 - p.grid == 20
+    # the page's alternative, 128x112, would give 2 * 64 = 128 tiles: 97% of 132
+    assert ((256 + 127) // 128) * ((7168 + 111) // 112) == 128
+
+
+def test_plan_fills_whole_waves_on_the_prefill_shape(L):
+    """4096x7168 on 256 CUs: 256x256 tiles are 448 = 1.75 waves; the FP8
+    planner takes 256x224 (512 tiles = 2 whole waves, the same trade as the
+    page's 112-wide blocks); the exact path keeps 256x256 (its 32x32 subtiles
+    do not split 224 columns over two waves)."""
+    f = _plan(0, 4096, 7168, 7168, fp8.FLAG_FAST_ACCUM)
+    assert (f.exact, f.tile_m, f.tile_n, f.tiles, f.grid) == (0, 256, 224, 512, 256)
+    e = _plan(0, 4096, 7168, 7168)
+    assert (e.exact, e.tile_m, e.tile_n, e.tiles, e.waves) == (1, 256, 256, 448, 8)
+    assert _plan(0, 64, 24576, 1536).tile_n == 96 and _plan(0, 64, 24576, 1536).tiles == 256
+    assert _plan(0, 16, 24576, 1536, fp8.FLAG_FAST_ACCUM).kernel == 1
+    assert _plan(0, 40, 24576, 1536, fp8.FLAG_FAST_ACCUM).kernel == 2
+    assert _plan(0, 4096, 7168, 7168, fp8.PLAN_MX).tile_n == 224
+    assert (_plan(0, 4096, 7168, 7168, fp8.PLAN_QOUT).tile_n, _plan(0, 128, 256, 512, fp8.PLAN_QOUT).tile_m) == (256, 128)
+
+
+@pytest.mark.parametrize("fast", [0, fp8.FLAG_FAST_ACCUM])
+@pytest.mark.parametrize("M", [128, 8704, 9216, 1088 * 128 // 16, 33 * 128, 256 * 128 + 128])
+def test_plan_contiguous_launches_cover_every_row_once(L, M, fast):
+    """Contiguous layout: 128-row tiles; when the last round of 128x256 tiles
+    would leave over half of the CUs idle, the blocks past the full rounds go
+    to a second launch of smaller tiles.  The two launches cover [0, M)
+    exactly once, at whole 128-row blocks, and the first holds whole rounds."""
+    N, cus = 4096, 256
+    p = _plan(1, M, N, 7168, fast)
+    assert p.tile_m == 128 and p.tile_n == 256
+    assert p.main_rows % 128 == 0 and 0 < p.main_rows <= M
+    assert p.tiles == ((p.main_rows + 127) // 128) * (N // 256)
+    if p.main_rows < M:
+        assert p.tiles % cus == 0, "the first launch holds whole rounds"
+        assert p.tail_tile_m == 128 and p.tail_tile_n in (64, 128)
+        assert p.tail_tiles == ((M - p.main_rows + 127) // 128) * (N // p.tail_tile_n)
+        blocks = ((M + 127) // 128) * (N // 256)
+        assert 2 * (blocks % cus) < cus
+    else:
+        assert p.tail_tile_m == 0
+
+
+def test_plan_decode_split_and_workspace(L):
+    """The decode kernel splits K over workgroups only with a workspace that
+    holds the partial sums: 16 x 2112 x 7168 on 256 CUs, 22 column tiles of 96,
+    at most 8 splits."""
+    p0 = _plan(0, 16, 2112, 7168, fp8.FLAG_FAST_ACCUM, ws=0)
+    assert (p0.kernel, p0.k_splits, p0.workspace_bytes, p0.tiles) == (1, 1, 0, 22)
+    big = 1 << 30
+    p = _plan(0, 16, 2112, 7168, fp8.FLAG_FAST_ACCUM, ws=big)
+    assert p.k_splits == 8 and p.workspace_bytes == 8 * 16 * 2112 * 4 and p.tiles == 22 * 8
+    p2 = _plan(0, 16, 2112, 7168, fp8.FLAG_FAST_ACCUM, ws=p.workspace_bytes - 1)
+    assert p2.k_splits == 1
+    assert _plan(0, 16, 2112, 7168, 0, ws=big).k_splits == 1      # the exact path never splits
+
+
+def test_plan_validation(L):
+    plan = fp8.GemmPlan()
+    f = L.fp8_gemm_plan
+    assert f(3, 4, 8, 128, 0, 256, 0, ctypes.byref(plan)) == INVALID
+    assert f(0, 4, 8, 128, 0, 0, 0, ctypes.byref(plan)) == INVALID
+    assert f(0, 4, 8, 128, 0, 256, 0, None) == INVALID
+    assert f(1, 4, 8, 128, fp8.PLAN_MX, 256, 0, ctypes.byref(plan)) == INVALID
+    assert f(0, 4, 8, 100, 0, 256, 0, ctypes.byref(plan)) == SHAPE
+
+
 def test_no_device_reported_without_gpu(L):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible")
     assert _gemm(L) == NODEV
+    assert L.fp8_gemm_nt_noalloc(A, A, A, A, A, 4, 8, 128, 0, None) == NODEV
+    assert L.fp8_gemm_workspace_size(16, 2112, 7168, fp8.FLAG_FAST_ACCUM) == 0
     assert L.fp8_quant_1x128(A, 4, 128, A, A, 0, None) == NODEV
     assert L.fp8_quant_mx(A, 4, 128, A, A, None) == NODEV
     assert L.fp8_gemm_nt_mx(A, A, A, A, A, 4, 8, 128, 0, None) == NODEV
