@@ -81,6 +81,8 @@ def lib():
         L.oracle_gemm_mx_w4.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.oracle_gemm_mx_w4_elems.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P]
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
         for fn in ("oracle_quant_1x128", "oracle_quant_128x128", "oracle_gemm_nt",
                    "oracle_gemm_nt_elems", "oracle_grouped_contiguous",
                    "oracle_grouped_masked", "oracle_quant_mx", "oracle_gemm_mx",
@@ -103,6 +105,11 @@ def _check(rc: int, what: str):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads used by the following calls; results do not depend on it."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def e4m3_decode(codes) -> np.ndarray:

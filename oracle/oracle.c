@@ -399,6 +399,18 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads for the following calls (n >= 1); no effect on any result: every
+ * parallel loop writes disjoint outputs, each computed in a fixed order. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* MXFP8: E4M3 elements, one E8M0 scale per 1x32 group along K               */
 /* ------------------------------------------------------------------------ */

@@ -107,6 +107,7 @@ int oracle_gemm_mx_w4_elems(const uint8_t* xq, const uint8_t* ea, const uint8_t*
 
 /* Number of OpenMP threads the oracle will use. */
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
