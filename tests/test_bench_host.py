@@ -71,9 +71,32 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
 
 def test_stale_counters_are_not_reported(tmp_path, monkeypatch):
     (tmp_path / "profiles").mkdir()
-    entry = {"source_sha": "abc", "hbm_bytes_per_dispatch": 123.0}
-    (tmp_path / "profiles" / "counters.json").write_text(json.dumps({"gemm_cfg2": entry}))
+    entry = {"source_sha": "abc", "hbm_bytes_per_dispatch": 123.0, "clock_mhz_grbm": 2000.0,
+             "mfma_busy_frac": 0.5}
+    (tmp_path / "profiles" / "counters.json").write_text(json.dumps({"gemm_exact_cfg2": entry}))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.load_traffic("gemm_cfg2", "abc") == 123.0
-    assert bench.load_traffic("gemm_cfg2", "def") is None
-    assert bench.load_traffic("gemm_cfg9", "abc") is None
+    assert bench.load_counters("gemm_exact_cfg2", "abc")["hbm_bytes_per_dispatch"] == 123.0
+    assert bench.load_counters("gemm_exact_cfg2", "def") is None
+    assert bench.load_counters("gemm_exact_cfg9", "abc") is None
+    r = bench.roofline(1e12, 1e9, 1e-3, "f16", True, bench.load_counters("gemm_exact_cfg2", "abc"))
+    assert r["bound"] == "mfma" and r["peak"] == 2500.0 and abs(r["frac"] - 1000 / 2500) < 1e-12
+    assert r["frac_of_fp8_peak"] == r["achieved"] / 5000.0
+    assert r["traffic"] == 123.0 and r["traffic_ratio"] == 123.0 / 1e9 and r["clock_mhz_counters"] == 2000.0
+    r = bench.roofline(1e12, 1e9, 1e-3, "fp8", False, None)
+    assert r["bound"] == "hbm" and r["traffic"] is None and abs(r["frac"] - 1000 / 8000) < 1e-12
+
+
+def test_stats_and_cpu_model():
+    s = bench.stats([3.0, 1.0, 2.0, 10.0])
+    assert s == {"mean": 4.0, "median": 2.5, "min": 1.0, "n": 4}
+    assert bench._cpu_model().get("model name") is not None
+
+
+def test_cpu_baseline_splits_quantization_and_gemm():
+    wl = workloads.dense(64, 256, 512, seed=0)
+    r = bench.cpu_baseline(wl, 0.2)
+    assert r["kind"] == "oracle" and r["cores"] >= 1 and r["nproc"] >= 1
+    assert r["quant_seconds"] > 0 and r["gemm_seconds"] > 0
+    assert r["one_thread"]["gemm_seconds"] > 0 and "1 thread" in r["one_thread"]["sample"]
+    import oracle
+    assert oracle.num_threads() == r["cores"]          # the thread count is restored
