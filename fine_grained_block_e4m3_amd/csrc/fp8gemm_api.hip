@@ -55,10 +55,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Scratch of fp8_gemm_nt_noalloc: the split-K partial sums of the decode GEMM
 // in a fixed device array instead of a workspace the caller passes.  Every
 // GPU holds its own copy (from when the library is loaded on it until the
-// process ends); every call on that GPU shares it.  4 MiB holds the largest
+// process ends); every call on that GPU shares it.  8 MiB holds the largest
 // split the planner picks on a device of up to 341 compute units: splits * N
-// stays below 96 * CUs columns and M <= 32 rows of FP32.
-constexpr size_t kScratchBytes = (size_t)4 << 20;
+// stays at or below 96 * CUs columns, and a split decode GEMM has at most 64
+// rows of FP32 partial sums (64 * 4 * 96 * 341 bytes < 8 MiB).
+constexpr size_t kScratchBytes = (size_t)8 << 20;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 // Device address of this device's scratch, resolved once per device (the
@@ -140,7 +141,17 @@ enum Inst : int {
     kFast128x256, kFast128x64,
     // exact-partial kernel (default)
     kExact64x96, kExact256x256, kExact128x256, kExact128x128, kExactQ256x256, kExactQ128x256,
+    kExactDecode, kExactDecodeX,
 };
+
+// Exact decode kernel: 32 W rows per wave, kExactDecodeNW waves per
+// workgroup, a W ring of kExactDecodeNS K blocks per wave, X in chunks of
+// kExactDecodeKBC K blocks.
+constexpr int kExactDecodeNW = 3, kExactDecodeNS = 5, kExactDecodeKBC = 4;
+// X-resident variant: at most kbmax K blocks per workgroup (its X range, sA
+// and the W rings fit in LDS), a W ring of kExactDecodeXNS blocks per wave.
+constexpr int kExactDecodeXNS = 4;
+constexpr int exact_decode_kbmax(int64_t M) { return M <= 32 ? 24 : 12; }
 
 struct InstInfo { int bm, bn, waves, kernel, exact; };
 InstInfo inst_info(Inst i) {
@@ -160,18 +171,21 @@ InstInfo inst_info(Inst i) {
         case kExact128x128: return {128, 128, 4, 0, 1};
         case kExactQ256x256: return {256, 256, 8, 0, 1};
         case kExactQ128x256: return {128, 256, 4, 0, 1};
+        case kExactDecode: return {64, 32 * kExactDecodeNW, kExactDecodeNW, 3, 1};
+        case kExactDecodeX: return {64, 32 * kExactDecodeNW, kExactDecodeNW, 4, 1};
     }
     return {0, 0, 0, 0, 0};
 }
 
-// Decode split-K: workgroups along K per 96-column tile of the M <= 32 decode
-// kernel (FP8 instruction path), when the column tiles are fewer than the
-// compute units and the caller's workspace holds the partial sums.
+// Decode split-K: workgroups along K per column tile of a decode kernel
+// (tile_n columns, K in chunks of kbc blocks), when the column tiles are
+// fewer than the compute units and the caller's workspace holds the partial
+// sums.
 constexpr int kDecodeTileN = 96;
 size_t decode_ws_bytes(int64_t splits, int64_t M, int64_t N) { return (size_t)(splits * M * N) * sizeof(float); }
-int64_t decode_splits(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
-    const int64_t tiles = cdiv(N, kDecodeTileN);
-    const int64_t nct = cdiv(K / 128, 4);          // K chunks of 4 blocks
+int64_t decode_splits(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes, int tile_n, int kbc) {
+    const int64_t tiles = cdiv(N, tile_n);
+    const int64_t nct = cdiv(K / 128, kbc);
     int64_t splits = tiles < cus ? cus / tiles : 1;
     if (splits > nct) splits = nct;
     if (splits > 8) splits = 8;
@@ -213,7 +227,7 @@ Plan plan_fast(int mode, int64_t M, int64_t N, int64_t K, bool mx, bool qout, in
             // them, several per CU) measured slower on every shape tried.
             if (!mx && M <= 32) {
                 pl.main = kFastDecode;
-                pl.k_splits = decode_splits(M, N, K, cus, ws_bytes);
+                pl.k_splits = decode_splits(M, N, K, cus, ws_bytes, kDecodeTileN, 4);
             } else if (!mx && M <= 48 && K <= fp8k::kDecodeKxMaxK) {
                 pl.main = kFastDecodeKx;
             } else {
@@ -264,14 +278,32 @@ Plan plan_fast(int mode, int64_t M, int64_t N, int64_t K, bool mx, bool qout, in
 
 // The exact-partial path (FP16 matrix instruction on E4M3 operands widened
 // exactly).  Waves hold 64x128 (or 64x64) of 32x32 subtiles.
-Plan plan_exact(int mode, int64_t M, int64_t N, bool qout, int cus) {
+Plan plan_exact(int mode, int64_t M, int64_t N, int64_t K, bool qout, int cus, size_t ws_bytes) {
     Plan pl{kExact128x128, M, kExact128x128, 1};
     if (mode == fp8k::kDense) {
         if (qout) {
             // a 1x128 output group per wave: 128-column waves
             pl.main = cdiv(M, 256) * cdiv(N, 256) >= cus ? kExactQ256x256 : kExactQ128x256;
         } else if (M <= 64) {
-            pl.main = kExact64x96;
+            // decode-sized M.  With few column tiles (and a workspace) K is
+            // split over workgroups: the exact decode kernel with X resident
+            // when each range holds at most kbmax blocks, else with X in
+            // chunks.  Unsplit, M <= 32 takes the decode kernel, M > 32 the
+            // 64x96 tile of the main kernel (kernel trace, N 24576, K 1536:
+            // M 64 20.0 vs 15.4 us, M 48 19.8 vs 15.1, M 32 13.8 vs 14.6,
+            // M 16 14.3 vs 14.4; N 4096, K 7168: M 16 16.9 us split vs 40
+            // unsplit).
+            const int64_t sx = decode_splits(M, N, K, cus, ws_bytes, 32 * kExactDecodeNW, 1);
+            const bool fits = cdiv(K / 128, sx) <= exact_decode_kbmax(M);
+            if (fits && (sx > 1 || M <= 32)) {
+                pl.main = kExactDecodeX;
+                pl.k_splits = sx;
+            } else if (sx == 1 && M > 32) {
+                pl.main = kExact64x96;
+            } else {
+                pl.main = kExactDecode;
+                pl.k_splits = decode_splits(M, N, K, cus, ws_bytes, 32 * kExactDecodeNW, kExactDecodeKBC);
+            }
         } else if (cdiv(M, 256) * cdiv(N, 256) >= cus) {
             pl.main = kExact256x256;
         } else if (cdiv(M, 128) * cdiv(N, 256) >= cus) {
@@ -300,7 +332,7 @@ Plan plan_exact(int mode, int64_t M, int64_t N, bool qout, int cus) {
 Plan make_plan(int mode, int64_t M, int64_t N, int64_t K, uint32_t flags, bool mx, bool qout, int cus,
                size_t ws_bytes) {
     return (mx || (flags & FP8_FLAG_FAST_ACCUM)) ? plan_fast(mode, M, N, K, mx, qout, cus, ws_bytes)
-                                                 : plan_exact(mode, M, N, qout, cus);
+                                                 : plan_exact(mode, M, N, K, qout, cus, ws_bytes);
 }
 
 // ---------------------------------------------------------------------------
@@ -388,8 +420,67 @@ fp8_status launch_fast(Inst i, const fp8k::GemmParams& p, int64_t splits, void* 
     }
 }
 
+// Exact decode GEMM (M <= 64): one workgroup per 32*NW output columns and all
+// M rows; MSUB = ceil(M/32) row subtiles.  With splits > 1 the K chunks are
+// split over that many workgroups per tile (FP32 partial sums in the
+// caller's workspace, added in split order by a second kernel).
+template <int NW, int NS, int KBC>
+fp8_status launch_decode_exact(const fp8k::GemmParams& p0, int64_t splits, void* ws, hipStream_t stream) {
+    fp8k::GemmParams p = p0;
+    const int64_t tiles = cdiv(p.N, 32 * NW);
+    if (tiles <= 0) return FP8_OK;
+    if (splits <= 1) ws = nullptr;
+    p.part = static_cast<float*>(ws);
+    const dim3 grid((unsigned)tiles, (unsigned)(ws ? splits : 1)), block(64 * NW);
+    switch ((p.M + 31) / 32) {
+        case 1: hipLaunchKernelGGL((fp8k::decode_exact_kernel<1, NW, NS, KBC>), grid, block, 0, stream,
+                                   p.xq, p.sa, p.wq, p.sb, p.y, p); break;
+        case 2: hipLaunchKernelGGL((fp8k::decode_exact_kernel<2, NW, NS, KBC>), grid, block, 0, stream,
+                                   p.xq, p.sa, p.wq, p.sb, p.y, p); break;
+        default: return FP8_ERR_UNSUPPORTED;
+    }
+    fp8_status st = launch_status();
+    if (ws && st == FP8_OK) {
+        const int64_t mn = p.M * p.N;
+        hipLaunchKernelGGL(fp8k::decode_split_reduce, dim3((unsigned)cdiv(mn, 256)), dim3(256), 0, stream,
+                           static_cast<const float*>(ws), (int)splits, mn, p.y);
+        st = launch_status();
+    }
+    return st;
+}
+
+// The X-resident variant: K blocks [s*KB/S, (s+1)*KB/S) per workgroup (at
+// most exact_decode_kbmax(M) of them, which the plan ensures).
+template <int NW, int NS>
+fp8_status launch_decode_exact_x(const fp8k::GemmParams& p0, int64_t splits, void* ws, hipStream_t stream) {
+    fp8k::GemmParams p = p0;
+    const int64_t tiles = cdiv(p.N, 32 * NW);
+    if (tiles <= 0) return FP8_OK;
+    if (splits <= 1) ws = nullptr;
+    const int64_t s = ws ? splits : 1;
+    if (s > p.K / 128 || cdiv(p.K / 128, s) > exact_decode_kbmax(p.M)) return FP8_ERR_UNSUPPORTED;
+    p.part = static_cast<float*>(ws);
+    const dim3 grid((unsigned)tiles, (unsigned)s), block(64 * NW);
+    switch ((p.M + 31) / 32) {
+        case 1: hipLaunchKernelGGL((fp8k::decode_exact_x_kernel<1, NW, NS, 24>), grid, block, 0, stream,
+                                   p.xq, p.sa, p.wq, p.sb, p.y, p); break;
+        case 2: hipLaunchKernelGGL((fp8k::decode_exact_x_kernel<2, NW, NS, 12>), grid, block, 0, stream,
+                                   p.xq, p.sa, p.wq, p.sb, p.y, p); break;
+        default: return FP8_ERR_UNSUPPORTED;
+    }
+    fp8_status st = launch_status();
+    if (ws && st == FP8_OK) {
+        const int64_t mn = p.M * p.N;
+        hipLaunchKernelGGL(fp8k::decode_split_reduce, dim3((unsigned)cdiv(mn, 256)), dim3(256), 0, stream,
+                           static_cast<const float*>(ws), (int)splits, mn, p.y);
+        st = launch_status();
+    }
+    return st;
+}
+
 template <int MODE, bool POW2>
-fp8_status launch_exact_inst(Inst i, const fp8k::GemmParams& p, int cus, hipStream_t stream, int64_t m_hi) {
+fp8_status launch_exact_inst(Inst i, const fp8k::GemmParams& p, int64_t splits, void* ws, int cus,
+                             hipStream_t stream, int64_t m_hi) {
     if constexpr (MODE == fp8k::kDense) {
         switch (i) {
             case kExact64x96: return launch_exact<64, 96, 2, 3, MODE, POW2, 3>(p, cus, stream);
@@ -398,6 +489,9 @@ fp8_status launch_exact_inst(Inst i, const fp8k::GemmParams& p, int cus, hipStre
             case kExact128x128: return launch_exact<128, 128, 2, 2, MODE, POW2, 4>(p, cus, stream);
             case kExactQ256x256: return launch_exact<256, 256, 4, 2, MODE, POW2, 2, true>(p, cus, stream);
             case kExactQ128x256: return launch_exact<128, 256, 2, 2, MODE, POW2, 3, true>(p, cus, stream);
+            case kExactDecode:
+                return launch_decode_exact<kExactDecodeNW, kExactDecodeNS, kExactDecodeKBC>(p, splits, ws, stream);
+            case kExactDecodeX: return launch_decode_exact_x<kExactDecodeNW, kExactDecodeXNS>(p, splits, ws, stream);
             default: return FP8_ERR_UNSUPPORTED;
         }
     } else {
@@ -417,7 +511,7 @@ fp8_status run_plan(const Plan& pl, bool exact, const fp8k::GemmParams& p, void*
                     hipStream_t stream, bool qout) {
     constexpr bool kPow2 = PATH == fp8k::kPathFp8Pow2;
     auto one = [&](Inst i, const fp8k::GemmParams& q, int64_t m_hi) {
-        return exact ? launch_exact_inst<MODE, kPow2>(i, q, cus, stream, m_hi)
+        return exact ? launch_exact_inst<MODE, kPow2>(i, q, pl.k_splits, ws, cus, stream, m_hi)
                      : launch_fast<MODE, PATH>(i, q, pl.k_splits, ws, cus, stream, m_hi, qout);
     };
     if (MODE == fp8k::kContiguous && pl.main_rows < p.M) {
@@ -641,7 +735,8 @@ size_t fp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, uint32_t flags) 
     int cus = 0;
     if (current_device_cus(&cus) != FP8_OK) return 0;
     const Plan pl = make_plan(fp8k::kDense, M, N, K, flags, false, false, cus, SIZE_MAX);
-    return pl.main == kFastDecode && pl.k_splits > 1 ? decode_ws_bytes(pl.k_splits, M, N) : 0;
+    return (pl.main == kFastDecode || pl.main == kExactDecode || pl.main == kExactDecodeX) && pl.k_splits > 1
+               ? decode_ws_bytes(pl.k_splits, M, N) : 0;
 }
 
 fp8_status fp8_gemm_plan(int32_t layout, int64_t M, int64_t N, int64_t K, uint32_t flags, int32_t compute_units,
@@ -665,7 +760,7 @@ fp8_status fp8_gemm_plan(int32_t layout, int64_t M, int64_t N, int64_t K, uint32
     plan->k_splits = (int32_t)pl.k_splits;
     plan->workspace_bytes = pl.k_splits > 1 ? decode_ws_bytes(pl.k_splits, M, N) : 0;
     if (a.kernel != 0) {
-        plan->tiles = cdiv(N, kDecodeTileN) * pl.k_splits;
+        plan->tiles = cdiv(N, a.bn) * pl.k_splits;
         plan->grid = (int32_t)plan->tiles;
     } else {
         const int64_t rows = layout == 1 ? pl.main_rows : M;

@@ -503,3 +503,471 @@ __global__ __launch_bounds__(512, 1) void decode_kx_kernel(
 }
 
 }  // namespace fp8k
+
+namespace fp8k {
+
+// ---------------------------------------------------------------------------
+// Exact decode GEMM (M <= 64), the default path for decode-sized M: the
+// streaming structure of decode_kernel (per-wave W rings of whole 128-byte
+// rows, no barrier per K block; X and scales in chunks shared by the waves),
+// with each 128-K block partial formed exactly: E4M3 bytes widened to FP16
+// (exact), products by the FP16 matrix instruction (a product of two E4M3
+// values has at most 8 significant bits and is exact in its FP32 sum), the
+// block partial summed in FP32 and promoted with sA*sB into the FP32
+// accumulator (DeepGEMM page, sections "细粒度缩放在 GEMM 层面引爆的两个问题"
+// and "主循环骨架": per-block partials in limited precision, promoted into a
+// full-precision accumulator).
+//   * Wave w owns 32 W rows (output columns) and all rows of X in MSUB 32-row
+//     subtiles: 32x32x16 FP16 MFMAs, W the A operand (lane l: column m = l%32
+//     of the result, rows n = 8(r/4) + 4(l/32) + r%4 of its 16 values), so a
+//     lane holds one sA per subtile and the wave's 32 rows share one sB.
+//   * K order inside a block: lane group h = l/32 takes bytes 64h .. 64h+63
+//     of its row, step s of the block bytes 64h + 8s .. +7, the same for both
+//     operands.
+//   * W: 4 KB per K block per wave (four DMAs of 8 whole rows), NS-stage ring,
+//     waits on the wave's own vector-memory counter only.
+//   * X, sA, sB: chunks of KBC K blocks, double-buffered, issued one chunk
+//     ahead by all waves together, one barrier per chunk (as decode_kernel).
+//     An X chunk is stored densely (KBC*128 bytes per row, every DMA lane
+//     carrying data) with chunk c of row r in slot c ^ (r mod 16): a fragment
+//     read of 16 rows at one logical chunk then covers all 64 banks once.
+// ---------------------------------------------------------------------------
+template <int MSUB, int NW, int NS, int KBC>
+struct DecodeExactLayout {
+    static constexpr int XSTRIDE = KBC * 128;              // LDS bytes per X row of a chunk
+    static constexpr int MR = 32 * MSUB;                   // X rows staged (rows past M read zeros)
+    static constexpr int XBYTES = MR * XSTRIDE;
+    static constexpr int NXL = XBYTES / 1024;              // 1 KB loads of an X chunk
+    static constexpr int NSA = (KBC * MR * 4 + 255) / 256; // dword loads of its sA
+    static constexpr int NT = NXL + NSA + 1;               // + one dword load of its sB
+    static constexpr int NPW = (NT + NW - 1) / NW;         // chunk loads per wave
+    static constexpr int X0 = 0;
+    static constexpr int SA0 = 2 * XBYTES;                 // sA [KBC][MR] floats, two buffers
+    static constexpr int SB0 = SA0 + 2 * NSA * 256;        // sB [2][KBC] floats, two buffers
+    static constexpr int W0 = SB0 + 2 * 256;               // W rings [wave][stage] 4 KB
+    static constexpr int SPARE = W0 + NW * NS * 4096;      // target of the surplus chunk loads
+    static constexpr int BYTES = SPARE + 1024;
+    static_assert(KBC >= 2 && XBYTES % 1024 == 0, "16 chunks per row at least; whole wave loads");
+    static_assert(2 * KBC <= 64, "one wave load holds the sB of two weight blocks");
+    static_assert(BYTES <= 160 * 1024, "LDS");
+};
+
+// Number of multiples of KBC in (q - D, q] for a position q = c*KBC + pos in
+// the steady state (c*KBC >= D): the X/scale chunk loads issued between the
+// W loads of K block q and its use.
+__host__ __device__ constexpr int chunks_between(int pos, int D, int KBC) {
+    return D > pos ? (D - pos + KBC - 1) / KBC : 0;
+}
+
+template <int MSUB, int NW, int NS, int KBC>
+__global__ __launch_bounds__(64 * NW, 1) void decode_exact_kernel(
+    const uint8_t* __restrict__ xq_, const float* __restrict__ sa_, const uint8_t* __restrict__ wq_,
+    const float* __restrict__ sb_, uint16_t* __restrict__ y_, GemmParams p) {
+    using L = DecodeExactLayout<MSUB, NW, NS, KBC>;
+    constexpr int D = NS - 1, NPW = L::NPW;
+    constexpr int CW = (D + KBC - 1) / KBC;             // chunks before the steady-state waits apply
+    static_assert(MSUB >= 1 && MSUB <= 2 && NW >= 1 && NS >= 2, "decode tile");
+    static_assert(4 * D + NPW * chunks_between(0, D, KBC) <= 63 && 4 * KBC <= 63, "vmcnt range");
+    constexpr int TN = 32 * NW;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int w = uniform(threadIdx.x >> 6);
+    const int r32 = lane & 31, h = lane >> 5;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int KB = (int)(K >> 7);
+    // Split K (grid.y > 1): this workgroup takes the chunks [cs0, cs0 + NC)
+    // of the K range and writes FP32 partial sums.
+    const int NCT = (KB + KBC - 1) / KBC;
+    const int cs0 = (int)(blockIdx.y * NCT / gridDim.y);
+    const int NC = (int)((blockIdx.y + 1) * NCT / gridDim.y) - cs0;
+    const int kq0 = cs0 * KBC;                          // first K block of this range
+    const int NQ = (KB - kq0 < NC * KBC) ? KB - kq0 : NC * KBC;   // K blocks in this range
+    const int64_t n0 = (int64_t)blockIdx.x * TN;
+    const int64_t nw = n0 + 32 * w;                     // this wave's first column
+    const uint32_t lds0 = lds_addr(smem);
+
+    const int64_t rows_w = N - n0 < TN ? N - n0 : TN;
+    const i32x4 wr = make_rsrc(wq_ + n0 * K, (uint32_t)(rows_w * K));
+    const i32x4 xr = make_rsrc(xq_, (uint32_t)(M * K));
+    const i32x4 sar = make_rsrc(sa_, (uint32_t)(KB * M * 4));
+    const int64_t nb0 = n0 >> 7, nb1 = (n0 + rows_w - 1) >> 7;
+    const i32x4 sbr = make_rsrc(sb_ + nb0 * KB, (uint32_t)((nb1 - nb0 + 1) * KB * 4));
+    const i32x4 none = make_rsrc(wq_, 0u);
+    constexpr uint32_t kFar = 0x7FFFFFF0u;
+
+    // ---- W: this wave's 32 rows, four 1 KB loads per K block ----
+    // load j, lane l: row 8j + l/8, LDS slot l%8 holding chunk (l%8) ^ lds_swz(row)
+    uint32_t wsrc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 8 * j + (lane >> 3);
+        wsrc[j] = (uint32_t)((32 * w + r) * K) + 16 * ((lane & 7) ^ lds_swz(r));
+    }
+    const uint32_t wring = lds0 + L::W0 + (uint32_t)w * NS * 4096;
+    auto issue_w = [&](int q) FP8K_INLINE {            // q: position in this range
+        const bool in = q < NQ;
+        const i32x4 rs = in ? wr : none;
+        const uint32_t dst = wring + (uint32_t)(q % NS) * 4096;
+        const uint32_t off = (uint32_t)(in ? kq0 + q : 0) * 128;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_lds16_one<0>(dst + 1024 * j, wsrc[j] + off, rs, 0);
+    };
+
+    // ---- X, sA, sB of local chunk c: NPW loads per wave, slot i = w + NW*t ----
+    auto issue_chunk = [&](int c) FP8K_INLINE {
+        const bool in = c < NC;
+        const int buf = c & 1;
+        const int k0 = (cs0 + c) * KBC * 128, kb0 = (cs0 + c) * KBC;
+#pragma unroll
+        for (int t = 0; t < NPW; ++t) {
+            const int i = w + NW * t;                   // wave-uniform
+            if (i < L::NXL) {
+                const int d = 1024 * i + 16 * lane;
+                const int r = d / L::XSTRIDE, j = (d - r * L::XSTRIDE) >> 4;
+                const int cc = j ^ (r & 15);
+                dma_lds16_one<0>(lds0 + L::X0 + buf * L::XBYTES + 1024 * i, (uint32_t)(r * K + k0 + 16 * cc),
+                                 in ? xr : none, 0);
+            } else if (i < L::NXL + L::NSA) {
+                const int f = 64 * (i - L::NXL) + lane;      // float f of the chunk's [KBC][MR] sA
+                const int kb = f / L::MR, m = f - kb * L::MR;
+                const uint32_t src = (in && kb < KBC && m < M) ? (uint32_t)(((kb0 + kb) * M + m) * 4) : kFar;
+                dma_lds4(lds0 + L::SA0 + buf * (L::NSA * 256) + 256 * (i - L::NXL), src, in ? sar : none, 0);
+            } else if (i < L::NT) {
+                // lane b*KBC + kb: sB of weight block nb0 + b, K block kb0 + kb
+                const int b = lane / KBC, kb = lane - b * KBC;
+                const uint32_t src = (in && b < 2) ? (uint32_t)((b * KB + kb0 + kb) * 4) : kFar;
+                dma_lds4(lds0 + L::SB0 + buf * 256, src, in ? sbr : none, 0);
+            } else {
+                dma_lds16_one<0>(lds0 + L::SPARE, kFar, none, 0);
+            }
+        }
+    };
+
+    // ---- fragments: lane (r32, h) reads logical chunks 4h .. 4h+3 of its row's block ----
+    const int sw = lds_swz(r32);
+    uint32_t fo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fo[j] = 16u * (uint32_t)((4 * h + j) ^ sw);
+    const int sbl = (int)((nw >> 7) - nb0);             // this wave's weight block in the chunk's sB
+    auto rd16 = [&](uint32_t off) FP8K_INLINE -> i32x4 { return *reinterpret_cast<const i32x4*>(smem + off); };
+
+    f32x16 acc[MSUB];
+#pragma unroll
+    for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[ms][r] = 0.f;
+
+    auto compute = [&](int q, int buf, int kbl) FP8K_INLINE {
+        const uint32_t ws = L::W0 + (uint32_t)w * NS * 4096 + (uint32_t)(q % NS) * 4096 + (uint32_t)r32 * 128;
+        i32x4 wv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wv[j] = rd16(ws + fo[j]);
+        // X row 32 ms + r32, logical chunk 8 kbl + 4h + j in slot (8 kbl + 4h + j) ^ (r32 mod 16)
+        const uint32_t xs = L::X0 + buf * L::XBYTES + (uint32_t)r32 * L::XSTRIDE;
+        i32x4 xv[MSUB][4];
+#pragma unroll
+        for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                xv[ms][j] = rd16(xs + 32 * ms * L::XSTRIDE + 16 * ((8 * kbl + 4 * h + j) ^ (r32 & 15)));
+        const float sbv = *reinterpret_cast<const float*>(smem + L::SB0 + buf * 256 + 4 * (sbl * KBC + kbl));
+        const float* sap = reinterpret_cast<const float*>(smem + L::SA0 + buf * (L::NSA * 256)) + kbl * L::MR + r32;
+        f32x16 part[MSUB];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int j = s >> 1, o = 2 * (s & 1);
+            const f16x8 a = e4m3x8_to_f16(wv[j][o], wv[j][o + 1]);
+#pragma unroll
+            for (int ms = 0; ms < MSUB; ++ms) {
+                const f16x8 b = e4m3x8_to_f16(xv[ms][j][o], xv[ms][j][o + 1]);
+                part[ms] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, s == 0 ? f32x16{} : part[ms], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int ms = 0; ms < MSUB; ++ms) {
+            const float f = sap[32 * ms] * sbv;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[ms][r] = __builtin_fmaf(f, part[ms][r], acc[ms][r]);
+        }
+    };
+
+    // ---- issue order and waits ----
+    // Position q (K block kq0 + q) of local chunk c = q / KBC: at the start of
+    // a chunk the wave waits for that chunk (issued one chunk earlier, before
+    // the KBC W blocks of the previous chunk: 4*KBC loads after it; chunk 0:
+    // the 4*D prologue W loads), a barrier publishes it and frees the other
+    // buffer, and the next chunk is issued.  Before K block q is used, the W
+    // blocks q+1 .. q+D (4 loads each) and the chunks issued at positions in
+    // (q-D, q] may still be in flight.  In the first CW chunks fewer chunk
+    // loads than that follow W block q, so the wait there counts W loads only
+    // (a stricter wait).
+    issue_chunk(0);
+#pragma unroll
+    for (int j = 0; j < D; ++j) issue_w(j);
+    for (int c = 0; c < NC; ++c) {
+        if (c == 0) wait_vmcnt<4 * D>();
+        else wait_vmcnt<4 * KBC>();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue_chunk(c + 1);
+        const bool steady = c >= CW;
+        static_for<KBC>([&](auto pc) FP8K_INLINE {
+            constexpr int pos = decltype(pc)::value;
+            const int q = c * KBC + pos;
+            // position q+D reuses the ring slot of position q-1: this wave's
+            // reads of it must have completed
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            issue_w(q + D);
+            if (steady) wait_vmcnt<4 * D + NPW * chunks_between(pos, D, KBC)>();
+            else wait_vmcnt<4 * D>();
+            asm volatile("" ::: "memory");
+            if (q < NQ) compute(q, c & 1, pos);
+        });
+    }
+    wait_vmcnt<0>();
+
+    // ---- stores: lane holds m = 32 ms + r32, n = nw + 8k + 4h + (0..3), k = 0..3 ----
+    float* part_base = p.part ? p.part + (int64_t)blockIdx.y * M * N : nullptr;
+#pragma unroll
+    for (int ms = 0; ms < MSUB; ++ms) {
+        const int64_t m = 32 * ms + r32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t n = nw + 8 * k + 4 * h;
+            if (n >= N) continue;
+            if (part_base) {
+                float* prow = part_base + m * N;
+                if ((N & 3) == 0 && n + 3 < N) {
+                    *reinterpret_cast<f32x4*>(prow + n) =
+                        f32x4{acc[ms][4 * k], acc[ms][4 * k + 1], acc[ms][4 * k + 2], acc[ms][4 * k + 3]};
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) prow[n + r] = acc[ms][4 * k + r];
+                }
+                continue;
+            }
+            uint16_t* yrow = y_ + m * N;
+            const uint32_t lo = pack_bf16x2(acc[ms][4 * k], acc[ms][4 * k + 1]);
+            const uint32_t hi = pack_bf16x2(acc[ms][4 * k + 2], acc[ms][4 * k + 3]);
+            if ((N & 3) == 0 && n + 3 < N) {
+                *reinterpret_cast<uint2*>(yrow + n) = make_uint2(lo, hi);
+            } else {
+                yrow[n] = (uint16_t)(lo & 0xFFFF);
+                if (n + 1 < N) yrow[n + 1] = (uint16_t)(lo >> 16);
+                if (n + 2 < N) yrow[n + 2] = (uint16_t)(hi & 0xFFFF);
+                if (n + 3 < N) yrow[n + 3] = (uint16_t)(hi >> 16);
+            }
+        }
+    }
+}
+
+}  // namespace fp8k
+
+namespace fp8k {
+
+// ---------------------------------------------------------------------------
+// Exact decode GEMM with X resident in LDS (M <= 64, a K range of at most
+// KBMAX blocks per workgroup): the same exact block partials and per-wave W
+// rings as decode_exact_kernel, but X, its scales and the weight scales of
+// the workgroup's K range are loaded once, before the K loop, so that the
+// loop holds no barrier and no chunk loads: per K block a wave issues the
+// four W loads D blocks ahead, waits for the block in hand and computes it.
+//   * Every workgroup reads the same X: each starts its X loads at a
+//     different 1 KB piece (rotated by its index), so that the workgroups of
+//     an XCD do not all ask the same L2 channel for the same lines at once.
+//   * X rows in LDS: stride XS = the range's bytes rounded to an odd multiple
+//     of 128, chunk c of a K block at slot c ^ lds_swz(row) inside its block
+//     (fragment reads of 16 rows at one logical chunk then hit distinct bank
+//     groups).
+//   * Split K (grid.y > 1): workgroup (t, s) takes K blocks
+//     [s*KB/S, (s+1)*KB/S) and writes FP32 partial sums [s][M][N].
+// ---------------------------------------------------------------------------
+template <int MSUB, int NW, int NS, int KBMAX>
+struct DecodeExactXLayout {
+    static constexpr int MR = 32 * MSUB;
+    static constexpr int XS_MAX = decode_stride(KBMAX * 128);
+    static constexpr int X0 = 0;
+    static constexpr int XBYTES = MR * XS_MAX;
+    static constexpr int SA0 = (XBYTES + 1023) / 1024 * 1024;  // sA [KBr][MR] floats
+    static constexpr int SA_BYTES = (KBMAX * MR * 4 + 255) / 256 * 256;
+    static constexpr int SB0 = SA0 + SA_BYTES;                 // sB [2][KBr] floats, one wave load
+    static constexpr int W0 = SB0 + 256;                       // W rings [wave][stage] 4 KB
+    static constexpr int BYTES = W0 + NW * NS * 4096;
+    static_assert(2 * KBMAX <= 64, "one wave load holds the sB of two weight blocks");
+    static_assert(BYTES <= 160 * 1024, "LDS");
+};
+
+template <int MSUB, int NW, int NS, int KBMAX>
+__global__ __launch_bounds__(64 * NW, 1) void decode_exact_x_kernel(
+    const uint8_t* __restrict__ xq_, const float* __restrict__ sa_, const uint8_t* __restrict__ wq_,
+    const float* __restrict__ sb_, uint16_t* __restrict__ y_, GemmParams p) {
+    using L = DecodeExactXLayout<MSUB, NW, NS, KBMAX>;
+    constexpr int D = NS - 1;
+    static_assert(MSUB >= 1 && MSUB <= 2 && NW >= 1 && NS >= 2 && 4 * D <= 63, "decode tile");
+    constexpr int TN = 32 * NW;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int w = uniform(threadIdx.x >> 6);
+    const int r32 = lane & 31, h = lane >> 5;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int KB = (int)(K >> 7);
+    const int kb0 = (int)(blockIdx.y * KB / gridDim.y);
+    const int NQ = (int)((blockIdx.y + 1) * KB / gridDim.y) - kb0;   // K blocks of this range (<= KBMAX)
+    const int xs = decode_stride(NQ * 128);              // LDS row stride of X
+    const int64_t n0 = (int64_t)blockIdx.x * TN;
+    const int64_t nw = n0 + 32 * w;
+    const uint32_t lds0 = lds_addr(smem);
+
+    const int64_t rows_w = N - n0 < TN ? N - n0 : TN;
+    const i32x4 wr = make_rsrc(wq_ + n0 * K, (uint32_t)(rows_w * K));
+    const i32x4 xr = make_rsrc(xq_, (uint32_t)(M * K));
+    const i32x4 sar = make_rsrc(sa_, (uint32_t)(KB * M * 4));
+    const int64_t nb0 = n0 >> 7, nb1 = (n0 + rows_w - 1) >> 7;
+    const i32x4 sbr = make_rsrc(sb_ + nb0 * KB, (uint32_t)((nb1 - nb0 + 1) * KB * 4));
+    const i32x4 none = make_rsrc(wq_, 0u);
+    constexpr uint32_t kFar = 0x7FFFFFF0u;
+
+    // ---- prologue: X rows [0, MR) x K blocks [kb0, kb0 + NQ), sA, sB (all waves) ----
+    {
+        const int nxl = L::MR * xs / 1024;               // whole 1 KB loads (MR*xs is a multiple of 1 KB)
+        const int nsa = (NQ * L::MR * 4 + 255) / 256;
+        const int ntot = nxl + nsa + 1;
+        const int rot = (int)(blockIdx.x % (unsigned)nxl);
+        for (int i = w; i < ntot; i += NW) {             // wave-uniform
+            if (i < nxl) {
+                const int ir = i + rot < nxl ? i + rot : i + rot - nxl;   // rotated 1 KB piece
+                const int d = 1024 * ir + 16 * lane;
+                const int r = d / xs, j = (d - r * xs) >> 4;
+                const int c = (j & ~7) | ((j & 7) ^ lds_swz(r));   // logical chunk in slot j
+                const uint32_t src = (16 * j < NQ * 128) ? (uint32_t)(r * K + kb0 * 128 + 16 * c) : kFar;
+                dma_lds16_one<0>(lds0 + L::X0 + 1024 * ir, src, xr, 0);
+            } else if (i < nxl + nsa) {
+                const int f = 64 * (i - nxl) + lane;     // float f of [NQ][MR]
+                const int kb = f / L::MR, m = f - kb * L::MR;
+                const uint32_t src = (kb < NQ && m < M) ? (uint32_t)(((kb0 + kb) * M + m) * 4) : kFar;
+                dma_lds4(lds0 + L::SA0 + 256 * (i - nxl), src, sar, 0);
+            } else {
+                // lane b*NQ + kb: sB of weight block nb0 + b, K block kb0 + kb
+                const int b = lane / NQ, kb = lane - b * NQ;
+                const uint32_t src = (b < 2) ? (uint32_t)((b * KB + kb0 + kb) * 4) : kFar;
+                dma_lds4(lds0 + L::SB0, src, sbr, 0);
+            }
+        }
+    }
+
+    // ---- W: this wave's 32 rows, four 1 KB loads per K block ----
+    // load j, lane l: row 8j + l/8, LDS slot l%8 holding chunk (l%8) ^ lds_swz(row)
+    uint32_t wsrc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 8 * j + (lane >> 3);
+        wsrc[j] = (uint32_t)((32 * w + r) * K) + 16 * ((lane & 7) ^ lds_swz(r));
+    }
+    const uint32_t wring = lds0 + L::W0 + (uint32_t)w * NS * 4096;
+    auto issue_w = [&](int q) FP8K_INLINE {
+        const bool in = q < NQ;
+        const i32x4 rs = in ? wr : none;
+        const uint32_t dst = wring + (uint32_t)(q % NS) * 4096;
+        const uint32_t off = (uint32_t)(in ? kb0 + q : 0) * 128;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_lds16_one<0>(dst + 1024 * j, wsrc[j] + off, rs, 0);
+    };
+#pragma unroll
+    for (int j = 0; j < D; ++j) issue_w(j);
+    // this wave's prologue loads are the ones before the 4*D W loads
+    wait_vmcnt<4 * D>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    const int sw = lds_swz(r32);
+    uint32_t fo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fo[j] = 16u * (uint32_t)((4 * h + j) ^ sw);
+    const int sbl = (int)((nw >> 7) - nb0);
+    const float* sat = reinterpret_cast<const float*>(smem + L::SA0);
+    const float* sbt = reinterpret_cast<const float*>(smem + L::SB0);
+    auto rd16 = [&](uint32_t off) FP8K_INLINE -> i32x4 { return *reinterpret_cast<const i32x4*>(smem + off); };
+
+    f32x16 acc[MSUB];
+#pragma unroll
+    for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[ms][r] = 0.f;
+
+    for (int q = 0; q < NQ; ++q) {
+        // block q+D reuses the ring slot of block q-1: its reads have completed
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue_w(q + D);
+        wait_vmcnt<4 * D>();
+        asm volatile("" ::: "memory");
+        const uint32_t wsl = L::W0 + (uint32_t)w * NS * 4096 + (uint32_t)(q % NS) * 4096 + (uint32_t)r32 * 128;
+        i32x4 wv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wv[j] = rd16(wsl + fo[j]);
+        const uint32_t xrow = L::X0 + (uint32_t)r32 * xs + 128 * q;
+        i32x4 xv[MSUB][4];
+#pragma unroll
+        for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xv[ms][j] = rd16(xrow + 32 * ms * xs + fo[j]);
+        const float sbv = sbt[sbl * NQ + q];
+        f32x16 part[MSUB];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int j = s >> 1, o = 2 * (s & 1);
+            const f16x8 a = e4m3x8_to_f16(wv[j][o], wv[j][o + 1]);
+#pragma unroll
+            for (int ms = 0; ms < MSUB; ++ms) {
+                const f16x8 b = e4m3x8_to_f16(xv[ms][j][o], xv[ms][j][o + 1]);
+                part[ms] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, s == 0 ? f32x16{} : part[ms], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int ms = 0; ms < MSUB; ++ms) {
+            const float f = sat[q * L::MR + 32 * ms + r32] * sbv;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[ms][r] = __builtin_fmaf(f, part[ms][r], acc[ms][r]);
+        }
+    }
+    wait_vmcnt<0>();
+
+    // ---- stores: lane holds m = 32 ms + r32, n = nw + 8k + 4h + (0..3), k = 0..3 ----
+    float* part_base = p.part ? p.part + (int64_t)blockIdx.y * M * N : nullptr;
+#pragma unroll
+    for (int ms = 0; ms < MSUB; ++ms) {
+        const int64_t m = 32 * ms + r32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t n = nw + 8 * k + 4 * h;
+            if (n >= N) continue;
+            if (part_base) {
+                float* prow = part_base + m * N;
+                if ((N & 3) == 0 && n + 3 < N) {
+                    *reinterpret_cast<f32x4*>(prow + n) =
+                        f32x4{acc[ms][4 * k], acc[ms][4 * k + 1], acc[ms][4 * k + 2], acc[ms][4 * k + 3]};
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) prow[n + r] = acc[ms][4 * k + r];
+                }
+                continue;
+            }
+            uint16_t* yrow = y_ + m * N;
+            const uint32_t lo = pack_bf16x2(acc[ms][4 * k], acc[ms][4 * k + 1]);
+            const uint32_t hi = pack_bf16x2(acc[ms][4 * k + 2], acc[ms][4 * k + 3]);
+            if ((N & 3) == 0 && n + 3 < N) {
+                *reinterpret_cast<uint2*>(yrow + n) = make_uint2(lo, hi);
+            } else {
+                yrow[n] = (uint16_t)(lo & 0xFFFF);
+                if (n + 1 < N) yrow[n + 1] = (uint16_t)(lo >> 16);
+                if (n + 2 < N) yrow[n + 2] = (uint16_t)(hi & 0xFFFF);
+                if (n + 3 < N) yrow[n + 3] = (uint16_t)(hi >> 16);
+            }
+        }
+    }
+}
+
+}  // namespace fp8k

@@ -128,11 +128,12 @@ fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq,
                        int64_t K, uint32_t flags, void* stream);
 
 /*
- * fp8_gemm_nt with a caller-owned device workspace.  With FP8_FLAG_FAST_ACCUM,
- * M <= 32 and fewer 96-column tiles than compute units, the decode kernel
- * splits K over up to 8 workgroups per tile when `workspace` holds their FP32
- * partial sums, and a second kernel adds them in split order (the same result
- * for the same split).  fp8_gemm_workspace_size() gives the bytes that enable
+ * fp8_gemm_nt with a caller-owned device workspace.  For decode-sized M (the
+ * default path: M <= 64; FP8_FLAG_FAST_ACCUM: M <= 32) and fewer 96-column
+ * tiles than compute units, the decode kernel splits K over up to 8
+ * workgroups per tile when `workspace` holds their FP32 partial sums, and a
+ * second kernel adds them in split order (the same result for the same
+ * split).  fp8_gemm_workspace_size() gives the bytes that enable
  * the split for a shape on the current device (0: no split).  With a smaller
  * or no workspace the GEMM runs unsplit.  The workspace is only read and
  * written by this call's kernels, in stream order; calls that overlap on one
@@ -147,7 +148,7 @@ fp8_status fp8_gemm_nt_ws(const uint8_t* xq, const float* sa, const uint8_t* wq,
 /*
  * fp8_gemm_nt for callers that cannot allocate (code under graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): fp8_gemm_nt_ws with
- * the split-K workspace taken from a fixed 4 MiB device array inside the
+ * the split-K workspace taken from a fixed 8 MiB device array inside the
  * library (one per GPU, loaded with the library, held until the process
  * ends) instead of the caller's memory.  Calls no hipMalloc, hipFree or
  * other allocating routine; the first call on a device looks up that
@@ -305,8 +306,10 @@ fp8_status fp8_gemm_nt_mx_w4(const uint8_t* xq, const uint32_t* ea,
 #define FP8_PLAN_QOUT 0x200u
 typedef struct {
     int32_t exact;          /* 1: exact partials (FP16 instruction); 0: FP8 instruction */
-    int32_t kernel;         /* 0: tile kernel; 1: decode kernel (M <= 32); 2: X-resident decode kernel */
-    int32_t tile_m, tile_n; /* workgroup tile of the main launch (decode kernels: 96 columns) */
+    int32_t kernel;         /* 0: tile kernel; 1: decode kernel (M <= 32); 2: X-resident decode kernel;
+                               3: exact decode kernel (M <= 64, X in chunks); 4: exact decode kernel
+                               with X resident (M <= 64, short K ranges) */
+    int32_t tile_m, tile_n; /* workgroup tile of the main launch (decode kernels: all M rows x tile_n columns) */
     int32_t waves;          /* waves per workgroup */
     int32_t grid;           /* workgroups of the main launch */
     int64_t tiles;          /* tiles of the main launch (decode kernels: workgroups) */

@@ -188,7 +188,12 @@ def test_plan_fills_whole_waves_on_the_prefill_shape(L):
     assert (f.exact, f.tile_m, f.tile_n, f.tiles, f.grid) == (0, 256, 224, 512, 256)
     e = _plan(0, 4096, 7168, 7168)
     assert (e.exact, e.tile_m, e.tile_n, e.tiles, e.waves) == (1, 256, 256, 448, 8)
-    assert _plan(0, 64, 24576, 1536).tile_n == 96 and _plan(0, 64, 24576, 1536).tiles == 256
+    d = _plan(0, 32, 24576, 1536)                   # exact decode kernel, X resident: 96 columns per workgroup
+    assert (d.exact, d.kernel, d.tile_n, d.tiles, d.grid) == (1, 4, 96, 256, 256)
+    d = _plan(0, 64, 24576, 1536)                   # unsplit, M > 32: the 64x96 tile
+    assert (d.kernel, d.tile_m, d.tile_n) == (0, 64, 96)
+    assert _plan(0, 32, 24576, 3072).kernel == 4 and _plan(0, 32, 24576, 3200).kernel == 3   # 25 blocks: chunks
+    assert _plan(0, 65, 24576, 1536).kernel == 0
     assert _plan(0, 16, 24576, 1536, fp8.FLAG_FAST_ACCUM).kernel == 1
     assert _plan(0, 40, 24576, 1536, fp8.FLAG_FAST_ACCUM).kernel == 2
     assert _plan(0, 4096, 7168, 7168, fp8.PLAN_MX).tile_n == 224
@@ -228,7 +233,20 @@ def test_plan_decode_split_and_workspace(L):
     assert p.k_splits == 8 and p.workspace_bytes == 8 * 16 * 2112 * 4 and p.tiles == 22 * 8
     p2 = _plan(0, 16, 2112, 7168, fp8.FLAG_FAST_ACCUM, ws=p.workspace_bytes - 1)
     assert p2.k_splits == 1
-    assert _plan(0, 16, 2112, 7168, 0, ws=big).k_splits == 1      # the exact path never splits
+    e = _plan(0, 16, 2112, 7168, 0, ws=big)       # exact decode kernel: 96-column tiles
+    assert (e.kernel, e.k_splits, e.tiles, e.workspace_bytes) == (4, 8, 22 * 8, 8 * 16 * 2112 * 4)
+    e = _plan(0, 64, 4096, 7168, 0, ws=big)       # 43 tiles: 256 // 43 = 5 splits of 11-12 blocks
+    assert (e.kernel, e.k_splits, e.workspace_bytes) == (4, 5, 5 * 64 * 4096 * 4)
+    e = _plan(0, 64, 4096, 7168, 0, ws=0)         # no workspace, M > 32: the 64x96 tile
+    assert (e.kernel, e.k_splits, e.workspace_bytes) == (0, 1, 0)
+    e = _plan(0, 16, 4096, 7168, 0, ws=0)         # no workspace, M <= 32: one range of 56 blocks, X in chunks
+    assert (e.kernel, e.k_splits, e.workspace_bytes) == (3, 1, 0)
+    e = _plan(0, 16, 2112, 32768, 0, ws=big)      # 8 ranges of 32 blocks: X in chunks, split
+    assert (e.kernel, e.k_splits) == (3, 8)
+    # the largest split a 256-CU device asks for fits the no-allocation entry point's 8 MiB
+    worst = max(_plan(0, 64, n, 7168, 0, ws=big).workspace_bytes for n in range(96, 96 * 129, 96))
+    assert 0 < worst <= 64 * 4 * 96 * 256 <= 8 << 20
+    assert _plan(0, 64, 24576, 1536, 0, ws=big).k_splits == 1     # 256 tiles: no split
 
 
 def test_plan_validation(L):

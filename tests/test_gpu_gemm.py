@@ -11,6 +11,8 @@ Two accumulation paths are tested:
 Bit-exact where the result is exactly representable (layout probes, small
 integers with power-of-two scales) on both paths.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -239,8 +241,11 @@ def test_decode_instance(M, N, K, ue8m0, fast):
     64x96 tile of the main kernel (one K block, ragged N, an N edge inside a
     tile, a single tile), as do K = 1792 and above.  These are the
     FP8-instruction kernels (FP8_FLAG_FAST_ACCUM, with a workspace for the
-    split); the default path takes its 64x96 tile for every M <= 64.  Every
-    element."""
+    split).  The default path takes its exact decode kernel: with X resident
+    in LDS for M <= 32, and split over K (a workspace comes with the call)
+    when the 96-column tiles are fewer than the CUs, each range holding at
+    most 24 K blocks (M <= 32) or 12 (M > 32), else with X in chunks; unsplit
+    with M > 32 it takes the 64x96 tile.  Every element."""
     flags = oracle.FLAG_UE8M0 if ue8m0 else 0
     wl = workloads.dense(M, N, K, seed=M * 31 + N + K, outlier_frac=0.01, outlier_mult=50.0)
     xq, sa = oracle.quant_1x128(wl.x, flags)
@@ -248,6 +253,34 @@ def test_decode_instance(M, N, K, ue8m0, fast):
     ref = oracle.gemm_nt(xq, sa, wq, sb, flags)
     y = run_gemm(xq, sa, wq, sb, ue8m0=ue8m0, fast=fast)
     say(f"stats {check(y, xq, sa, wq, sb, ref, fast, ue8m0=ue8m0, what=f'decode {M}x{N}x{K}')}")
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 7168), (32, 1000, 3200), (17, 777, 3328), (64, 130, 1664),
+                                   (1, 200, 1792), (40, 24700, 2048)])
+def test_exact_decode_without_workspace(M, N, K, ue8m0):
+    """The default path through fp8_gemm_nt, which passes no workspace: for
+    M <= 32 the exact decode kernel runs unsplit, X resident in LDS up to 24
+    K blocks and streamed in chunks of four K blocks beyond (partial last
+    chunks included); for 32 < M <= 64 the 64x96 tile of the main kernel.
+    Every element."""
+    L = fp8.load_library()
+    flags = oracle.FLAG_UE8M0 if ue8m0 else 0
+    plan = fp8.gemm_plan("dense", M, N, K, ue8m0=ue8m0)
+    assert plan["kernel"] == ((4 if K // 128 <= 24 else 3) if M <= 32 else 0) and plan["k_splits"] == 1
+    wl = workloads.dense(M, N, K, seed=M + N + K, outlier_frac=0.01, outlier_mult=50.0)
+    xq, sa = oracle.quant_1x128(wl.x, flags)
+    wq, sb = oracle.quant_128x128(wl.w, flags)
+    a = [dev(t) for t in (xq, sa, wq, sb)]
+    full, y = guarded((M, N))
+    say(f"fp8_gemm_nt (no workspace) M={M} N={N} K={K} ue8m0={ue8m0} kernel={plan['kernel']}")
+    st = L.fp8_gemm_nt(*[ctypes.c_void_p(t.data_ptr()) for t in a], ctypes.c_void_p(y.data_ptr()), M, N, K, flags,
+                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    check_guards(full, M * N)
+    ref = oracle.gemm_nt(xq, sa, wq, sb, flags)
+    say(f"stats {assert_close(bf16_bits(y), ref, f'no-workspace decode {M}x{N}x{K}')}")
 
 
 def test_decode_instance_deterministic():
