@@ -357,10 +357,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
                         gw[b] = e == 0 ? e4m3x8_to_f16(rw[b][2], rw[b][3]) : e4m3x8_to_f16(nw[b][0], nw[b][1]);
                     if constexpr (final) {
                         // factors into the next block's units: s_kb / s_kb+1.
-                        // A zero FP32 scale keeps the current units (factor
-                        // 1): the block it scales holds zero codes (an absmax
-                        // quantizer's all-zero group), so it adds nothing in
-                        // any units.  (Rows past the valid range read zero
+                        // A zero scale keeps the current units (factor 1, or
+                        // no exponent shift): the block it scales holds zero
+                        // codes (the contract of a zero scale), so it adds
+                        // nothing in any units.  (Rows past the valid range read zero
                         // scales too; they are never stored.)  After the last
                         // block the factor is 1.  Computed branch-free (the
                         // selects stay inside the MFMA schedule).
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
                             if constexpr (POW2) {
                                 int d = e8m0_of(sa_c[a]) - e8m0_of(sa_n[a]);
                                 asm volatile("" : "+v"(d));
-                                da[a] = last ? 0 : d;
+                                da[a] = (last || sa_n[a] == 0.f) ? 0 : d;
                             } else {
                                 float r = sa_c[a] * __builtin_amdgcn_rcpf(sa_n[a]);
                                 asm volatile("" : "+v"(r));
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
                             if constexpr (POW2) {
                                 int d = e8m0_of(sb_c[b]) - e8m0_of(sb_n[b]);
                                 asm volatile("" : "+v"(d));
-                                db[b] = last ? 0 : d;
+                                db[b] = (last || sb_n[b] == 0.f) ? 0 : d;
                             } else {
                                 float r = sb_c[b] * __builtin_amdgcn_rcpf(sb_n[b]);
                                 asm volatile("" : "+v"(r));
@@ -411,11 +411,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
 #pragma unroll
                 for (int b = 0; b < FJ; ++b) rw[b] = nw[b];
             });
-            // the next block's scales become current (a zero FP32 scale keeps the units)
+            // the next block's scales become current (a zero scale keeps the units)
 #pragma unroll
-            for (int a = 0; a < FI; ++a) sa_c[a] = (last || (!POW2 && sa_n[a] == 0.f)) ? sa_c[a] : sa_n[a];
+            for (int a = 0; a < FI; ++a) sa_c[a] = (last || sa_n[a] == 0.f) ? sa_c[a] : sa_n[a];
 #pragma unroll
-            for (int b = 0; b < FJ; ++b) sb_c[b] = (last || (!POW2 && sb_n[b] == 0.f)) ? sb_c[b] : sb_n[b];
+            for (int b = 0; b < FJ; ++b) sb_c[b] = (last || sb_n[b] == 0.f) ? sb_c[b] : sb_n[b];
         };
         int kb = 0;
         for (; kb + STAGES <= KB; kb += STAGES)

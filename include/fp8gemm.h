@@ -122,6 +122,11 @@ fp8_status fp8_quant_128x128(const float* w, int64_t N, int64_t K, uint8_t* wq,
  *   y  bf16 bits (M,N).
  * flags: FP8_FLAG_UE8M0, FP8_FLAG_FAST_ACCUM.  Uses the caller's buffers only
  * (equivalent to fp8_gemm_nt_ws with no workspace).
+ * Scales are finite and non-negative; a zero scale is taken to come with
+ * all-zero codes in its group (the quantizers never write one: their scales
+ * are at least 1e-4/448).  The default path keeps its accumulator in units
+ * of the current block's scale product and skips a zero factor, so nonzero
+ * codes under a zero scale are outside its contract.
  */
 fp8_status fp8_gemm_nt(const uint8_t* xq, const float* sa, const uint8_t* wq,
                        const float* sb, uint16_t* y, int64_t M, int64_t N,

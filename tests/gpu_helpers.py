@@ -103,8 +103,9 @@ def fp8_mfma_error_bound(xq, sa, wq, sb, ref, pow2: bool = False) -> np.ndarray:
     sa64 = sa.astype(np.float64)
     sb64 = sb.astype(np.float64)
     if pow2:
-        sa64 = np.exp2(np.floor(np.log2(sa64)))
-        sb64 = np.exp2(np.floor(np.log2(sb64)))
+        with np.errstate(divide="ignore"):          # a zero scale stays zero
+            sa64 = np.exp2(np.floor(np.log2(sa64)))
+            sb64 = np.exp2(np.floor(np.log2(sb64)))
     sa_g = np.repeat(sa64.T, 16, axis=1)                                   # (M, G)
     sb_g = np.repeat(np.repeat(sb64, 128, axis=0)[:N], 16, axis=1)         # (N, G)
     amax = np.abs(DEC[xq]).reshape(M, G, 8).max(axis=2) * sa_g

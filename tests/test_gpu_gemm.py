@@ -412,3 +412,31 @@ def test_split_decode_graph_replays():
         fp8.gemm_nt(*other, fast_accum=True)   # eager work on the default stream between replays
         torch.cuda.synchronize()
         assert np.array_equal(bf16_bits(y), eager), f"replay {i}"
+
+
+@pytest.mark.parametrize("fast", PATHS)
+@pytest.mark.parametrize("ue8m0", [False, True])
+@pytest.mark.parametrize("M,N,K", [(300, 384, 1024), (16, 1000, 1024), (64, 24700, 1024), (2048, 2048, 768)])
+def test_zero_scale_blocks(M, N, K, ue8m0, fast):
+    """A zero scale comes with all-zero codes in its group (the header's
+    contract): such groups, in the middle of K and at its ends, of X rows and
+    of W blocks, add nothing, on every kernel (main tiles, the decode
+    kernels).  The default path keeps its accumulator in units of the
+    current block's scale product and must skip the zero factor."""
+    flags = oracle.FLAG_UE8M0 if ue8m0 else 0
+    wl = workloads.dense(M, N, K, seed=M + N + 7, outlier_frac=0.01, outlier_mult=50.0)
+    xq, sa = oracle.quant_1x128(wl.x, flags)
+    wq, sb = oracle.quant_128x128(wl.w, flags)
+    rng = np.random.default_rng(M)
+    KB = K // 128
+    for kb in (0, KB // 2, KB - 1):
+        rows = rng.choice(M, size=max(1, M // 3), replace=False)
+        xq[rows, 128 * kb:128 * (kb + 1)] = 0
+        sa[kb, rows] = 0.0
+    nb = (N + 127) // 128
+    for kb, b in ((1, 0), (KB - 1, nb - 1)):
+        wq[128 * b:128 * (b + 1), 128 * kb:128 * (kb + 1)] = 0
+        sb[b, kb] = 0.0
+    ref = oracle.gemm_nt(xq, sa, wq, sb, flags)
+    y = run_gemm(xq, sa, wq, sb, ue8m0=ue8m0, fast=fast)
+    say(f"stats {check(y, xq, sa, wq, sb, ref, fast, ue8m0=ue8m0, what=f'zero scales {M}x{N}x{K}')}")
