@@ -390,26 +390,28 @@ def test_split_decode_workspace_and_streams():
             assert np.array_equal(bf16_bits(y), r)
 
 
-def test_split_decode_graph_replays():
-    """A split-K decode GEMM (FP8_FLAG_FAST_ACCUM, workspace from torch's graph
-    pool) captured in a graph: every replay, with eager work and
-    synchronizations between replays, equals the eager result bit for bit."""
+@pytest.mark.parametrize("fast", PATHS)
+def test_split_decode_graph_replays(fast):
+    """A split-K decode GEMM (both paths, workspace from torch's graph pool)
+    captured in a graph: every replay, with eager work and synchronizations
+    between replays, equals the eager result bit for bit."""
     o = _split_operands(43)
+    assert fp8.load_library().fp8_gemm_workspace_size(16, 2112, 7168, fp8.FLAG_FAST_ACCUM if fast else 0) > 0
     s = torch.cuda.Stream()
     y = torch.empty((16, 2112), dtype=torch.bfloat16, device="cuda")
     with torch.cuda.stream(s):
-        fp8.gemm_nt(*o, fast_accum=True, out=y)
+        fp8.gemm_nt(*o, fast_accum=fast, out=y)
     torch.cuda.synchronize()
     eager = bf16_bits(y)
     g = torch.cuda.CUDAGraph()
-    say("split decode: capture")
+    say(f"split decode: capture fast_accum={fast}")
     with torch.cuda.graph(g, stream=s):
-        fp8.gemm_nt(*o, fast_accum=True, out=y)
+        fp8.gemm_nt(*o, fast_accum=fast, out=y)
     other = _split_operands(44)
     for i in range(4):
         y.zero_()
         g.replay()
-        fp8.gemm_nt(*other, fast_accum=True)   # eager work on the default stream between replays
+        fp8.gemm_nt(*other, fast_accum=fast)   # eager work on the default stream between replays
         torch.cuda.synchronize()
         assert np.array_equal(bf16_bits(y), eager), f"replay {i}"
 
