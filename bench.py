@@ -263,88 +263,115 @@ def cpu_baseline(wl, target_s: float, mx: bool = False, w4: bool = False):
     }
 
 
+def _num(v):
+    if isinstance(v, (list, tuple)):
+        vals = [float(x) for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
+        return sum(vals) / len(vals) if vals else None
+    return float(v) if isinstance(v, (int, float)) and 0 <= v < 10000 else None
+
+
+def clock_sampler_main():
+    """`bench.py --clock-sampler`: a child process that reads the GPU's
+    graphics clock through amd-smi (it never opens the GPU for compute).
+    Waits for "start" on stdin, samples every 2 ms until "stop", then prints
+    one JSON object of samples."""
+    import select
+    out = {"samples": [], "error": None}
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        bdf = os.environ.get("FP8_BENCH_GPU_BDF", "")
+        h = handles[0] if handles else None
+        for hh in handles:
+            if bdf and amdsmi.amdsmi_get_gpu_device_bdf(hh).lower().startswith(bdf):
+                h = hh
+    except Exception as e:                      # monitoring is optional: report why it is missing
+        h, out["error"] = None, f"{type(e).__name__}: {e}"[:200]
+    sys.stdout.write("ready\n")
+    sys.stdout.flush()
+    if sys.stdin.readline().strip() != "start":
+        return
+    while True:
+        if select.select([sys.stdin], [], [], 0.002)[0]:
+            break
+        if h is None:
+            continue
+        smp = {"t": time.perf_counter()}
+        try:
+            info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)
+            smp["clk_info_mhz"] = _num(info.get("clk"))
+            smp["max_mhz"] = _num(info.get("max_clk"))
+        except Exception as e:
+            out["error"] = f"clock_info: {type(e).__name__}: {e}"[:200]
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            smp["current_gfxclks_mhz"] = _num(m.get("current_gfxclks"))
+            smp["current_gfxclk_mhz"] = _num(m.get("current_gfxclk"))
+            smp["average_gfxclk_mhz"] = _num(m.get("average_gfxclk_frequency"))
+            smp["gfx_activity_pct"] = _num(m.get("average_gfx_activity"))
+        except Exception as e:
+            out["error"] = f"gpu_metrics: {type(e).__name__}: {e}"[:200]
+        out["samples"].append(smp)
+    sys.stdout.write(json.dumps(out) + "\n")
+    sys.stdout.flush()
+
+
 class ClockSampler:
-    """The GPU's graphics clock read through amd-smi while work runs: the
-    clock-info reading and the metrics table (per-XCD current clocks, the
-    averaged clock and the graphics activity)."""
+    """The graphics clock read through amd-smi while work runs, from a child
+    process (`bench.py --clock-sampler`) started before this process touches
+    the GPU, so that neither the interpreter lock nor a fork after GPU
+    initialisation stands in the way."""
 
-    def __init__(self, torch_device):
+    def __init__(self):
+        import subprocess
         self.err = None
-        self.h = None
         try:
-            import amdsmi
-            self.amdsmi = amdsmi
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            self.h = handles[0] if handles else None
-            if len(handles) > 1:
-                import torch
-                p = torch.cuda.get_device_properties(torch_device)
-                want = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}"
-                for h in handles:
-                    if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want):
-                        self.h = h
-            if self.h is None:
-                self.err = "no GPU handle"
-        except Exception as e:          # monitoring is optional: report why it is missing
-            self.err = f"{type(e).__name__}: {e}"[:200]
-
-    @staticmethod
-    def _num(v):
-        if isinstance(v, (list, tuple)):
-            vals = [float(x) for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
-            return sum(vals) / len(vals) if vals else None
-        return float(v) if isinstance(v, (int, float)) and 0 <= v < 10000 else None
-
-    def _read(self):
-        a = self.amdsmi
-        out = {}
-        try:
-            info = a.amdsmi_get_clock_info(self.h, a.AmdSmiClkType.SYS)
-            out["clk_info_mhz"] = self._num(info.get("clk"))
-            out["max_mhz"] = self._num(info.get("max_clk"))
+            self.proc = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--clock-sampler"],
+                                         stdin=subprocess.PIPE, stdout=subprocess.PIPE, text=True)
+            if self.proc.stdout.readline().strip() != "ready":
+                raise RuntimeError("sampler did not start")
         except Exception as e:
-            self.err = f"clock_info: {type(e).__name__}: {e}"[:200]
-        try:
-            m = a.amdsmi_get_gpu_metrics_info(self.h)
-            out["current_gfxclks_mhz"] = self._num(m.get("current_gfxclks"))
-            out["current_gfxclk_mhz"] = self._num(m.get("current_gfxclk"))
-            out["average_gfxclk_mhz"] = self._num(m.get("average_gfxclk_frequency"))
-            out["gfx_activity_pct"] = self._num(m.get("average_gfx_activity"))
-        except Exception as e:
-            self.err = f"gpu_metrics: {type(e).__name__}: {e}"[:200]
-        return out
+            self.proc, self.err = None, f"{type(e).__name__}: {e}"[:200]
 
     def during(self, launch, n_launch, sync):
-        """Sample every 2 ms while n_launch back-to-back launches run; report
-        the medians over the samples taken while the graphics activity read
-        50% or more (all samples past the first quarter if it is missing)."""
-        if self.h is None:
+        """Sample while n_launch back-to-back launches run; report the medians
+        over the samples taken while the graphics activity read 50% or more
+        (all samples past the first quarter if it is missing)."""
+        if self.proc is None:
             return {"mhz": None, "error": self.err}
-        samples, stop = [], threading.Event()
-
-        def loop():
-            while not stop.is_set():
-                samples.append(self._read())
-                time.sleep(0.002)
-        t = threading.Thread(target=loop, daemon=True)
-        t.start()
-        for _ in range(n_launch):
-            launch()
-        sync()
-        stop.set()
-        t.join(timeout=5)
+        try:
+            self.proc.stdin.write("start\n")
+            self.proc.stdin.flush()
+            for _ in range(n_launch):
+                launch()
+            sync()
+            self.proc.stdin.write("stop\n")
+            self.proc.stdin.flush()
+            res = json.loads(self.proc.stdout.readline())
+            self.proc.wait(timeout=10)
+        except Exception as e:
+            return {"mhz": None, "error": f"{type(e).__name__}: {e}"[:200]}
+        samples = res["samples"]
         busy = [s for s in samples if (s.get("gfx_activity_pct") or 0) >= 50]
         use = busy or samples[len(samples) // 4:] or samples
-        res = {"samples": len(samples), "busy_samples": len(busy),
-               "source": "amd-smi, sampled every 2 ms", "error": self.err}
+        out = {"samples": len(samples), "busy_samples": len(busy),
+               "source": "amd-smi in a child process, sampled every 2 ms", "error": res.get("error")}
         for key in ("current_gfxclks_mhz", "current_gfxclk_mhz", "average_gfxclk_mhz", "clk_info_mhz",
                     "gfx_activity_pct", "max_mhz"):
             vals = [s[key] for s in use if s.get(key) is not None]
-            res[key] = stats(vals)["median"] if vals else None
-        res["mhz"] = next((res[k] for k in ("current_gfxclks_mhz", "current_gfxclk_mhz",
-                                             "average_gfxclk_mhz", "clk_info_mhz") if res[k]), None)
-        return res
+            out[key] = stats(vals)["median"] if vals else None
+        out["mhz"] = next((out[k] for k in ("current_gfxclks_mhz", "current_gfxclk_mhz",
+                                             "average_gfxclk_mhz", "clk_info_mhz") if out[k]), None)
+        return out
+
+    def close(self):
+        if self.proc is not None and self.proc.poll() is None:
+            try:
+                self.proc.stdin.close()
+                self.proc.wait(timeout=10)
+            except Exception:
+                self.proc.kill()
 
 
 def copy_calibration(n_bytes: int = 1 << 30, reps: int = 3):
@@ -516,7 +543,11 @@ def main():
                     help="MXFP8 activations with MXFP4 (E2M1) weights on a dense workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (scale for HBM byte counters)")
+    ap.add_argument("--clock-sampler", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.clock_sampler:
+        clock_sampler_main()
+        return
     if args.copy_calibration:
         copy_calibration()
         return
@@ -529,6 +560,9 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         print("--steps >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
+
+    # the clock sampler starts before this process touches the GPU
+    sampler = None if args.no_clock else ClockSampler()
 
     import numpy as np
     import torch
@@ -621,11 +655,11 @@ def main():
 
     # ---- GPU clock while the GEMM runs back to back (about half a second) ---
     clock = None
-    if not args.no_clock:
-        sampler = ClockSampler(dev)
+    if sampler is not None:
         n_clock = int(min(4000, max(50, 0.5e6 / max(per_kernel["gemm"]["mean"], 1.0))))
         clock = sampler.during(gemm, n_clock, torch.cuda.synchronize)
         clock["while"] = f"{n_clock} back-to-back launches of the {variant} GEMM on {wl.name}"
+        sampler.close()
 
     flops, nbytes, rows = prob.counts()
     gemm_s = per_kernel["gemm"]["mean"] / 1e6
