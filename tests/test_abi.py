@@ -278,3 +278,22 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 128)
     with pytest.raises(ValueError, match="GPU tensor"):
         fp8.quant_1x128(x)
+
+
+def test_library_imports_no_allocation_or_synchronization():
+    """The library allocates, frees and synchronizes nothing: none of the HIP
+    runtime's allocation, free, copy, fill or synchronization routines is
+    among the symbols it imports (read from the built shared object)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", fp8.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    hip = sorted(s for s in imported if s.startswith("hip"))
+    assert "hipLaunchKernel" in hip, hip
+    forbidden = ("Malloc", "Free", "Memcpy", "Memset", "Synchronize", "HostRegister", "MallocAsync")
+    bad = [s for s in hip if any(f in s for f in forbidden)]
+    assert not bad, bad
