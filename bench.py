@@ -273,25 +273,39 @@ def _num(v):
 def clock_sampler_main():
     """`bench.py --clock-sampler`: a child process that reads the GPU's
     graphics clock through amd-smi (it never opens the GPU for compute).
-    Waits for "start" on stdin, samples every 2 ms until "stop", then prints
-    one JSON object of samples."""
+    Waits for "start <PCI address>" on stdin, picks the amd-smi device with
+    that address (the host may show amd-smi more GPUs than the one this
+    benchmark runs on), samples every 2 ms until "stop", then prints one JSON
+    object of samples."""
     import select
-    out = {"samples": [], "error": None}
+    out = {"samples": [], "error": None, "bdf": None, "devices": 0}
     try:
         import amdsmi
         amdsmi.amdsmi_init()
         handles = amdsmi.amdsmi_get_processor_handles()
-        bdf = os.environ.get("FP8_BENCH_GPU_BDF", "")
-        h = handles[0] if handles else None
-        for hh in handles:
-            if bdf and amdsmi.amdsmi_get_gpu_device_bdf(hh).lower().startswith(bdf):
-                h = hh
+        out["devices"] = len(handles)
     except Exception as e:                      # monitoring is optional: report why it is missing
-        h, out["error"] = None, f"{type(e).__name__}: {e}"[:200]
+        handles, out["error"] = [], f"{type(e).__name__}: {e}"[:200]
     sys.stdout.write("ready\n")
     sys.stdout.flush()
-    if sys.stdin.readline().strip() != "start":
+    cmd = sys.stdin.readline().split()
+    if not cmd or cmd[0] != "start":
         return
+    want = cmd[1].lower() if len(cmd) > 1 else ""
+    h = None
+    try:
+        for hh in handles:
+            if want and amdsmi.amdsmi_get_gpu_device_bdf(hh).lower().startswith(want):
+                h = hh
+        if h is None and len(handles) == 1:
+            h = handles[0]
+        if h is not None:
+            out["bdf"] = amdsmi.amdsmi_get_gpu_device_bdf(h)
+        else:
+            seen = [amdsmi.amdsmi_get_gpu_device_bdf(hh) for hh in handles[:16]]
+            out["error"] = f"no amd-smi device at {want or '?'} among {seen}"[:200]
+    except Exception as e:
+        out["error"] = f"{type(e).__name__}: {e}"[:200]
     while True:
         if select.select([sys.stdin], [], [], 0.002)[0]:
             break
@@ -334,14 +348,15 @@ class ClockSampler:
         except Exception as e:
             self.proc, self.err = None, f"{type(e).__name__}: {e}"[:200]
 
-    def during(self, launch, n_launch, sync):
-        """Sample while n_launch back-to-back launches run; report the medians
-        over the samples taken while the graphics activity read 50% or more
-        (all samples past the first quarter if it is missing)."""
+    def during(self, launch, n_launch, sync, bdf=""):
+        """Sample while n_launch back-to-back launches run on the GPU at PCI
+        address bdf; report the medians over the samples taken while the
+        graphics activity read 50% or more (all samples past the first quarter
+        if it is missing)."""
         if self.proc is None:
             return {"mhz": None, "error": self.err}
         try:
-            self.proc.stdin.write("start\n")
+            self.proc.stdin.write(f"start {bdf}\n")
             self.proc.stdin.flush()
             for _ in range(n_launch):
                 launch()
@@ -355,7 +370,8 @@ class ClockSampler:
         samples = res["samples"]
         busy = [s for s in samples if (s.get("gfx_activity_pct") or 0) >= 50]
         use = busy or samples[len(samples) // 4:] or samples
-        out = {"samples": len(samples), "busy_samples": len(busy),
+        out = {"samples": len(samples), "busy_samples": len(busy), "bdf": res.get("bdf"),
+               "amd_smi_devices": res.get("devices"),
                "source": "amd-smi in a child process, sampled every 2 ms", "error": res.get("error")}
         for key in ("current_gfxclks_mhz", "current_gfxclk_mhz", "average_gfxclk_mhz", "clk_info_mhz",
                     "gfx_activity_pct", "max_mhz"):
@@ -657,7 +673,10 @@ def main():
     clock = None
     if sampler is not None:
         n_clock = int(min(4000, max(50, 0.5e6 / max(per_kernel["gemm"]["mean"], 1.0))))
-        clock = sampler.during(gemm, n_clock, torch.cuda.synchronize)
+        props = torch.cuda.get_device_properties(dev)
+        bdf = "{:04x}:{:02x}:{:02x}".format(getattr(props, "pci_domain_id", 0), getattr(props, "pci_bus_id", 0),
+                                            getattr(props, "pci_device_id", 0))
+        clock = sampler.during(gemm, n_clock, torch.cuda.synchronize, bdf)
         clock["while"] = f"{n_clock} back-to-back launches of the {variant} GEMM on {wl.name}"
         sampler.close()
 
