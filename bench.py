@@ -61,7 +61,7 @@ def kernel_source_sha() -> str:
     csrc = os.path.join(ROOT, "fine_grained_block_e4m3_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".h", ".hip")):
+        if name.endswith((".h", ".hip", ".inc")):
             with open(os.path.join(csrc, name), encoding="utf-8") as f:
                 src = f.read()
             src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)

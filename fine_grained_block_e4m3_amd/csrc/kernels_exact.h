@@ -51,6 +51,13 @@
 //     spread between the MFMA steps.
 //   * Persistent grid with the XCD-aware grouped raster order and the grouped
 //     tile walks of gemm_common.h.
+//   * Masked layout: one workgroup per possible tile (the hardware dispatcher
+//     balances tiles of unequal cost), and each wave multiplies only its
+//     32-row subtiles that hold valid rows (DeepGEMM page, "分组 GEMM 的两种
+//     布局": the masked layout computes the valid positions only), so a
+//     tile's cost follows its expert's count in steps of 32 rows.  The tile
+//     body (kernels_exact_tile.inc) is instantiated once per number of valid
+//     subtiles.
 #pragma once
 
 #include "gemm_common.h"
@@ -102,7 +109,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
-    const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+    // Wave rows and columns.  Masked layout: wave w takes row w / WAVES_N and
+    // column w % WAVES_N, so that with WAVES_N = 4 the two waves sharing a
+    // SIMD (w mod 4) own different rows; a tile whose valid rows end early
+    // then still gives every SIMD the same share of the multiplies.
+    const int wm = MODE == kMasked ? wave / WAVES_N : wave % WAVES_M;
+    const int wn = MODE == kMasked ? wave % WAVES_N : wave / WAVES_M;
     const int64_t K = p.K;
     const int KB = (int)(K / 128);
     const int64_t N = p.N;
@@ -124,7 +136,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
     const uint32_t qstep = uniform((int)(8 * NWAVES * K));
     // fragment addresses within a stage: row r of a subtile, logical chunk
     // 4h + pr at slot (4h + pr) ^ lds_swz(r); subtile and stage offsets are
-    // ds_read immediates (the swizzle depends on r mod 16 only)
+    // ds_read immediates (the swizzle depends on r mod 16 only).  Masked
+    // layout: set again per tile from the wave's first row and column there.
     uint32_t xa[NP], wa[NP];
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
@@ -132,7 +145,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
         xa[pr] = (uint32_t)((wm * TM + r32) * 128) + slot;
         wa[pr] = (uint32_t)(W_BASE + (wn * TN + r32) * 128) + slot;
     }
-    const uint32_t saa = (uint32_t)(SC_BASE + 4 * (wm * TM + r32));   // + 128*a per subtile
+    uint32_t saa = (uint32_t)(SC_BASE + 4 * (wm * TM + r32));   // + 128*a per subtile
     const bool sa_wave = wave < NSA;
     const uint32_t lds0 = uniform((int)lds_addr(smem));
     const uint32_t ldsw = lds0 + (uint32_t)(wave * 1024);
@@ -140,7 +153,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
     // XCD-aware order: workgroup b of a dispatch wave of G lands on XCD b%8;
     // each XCD gets a run of G/8 consecutive logical tiles.
     const int G = gridDim.x;
-    const bool remap = (G & 7) == 0;
+    // (Masked layout: one workgroup per possible tile, so the hardware
+    // dispatcher balances tiles of unequal cost; no remap.)
+    const bool remap = MODE != kMasked && (G & 7) == 0;
     const int rounds = (total_tiles + G - 1) / G;
 
     for (int round = 0; round < rounds; ++round) {
@@ -237,280 +252,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
             return *reinterpret_cast<const float*>(smem + buf * NWAVES * 256 + sb_slot[b]);
         };
 
-        f32x16 acc[FI][FJ];
-#pragma unroll
-        for (int a = 0; a < FI; ++a)
-#pragma unroll
-            for (int b = 0; b < FJ; ++b)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
-
-        // ---------------- K loop ----------------
-        // Prologue: blocks 0 .. STAGES-2 in full, all in flight together; once
-        // block 0 has landed for every wave, window position 0 of block
-        // STAGES-1; then the first reads of block 0.  (All waves are done with
-        // the previous tile's buffers at the first barrier.  No wait for the
-        // vector-memory counter before it: that counter also counts the
-        // previous tile's output stores.)
-        lds_barrier();
-        static_for<STAGES - 1>([&](auto sc) FP8K_INLINE {
-            constexpr int b = decltype(sc)::value;
-            issue_all(stage_loads(b, b));
-        });
-        wait_vmcnt<(STAGES - 2) * NPIECE>();
-        lds_barrier();
-        issue_window(stage_loads(STAGES - 1, STAGES - 1), std::integral_constant<int, 0>{});
-
-        i32x4 rx[FI], rw[FJ];          // raw E4M3 bytes of the current pair of steps
-#pragma unroll
-        for (int a = 0; a < FI; ++a) rx[a] = read_x(0, a, 0);
-#pragma unroll
-        for (int b = 0; b < FJ; ++b) rw[b] = read_w(0, b, 0);
-        // scales of the current block, and the rescale factors (exponent
-        // shifts for power-of-two scales) applied before its first MFMAs
-        // (the factor of subtile (a, b) is fa[a] * fb[b], or the shift da[a] + db[b])
-        float sa_c[FI], sb_c[FJ];
-        float fa[FI], fb[FJ];
-        int da[FI], db[FJ];
-#pragma unroll
-        for (int a = 0; a < FI; ++a) sa_c[a] = read_sa(0, a);
-#pragma unroll
-        for (int b = 0; b < FJ; ++b) sb_c[b] = read_sb(0, b);
-#pragma unroll
-        for (int a = 0; a < FI; ++a) {
-            fa[a] = 1.f;
-            da[a] = 0;
-        }
-#pragma unroll
-        for (int b = 0; b < FJ; ++b) {
-            fb[b] = 1.f;
-            db[b] = 0;
-        }
-
-        // operands of the current MFMA step, widened one step ahead of use
-        f16x8 hx[FI], hw[FJ];
-#pragma unroll
-        for (int a = 0; a < FI; ++a) hx[a] = e4m3x8_to_f16(rx[a][0], rx[a][1]);
-#pragma unroll
-        for (int b = 0; b < FJ; ++b) hw[b] = e4m3x8_to_f16(rw[b][0], rw[b][1]);
-
-        // Promotion into the next block's units, in the window between a
-        // subtile's last MFMA of one block and its first MFMA of the next:
-        // half of the subtiles in the block's last step, the other half in
-        // the next block's first step, each H = T/2 MFMAs away from the MFMAs
-        // on either side, so that the multiplies neither wait for an MFMA
-        // result nor hold up the next MFMA (3% on 4096x7168x7168 against
-        // rescaling right beside them).
-        auto rescale = [&](int a, int b, int v0) FP8K_INLINE {
-            const float f = fa[a] * fb[b];
-            const int d = da[a] + db[b];
-#pragma unroll
-            for (int v = v0; v < v0 + 8; ++v) {
-                if constexpr (POW2) acc[a][b][v] = __builtin_amdgcn_ldexpf(acc[a][b][v], d);
-                else acc[a][b][v] *= f;
-            }
-        };
-        auto block = [&](int kb, auto bufc) FP8K_INLINE {
-            constexpr int BUF = decltype(bufc)::value;
-            constexpr int NBUF = (BUF + 1) % STAGES;
-            // block kb+STAGES-1 (window positions 1 .. into its stage) and
-            // kb+STAGES (position 0, after this block's barrier, into BUF)
-            const StageLoads L1 = stage_loads(kb + STAGES - 1, (BUF + STAGES - 1) % STAGES);
-            const StageLoads L2 = stage_loads(kb + STAGES, BUF);
-            const bool last = kb + 1 >= KB;
-            float sa_n[FI], sb_n[FJ];
-            static_for<NP>([&](auto pc) FP8K_INLINE {
-                constexpr int pr = decltype(pc)::value;
-                __builtin_amdgcn_sched_barrier(0);
-                if constexpr (pr == RB) {
-                    // every read of block kb is done (lgkm) and this wave's
-                    // loads of block kb+1 have landed; then publish
-                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    wait_vmcnt<(STAGES - 2) * NPIECE>();
-                    lds_barrier();
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                // reads of the next pair: this block, or the next one after the barrier
-                constexpr int nbuf = pr + 1 < NP ? BUF : NBUF, npr = (pr + 1) % NP;
-                i32x4 nx[FI], nw[FJ];
-#pragma unroll
-                for (int a = 0; a < FI; ++a) nx[a] = read_x(nbuf, a, npr);
-#pragma unroll
-                for (int b = 0; b < FJ; ++b) nw[b] = read_w(nbuf, b, npr);
-                if constexpr (pr == NP - 1) {
-#pragma unroll
-                    for (int a = 0; a < FI; ++a) sa_n[a] = read_sa(NBUF, a);
-#pragma unroll
-                    for (int b = 0; b < FJ; ++b) sb_n[b] = read_sb(NBUF, b);
-                }
-                if constexpr (pr < RB) issue_window(L1, std::integral_constant<int, pr + 1>{});
-                else issue_window(L2, std::integral_constant<int, 0>{});
-
-                static_for<2>([&](auto ec) FP8K_INLINE {
-                    constexpr int e = decltype(ec)::value;
-                    constexpr bool first = pr == 0 && e == 0, final = pr == NP - 1 && e == 1;
-                    // operands of the following step: the second half of this
-                    // pair's reads, or the first half of the next pair's
-                    f16x8 gx[FI], gw[FJ];
-#pragma unroll
-                    for (int a = 0; a < FI; ++a)
-                        gx[a] = e == 0 ? e4m3x8_to_f16(rx[a][2], rx[a][3]) : e4m3x8_to_f16(nx[a][0], nx[a][1]);
-#pragma unroll
-                    for (int b = 0; b < FJ; ++b)
-                        gw[b] = e == 0 ? e4m3x8_to_f16(rw[b][2], rw[b][3]) : e4m3x8_to_f16(nw[b][0], nw[b][1]);
-                    if constexpr (final) {
-                        // factors into the next block's units: s_kb / s_kb+1.
-                        // A zero scale keeps the current units (factor 1, or
-                        // no exponent shift): the block it scales holds zero
-                        // codes (the contract of a zero scale), so it adds
-                        // nothing in any units.  (Rows past the valid range read zero
-                        // scales too; they are never stored.)  After the last
-                        // block the factor is 1.  Computed branch-free (the
-                        // selects stay inside the MFMA schedule).
-#pragma unroll
-                        for (int a = 0; a < FI; ++a) {
-                            if constexpr (POW2) {
-                                int d = e8m0_of(sa_c[a]) - e8m0_of(sa_n[a]);
-                                asm volatile("" : "+v"(d));
-                                da[a] = (last || sa_n[a] == 0.f) ? 0 : d;
-                            } else {
-                                float r = sa_c[a] * __builtin_amdgcn_rcpf(sa_n[a]);
-                                asm volatile("" : "+v"(r));
-                                fa[a] = (last || sa_n[a] == 0.f) ? 1.f : r;
-                            }
-                        }
-#pragma unroll
-                        for (int b = 0; b < FJ; ++b) {
-                            if constexpr (POW2) {
-                                int d = e8m0_of(sb_c[b]) - e8m0_of(sb_n[b]);
-                                asm volatile("" : "+v"(d));
-                                db[b] = (last || sb_n[b] == 0.f) ? 0 : d;
-                            } else {
-                                float r = sb_c[b] * __builtin_amdgcn_rcpf(sb_n[b]);
-                                asm volatile("" : "+v"(r));
-                                fb[b] = (last || sb_n[b] == 0.f) ? 1.f : r;
-                            }
-                        }
-                    }
-                    // subtile u < T-H: rescaled in the final step after MFMA u+H;
-                    // subtile u >= T-H: in the next block's first step after MFMA
-                    // u-(T-H), i.e. H MFMAs away from the MFMAs on either side
-                    constexpr int T = FI * FJ, H = T / 2;
-                    static_for<T>([&](auto tc) FP8K_INLINE {
-                        constexpr int t = decltype(tc)::value, a = t / FJ, b = t % FJ;
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hw[b], hx[a], acc[a][b], 0, 0, 0);
-                        if constexpr (final && t >= H) {
-                            rescale((t - H) / FJ, (t - H) % FJ, 0);
-                            rescale((t - H) / FJ, (t - H) % FJ, 8);
-                        }
-                        if constexpr (first && t < H) {
-                            rescale((t + T - H) / FJ, (t + T - H) % FJ, 0);
-                            rescale((t + T - H) / FJ, (t + T - H) % FJ, 8);
-                        }
-                    });
-                    // one MFMA, then its share of the VALU work
-                    static_for<FI * FJ>([&](auto) FP8K_INLINE {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, (first || final) ? 12 : 3, 0);
-                    });
-#pragma unroll
-                    for (int a = 0; a < FI; ++a) hx[a] = gx[a];
-#pragma unroll
-                    for (int b = 0; b < FJ; ++b) hw[b] = gw[b];
-                });
-#pragma unroll
-                for (int a = 0; a < FI; ++a) rx[a] = nx[a];
-#pragma unroll
-                for (int b = 0; b < FJ; ++b) rw[b] = nw[b];
+        // The tile's K loop, promotion and epilogue for FIV valid 32-row
+        // subtiles of this wave (masked layout: the subtiles past the
+        // expert's count are neither multiplied nor stored; every other
+        // layout: FIV = FI).  The loads and barriers are the same for every
+        // FIV, so the waves of a workgroup stay in step.
+        if constexpr (MODE == kMasked) {
+            auto tile_body = [&](auto fivc) FP8K_INLINE {
+                constexpr int FIV = decltype(fivc)::value;
+#include "kernels_exact_tile.inc"
+            };
+            const int fiv = uniform(min(max(rows_valid - wm * TM + 31, 0) / 32, FI));
+            static_for<FI + 1>([&](auto fc) FP8K_INLINE {
+                if (fiv == decltype(fc)::value) tile_body(fc);
             });
-            // the next block's scales become current (a zero scale keeps the units)
-#pragma unroll
-            for (int a = 0; a < FI; ++a) sa_c[a] = (last || sa_n[a] == 0.f) ? sa_c[a] : sa_n[a];
-#pragma unroll
-            for (int b = 0; b < FJ; ++b) sb_c[b] = (last || sb_n[b] == 0.f) ? sb_c[b] : sb_n[b];
-        };
-        int kb = 0;
-        for (; kb + STAGES <= KB; kb += STAGES)
-            static_for<STAGES>([&](auto sc) FP8K_INLINE { block(kb + decltype(sc)::value, sc); });
-        static_for<STAGES - 1>([&](auto sc) FP8K_INLINE {
-            if (kb + decltype(sc)::value < KB) block(kb + decltype(sc)::value, sc);
-        });
-        // (the loads issued past the last block were discarded; they retire in
-        // order before the next tile's loads, and the kernel's end waits for them)
-
-        // final promotion: out of units of the last block's scale product
-#pragma unroll
-        for (int a = 0; a < FI; ++a)
-#pragma unroll
-            for (int b = 0; b < FJ; ++b)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    if constexpr (POW2)
-                        acc[a][b][v] = __builtin_amdgcn_ldexpf(acc[a][b][v], e8m0_of(sa_c[a]) + e8m0_of(sb_c[b]) - 254);
-                    else
-                        acc[a][b][v] = (acc[a][b][v] * sa_c[a]) * sb_c[b];
-                }
-
-        // ---------------- epilogue ----------------
-        // lane l, value v of subtile (a, b): m = wave row + 32a + l%32,
-        // n = wave column + 32b + 8*(v/4) + 4*(l/32) + v%4
-        if constexpr (QOUT) {
-            // E4M3 codes and one scale per 1x128 group along N: the group of
-            // row m is this wave's 128 columns, held by lanes l and l^32
-            // (DeepGEMM page, section "为什么只做 NT 布局": the activation
-            // quantization belongs fused into the kernel that produces them)
-#pragma unroll
-            for (int a = 0; a < FI; ++a) {
-                const int mloc = wm * TM + 32 * a + r32;
-                float amax = 0.f;
-#pragma unroll
-                for (int b = 0; b < FJ; ++b)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(acc[a][b][v]));
-                amax = fmaxf(amax, __shfl_xor(amax, 32));
-                if (mloc >= rows_valid) continue;
-                const int64_t m = row0 + mloc;
-                const float s = group_scale(amax, POW2);
-#pragma unroll
-                for (int b = 0; b < FJ; ++b)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int64_t n = n0 + wn * TN + 32 * b + 8 * q + 4 * h;   // N % 128 == 0
-                        if (n < N)
-                            *reinterpret_cast<uint32_t*>(p.yq + m * N + n) =
-                                cvt_e4m3x4(acc[a][b][4 * q] / s, acc[a][b][4 * q + 1] / s,
-                                           acc[a][b][4 * q + 2] / s, acc[a][b][4 * q + 3] / s);
-                    }
-                const int64_t nw = n0 + wn * TN;
-                if (h == 0 && nw < N) p.sy[(nw >> 7) * p.M + m] = s;
-            }
-            continue;
-        }
-#pragma unroll
-        for (int a = 0; a < FI; ++a) {
-            const int mloc = wm * TM + 32 * a + r32;
-            const int64_t m = row0 + mloc;
-            bool ok = mloc < rows_valid;
-            if constexpr (MODE == kContiguous)
-                if (ok) ok = m_indices_[m] == expert;
-            if (!ok) continue;
-            uint16_t* yrow = y_ + m * N;
-#pragma unroll
-            for (int b = 0; b < FJ; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t n = n0 + wn * TN + 32 * b + 8 * q + 4 * h;
-                    const uint32_t lo = pack_bf16x2(acc[a][b][4 * q], acc[a][b][4 * q + 1]);
-                    const uint32_t hi = pack_bf16x2(acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
-                    if ((N & 3) == 0 && n + 3 < N) {
-                        *reinterpret_cast<uint2*>(yrow + n) = make_uint2(lo, hi);
-                    } else {
-                        if (n < N) yrow[n] = (uint16_t)(lo & 0xFFFF);
-                        if (n + 1 < N) yrow[n + 1] = (uint16_t)(lo >> 16);
-                        if (n + 2 < N) yrow[n + 2] = (uint16_t)(hi & 0xFFFF);
-                        if (n + 3 < N) yrow[n + 3] = (uint16_t)(hi >> 16);
-                    }
-                }
+        } else {
+            constexpr int FIV = FI;
+#include "kernels_exact_tile.inc"
         }
     }
     // the last stages issued were discarded loads; let them retire before the

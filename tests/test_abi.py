@@ -200,6 +200,19 @@ def test_plan_fills_whole_waves_on_the_prefill_shape(L):
     assert (_plan(0, 4096, 7168, 7168, fp8.PLAN_QOUT).tile_n, _plan(0, 128, 256, 512, fp8.PLAN_QOUT).tile_m) == (256, 128)
 
 
+def test_plan_masked_default_path_launches_one_workgroup_per_tile(L):
+    """Masked layout, default path: 256-row tiles of 8 waves, one workgroup
+    per possible tile of an expert (the kernel skips the subtiles past the
+    expert's count and the hardware dispatcher balances the unequal tiles);
+    the FP8-instruction path stays persistent."""
+    e = _plan(2, 256, 7168, 2048)
+    assert (e.exact, e.kernel, e.tile_m, e.tile_n, e.waves, e.tiles, e.grid) == (1, 0, 256, 256, 8, 28, 28)
+    e = _plan(2, 512, 7168, 2048, cus=16)
+    assert (e.tiles, e.grid) == (56, 56)
+    f = _plan(2, 256, 7168, 2048, fp8.FLAG_FAST_ACCUM, cus=16)
+    assert f.exact == 0 and f.grid == min(f.tiles, 16)
+
+
 @pytest.mark.parametrize("fast", [0, fp8.FLAG_FAST_ACCUM])
 @pytest.mark.parametrize("M", [128, 8704, 9216, 1088 * 128 // 16, 33 * 128, 256 * 128 + 128])
 def test_plan_contiguous_launches_cover_every_row_once(L, M, fast):
