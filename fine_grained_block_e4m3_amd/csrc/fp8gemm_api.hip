@@ -97,13 +97,15 @@ fp8_status launch_status() {
 // A persistent launch of `kern` over the tiles of BM x BN: one workgroup per
 // compute unit, at most one per tile.  Dense/contiguous: tiles over rows
 // [p.m_lo, m_hi) (all rows by default).
-// persistent = false: one workgroup per possible tile instead.
+// Dense: columns [p.n_lo, n_hi) (all columns by default).  persistent =
+// false: one workgroup per possible tile instead.
 template <int BM, int BN, int MODE, typename Kernel>
 fp8_status launch_tiles(Kernel kern, int threads, fp8k::GemmParams p, int group_m, int cus,
-                        hipStream_t stream, int64_t m_hi, bool persistent = true) {
+                        hipStream_t stream, int64_t m_hi, bool persistent = true, int64_t n_hi = -1) {
     if (m_hi < 0) m_hi = p.M;
+    if (n_hi < 0) n_hi = p.N;
     p.m_tiles = (int)((MODE == fp8k::kMasked ? p.max_m : m_hi - p.m_lo) + BM - 1) / BM;
-    p.n_tiles = (int)((p.N + BN - 1) / BN);
+    p.n_tiles = (int)((n_hi - p.n_lo + BN - 1) / BN);
     p.group_m = group_m;
     int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
     if (MODE == fp8k::kMasked) tiles *= p.E;   // upper bound; the kernel counts the real ones
@@ -124,12 +126,13 @@ fp8_status launch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream, i
 
 // The exact-partial kernel (the default path).
 template <int BM, int BN, int WM, int WN, int MODE, bool POW2, int STAGES, bool QOUT = false>
-fp8_status launch_exact(const fp8k::GemmParams& p, int cus, hipStream_t stream, int64_t m_hi = -1) {
+fp8_status launch_exact(const fp8k::GemmParams& p, int cus, hipStream_t stream, int64_t m_hi = -1,
+                        int64_t n_hi = -1) {
     // masked: the tiles' costs follow the experts' counts (the kernel skips
     // the subtiles past them), so one workgroup per possible tile and the
     // hardware dispatcher balances them
     return launch_tiles<BM, BN, MODE>(fp8k::gemm_exact_kernel<BM, BN, WM, WN, MODE, POW2, STAGES, QOUT>,
-                                      64 * WM * WN, p, 4, cus, stream, m_hi, MODE != fp8k::kMasked);
+                                      64 * WM * WN, p, 4, cus, stream, m_hi, MODE != fp8k::kMasked, n_hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -144,7 +147,8 @@ enum Inst : int {
     kFastDecode, kFastDecodeKx, kFast64x96, kFast256x224, kFast256x256, kFast256x128, kFast128x128,
     kFast128x256, kFast128x64,
     // exact-partial kernel (default)
-    kExact64x96, kExact256x256, kExact128x256, kExact128x128, kExact128x64, kExactQ256x256, kExactQ128x256,
+    kExact64x96, kExact256x256, kExact256x192, kExact128x256, kExact128x128, kExact128x64, kExactQ256x256,
+    kExactQ128x256,
     kExactDecode, kExactDecodeX,
 };
 
@@ -171,6 +175,7 @@ InstInfo inst_info(Inst i) {
         case kFast128x64: return {128, 64, 8, 0, 0};
         case kExact64x96: return {64, 96, 6, 0, 1};
         case kExact256x256: return {256, 256, 8, 0, 1};
+        case kExact256x192: return {256, 192, 8, 0, 1};
         case kExact128x256: return {128, 256, 8, 0, 1};
         case kExact128x128: return {128, 128, 4, 0, 1};
         case kExact128x64: return {128, 64, 8, 0, 1};
@@ -202,8 +207,10 @@ int64_t decode_splits(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes,
 struct Plan {
     Inst main;
     int64_t main_rows;      // contiguous: the main launch covers rows [0, main_rows)
-    Inst tail;              // contiguous: the launch over [main_rows, M), if main_rows < M
+    Inst tail;              // contiguous: the launch over [main_rows, M), if main_rows < M;
+                            // dense: the launch over columns [main_cols, N), if main_cols > 0
     int64_t k_splits;       // decode kernel
+    int64_t main_cols = 0;  // dense, > 0: the main launch covers columns [0, main_cols)
 };
 
 // The FP8-instruction paths.  Compute-bound shapes use 8 waves (2 per SIMD)
@@ -283,6 +290,27 @@ Plan plan_fast(int mode, int64_t M, int64_t N, int64_t K, bool mx, bool qout, in
 
 // The exact-partial path (FP16 matrix instruction on E4M3 operands widened
 // exactly).  Waves hold 64x128 (or 64x64) of 32x32 subtiles.
+// Dense, 256-row tiles: the columns [0, c) in 256x256 tiles and the rest in
+// 256x192 tiles, as two launches, when that takes fewer rounds' worth of tile
+// width than 256x256 tiles throughout (the round time of a launch taken as
+// proportional to its tile width).  4096 x 7168 on 256 CUs: 448 tiles of 256
+// are 1.75 rounds, so the second round leaves a quarter of the CUs idle;
+// columns [0, 4096) as 256 tiles of 256 and [4096, 7168) as 256 tiles of 192
+// are one round each (the DeepGEMM page, section "非对齐块大小", makes the same
+// trade with 112-column blocks).  Returns c, or 0 to keep one launch.
+int64_t exact_split_cols(int64_t M, int64_t N, int cus) {
+    const int64_t mt = cdiv(M, 256), nt = cdiv(N, 256);
+    int64_t best = cdiv(mt * nt, cus) * 256, cols = 0;
+    for (int64_t j = 1; j < nt; ++j) {
+        const int64_t w = cdiv(mt * j, cus) * 256 + cdiv(mt * cdiv(N - 256 * j, 192), cus) * 192;
+        if (w < best || (cols > 0 && w == best)) {   // ties: the most columns in 256x256 tiles
+            best = w;
+            cols = 256 * j;
+        }
+    }
+    return cols;
+}
+
 Plan plan_exact(int mode, int64_t M, int64_t N, int64_t K, bool qout, int cus, size_t ws_bytes) {
     Plan pl{kExact128x128, M, kExact128x128, 1};
     if (mode == fp8k::kDense) {
@@ -311,6 +339,8 @@ Plan plan_exact(int mode, int64_t M, int64_t N, int64_t K, bool qout, int cus, s
             }
         } else if (cdiv(M, 256) * cdiv(N, 256) >= cus) {
             pl.main = kExact256x256;
+            pl.main_cols = exact_split_cols(M, N, cus);
+            if (pl.main_cols > 0) pl.tail = kExact256x192;
         } else if (cdiv(M, 128) * cdiv(N, 256) >= cus) {
             pl.main = kExact128x256;
         } else {
@@ -492,11 +522,12 @@ fp8_status launch_decode_exact_x(const fp8k::GemmParams& p0, int64_t splits, voi
 
 template <int MODE, bool POW2>
 fp8_status launch_exact_inst(Inst i, const fp8k::GemmParams& p, int64_t splits, void* ws, int cus,
-                             hipStream_t stream, int64_t m_hi) {
+                             hipStream_t stream, int64_t m_hi, int64_t n_hi = -1) {
     if constexpr (MODE == fp8k::kDense) {
         switch (i) {
             case kExact64x96: return launch_exact<64, 96, 2, 3, MODE, POW2, 3>(p, cus, stream);
-            case kExact256x256: return launch_exact<256, 256, 4, 2, MODE, POW2, 2>(p, cus, stream);
+            case kExact256x256: return launch_exact<256, 256, 4, 2, MODE, POW2, 2>(p, cus, stream, -1, n_hi);
+            case kExact256x192: return launch_exact<256, 192, 4, 2, MODE, POW2, 2>(p, cus, stream);
             case kExact128x256: return launch_exact<128, 256, 2, 4, MODE, POW2, 3>(p, cus, stream);
             case kExact128x128: return launch_exact<128, 128, 2, 2, MODE, POW2, 4>(p, cus, stream);
             case kExactQ256x256: return launch_exact<256, 256, 4, 2, MODE, POW2, 2, true>(p, cus, stream);
@@ -531,6 +562,14 @@ fp8_status run_plan(const Plan& pl, bool exact, const fp8k::GemmParams& p, void*
         return exact ? launch_exact_inst<MODE, kPow2>(i, q, pl.k_splits, ws, cus, stream, m_hi)
                      : launch_fast<MODE, PATH>(i, q, pl.k_splits, ws, cus, stream, m_hi, qout);
     };
+    if (MODE == fp8k::kDense && exact && pl.main_cols > 0 && pl.main_cols < p.N) {
+        // columns [0, main_cols), then [main_cols, N) with the narrower tile
+        fp8_status st = launch_exact_inst<MODE, kPow2>(pl.main, p, 1, ws, cus, stream, -1, pl.main_cols);
+        if (st != FP8_OK) return st;
+        fp8k::GemmParams t = p;
+        t.n_lo = pl.main_cols;
+        return one(pl.tail, t, -1);
+    }
     if (MODE == fp8k::kContiguous && pl.main_rows < p.M) {
         fp8_status st = one(pl.main, p, pl.main_rows);
         if (st != FP8_OK) return st;
@@ -774,6 +813,7 @@ fp8_status fp8_gemm_plan(int32_t layout, int64_t M, int64_t N, int64_t K, uint32
     plan->tile_n = a.bn;
     plan->waves = a.waves;
     plan->main_rows = layout == 1 ? pl.main_rows : M;
+    plan->main_cols = layout == 0 && pl.main_cols > 0 ? pl.main_cols : N;
     plan->k_splits = (int32_t)pl.k_splits;
     plan->workspace_bytes = pl.k_splits > 1 ? decode_ws_bytes(pl.k_splits, M, N) : 0;
     if (a.kernel != 0) {
@@ -781,7 +821,8 @@ fp8_status fp8_gemm_plan(int32_t layout, int64_t M, int64_t N, int64_t K, uint32
         plan->grid = (int32_t)plan->tiles;
     } else {
         const int64_t rows = layout == 1 ? pl.main_rows : M;
-        plan->tiles = cdiv(rows, a.bm) * cdiv(N, a.bn);
+        const int64_t cols = layout == 0 && pl.main_cols > 0 ? pl.main_cols : N;
+        plan->tiles = cdiv(rows, a.bm) * cdiv(cols, a.bn);
         // the exact masked launch has one workgroup per possible tile
         const bool per_tile = layout == 2 && a.exact;
         plan->grid = (int32_t)(plan->tiles < compute_units || per_tile ? plan->tiles : compute_units);
@@ -791,6 +832,12 @@ fp8_status fp8_gemm_plan(int32_t layout, int64_t M, int64_t N, int64_t K, uint32
         plan->tail_tile_m = t.bm;
         plan->tail_tile_n = t.bn;
         plan->tail_tiles = cdiv(M - pl.main_rows, t.bm) * cdiv(N, t.bn);
+    }
+    if (layout == 0 && pl.main_cols > 0 && pl.main_cols < N) {
+        const InstInfo t = inst_info(pl.tail);
+        plan->tail_tile_m = t.bm;
+        plan->tail_tile_n = t.bn;
+        plan->tail_tiles = cdiv(M, t.bm) * cdiv(N - pl.main_cols, t.bn);
     }
     return FP8_OK;
 }

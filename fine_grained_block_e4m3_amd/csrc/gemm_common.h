@@ -35,6 +35,7 @@ struct GemmParams {
     int64_t max_m;              // masked only
     int32_t E;
     int64_t m_lo;               // dense/contiguous: tiles cover rows [m_lo, m_lo + m_tiles*BM)
+    int64_t n_lo;               // dense: tiles cover columns [n_lo, n_lo + n_tiles*BN) (else 0)
     int32_t m_tiles;            // dense/contiguous: ceil((rows to cover)/BM); masked: ceil(max_m/BM)
     int32_t n_tiles;            // ceil(N/BN)
     int32_t group_m;            // raster group height in tiles
@@ -194,7 +195,7 @@ __device__ __forceinline__ bool decode_tile(int t, const GemmParams& p, const in
             tc.expert = e;
         }
     }
-    tc.n0 = (int64_t)nt * BN;
+    tc.n0 = p.n_lo + (int64_t)nt * BN;
     return true;
 }
 

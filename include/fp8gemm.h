@@ -321,10 +321,12 @@ typedef struct {
     int32_t grid;           /* workgroups of the main launch */
     int64_t tiles;          /* tiles of the main launch (decode kernels: workgroups) */
     int64_t main_rows;      /* rows [0, main_rows) in the main launch (contiguous); else M */
-    int32_t tail_tile_m, tail_tile_n; /* contiguous: tile of a second launch over [main_rows, M), or 0 */
+    int32_t tail_tile_m, tail_tile_n; /* tile of a second launch, or 0: contiguous, over rows
+                               [main_rows, M); dense, over columns [main_cols, N) */
     int64_t tail_tiles;
     int32_t k_splits;       /* decode kernel: workgroups along K per tile */
     size_t workspace_bytes; /* workspace the split uses */
+    int64_t main_cols;      /* columns [0, main_cols) in the main launch (dense); else N */
 } fp8_gemm_plan_t;
 fp8_status fp8_gemm_plan(int32_t layout, int64_t M, int64_t N, int64_t K,
                          uint32_t flags, int32_t compute_units,

@@ -182,12 +182,15 @@ def test_plan_pins_the_pages_unaligned_block_example(L):
 def test_plan_fills_whole_waves_on_the_prefill_shape(L):
     """4096x7168 on 256 CUs: 256x256 tiles are 448 = 1.75 waves; the FP8
     planner takes 256x224 (512 tiles = 2 whole waves, the same trade as the
-    page's 112-wide blocks); the exact path keeps 256x256 (its 32x32 subtiles
-    do not split 224 columns over two waves)."""
+    page's 112-wide blocks); the exact path (whose 32x32 subtiles do not
+    split 224 columns over two waves) runs the columns [0, 4096) as 256 tiles
+    of 256 and [4096, 7168) as 256 tiles of 192: one whole wave each."""
     f = _plan(0, 4096, 7168, 7168, fp8.FLAG_FAST_ACCUM)
     assert (f.exact, f.tile_m, f.tile_n, f.tiles, f.grid) == (0, 256, 224, 512, 256)
     e = _plan(0, 4096, 7168, 7168)
-    assert (e.exact, e.tile_m, e.tile_n, e.tiles, e.waves) == (1, 256, 256, 448, 8)
+    assert (e.exact, e.tile_m, e.tile_n, e.tiles, e.waves, e.grid) == (1, 256, 256, 256, 8, 256)
+    assert (e.main_cols, e.tail_tile_m, e.tail_tile_n, e.tail_tiles) == (4096, 256, 192, 256)
+    assert e.main_cols + 192 * (e.tail_tiles // 16) == 7168          # the two launches tile [0, N) once
     d = _plan(0, 32, 24576, 1536)                   # exact decode kernel, X resident: 96 columns per workgroup
     assert (d.exact, d.kernel, d.tile_n, d.tiles, d.grid) == (1, 4, 96, 256, 256)
     d = _plan(0, 64, 24576, 1536)                   # unsplit, M > 32: the 64x96 tile
@@ -198,6 +201,32 @@ def test_plan_fills_whole_waves_on_the_prefill_shape(L):
     assert _plan(0, 40, 24576, 1536, fp8.FLAG_FAST_ACCUM).kernel == 2
     assert _plan(0, 4096, 7168, 7168, fp8.PLAN_MX).tile_n == 224
     assert (_plan(0, 4096, 7168, 7168, fp8.PLAN_QOUT).tile_n, _plan(0, 128, 256, 512, fp8.PLAN_QOUT).tile_m) == (256, 128)
+
+
+def test_plan_exact_column_split_rule(L):
+    """The default path's column split: only when the two launches take fewer
+    rounds' worth of tile width than 256x256 tiles throughout; the main
+    launch covers whole 256-column tiles, the tail the rest of [0, N)."""
+    def rounds_width(M, N, cus, cols):
+        mt = -(-M // 256)
+        if cols == 0:
+            return -(-mt * -(-N // 256) // cus) * 256
+        return -(-mt * (cols // 256) // cus) * 256 + -(-mt * -(-(N - cols) // 192) // cus) * 192
+    for M, N, cus in [(4096, 7168, 256), (1900, 8102, 256), (2500, 7050, 256), (4096, 4096, 256),
+                      (8192, 7168, 256), (4096, 7168, 304), (3000, 5000, 128)]:
+        p = _plan(0, M, N, 7168, cus=cus)
+        if p.tile_m != 256 or p.exact != 1:
+            continue
+        cols = p.main_cols if p.main_cols < N else 0
+        assert cols % 256 == 0 and cols < N
+        best = min(rounds_width(M, N, cus, c) for c in range(0, N, 256))
+        assert rounds_width(M, N, cus, cols) == best
+        if cols:
+            assert (p.tail_tile_n, p.tail_tiles) == (192, -(-M // 256) * -(-(N - cols) // 192))
+        else:
+            assert p.tail_tiles == 0
+    assert _plan(0, 1900, 8102, 640).main_cols == 8102       # one whole wave already: no split
+    assert _plan(0, 2500, 7050, 640).main_cols == 6400       # 250 + 40 tiles: one wave each
 
 
 def test_plan_masked_default_path_launches_one_workgroup_per_tile(L):

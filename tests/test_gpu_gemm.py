@@ -199,10 +199,11 @@ def test_huge_tile_instance_ragged_sampled(ue8m0, fast):
 def test_224_wide_tile_instance_ragged_sampled(ue8m0, fast):
     """Shapes that fill whole waves with 256x224 tiles but not with 256x256
     ones take the 256x224 instance on the FP8-instruction path, which holds X
-    in registers and streams the W subtiles (the default path: 256x256): here
-    10 x 32 tiles, the last n tile holding 106 columns that straddle two
-    weight blocks, a ragged last m tile and an odd number of K blocks; every
-    row and column of the ragged edges is checked."""
+    in registers and streams the W subtiles: here 10 x 32 tiles, the last n
+    tile holding 106 columns that straddle two weight blocks, a ragged last m
+    tile and an odd number of K blocks.  The default path splits the columns:
+    [0, 6400) in 256x256 tiles, [6400, 7050) in 256x192 tiles whose last one
+    holds 74 columns.  Every row and column of the ragged edges is checked."""
     M, N, K = 2500, 7050, 640
     flags = oracle.FLAG_UE8M0 if ue8m0 else 0
     wl = workloads.dense(M, N, K, seed=17, outlier_frac=0.001, outlier_mult=100.0)
