@@ -510,6 +510,26 @@ def time_batched(fn, reps, stream):
     return a.elapsed_time(b) / reps
 
 
+def launch_plan(prob, fast):
+    """The kernel launches one GEMM call of the workload makes (the library's
+    host-side plan): the timed figures cover all of them."""
+    import torch
+    wl = prob.wl
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    M = wl.max_m if wl.kind == "masked" else prob.M
+    pl = prob.fp8.gemm_plan(wl.kind, M, wl.N, prob.K, ue8m0=wl.ue8m0, fast_accum=fast,
+                            mx=prob.mx, compute_units=cus)
+    kind = {0: "tile", 1: "decode", 2: "decode_x", 3: "exact_decode", 4: "exact_decode_x"}[pl["kernel"]]
+    out = {"launches": 1, "main": f"{kind} {pl['tile_m']}x{pl['tile_n']}, {pl['tiles']} tiles, grid {pl['grid']}"
+                                   + (" per expert" if wl.kind == "masked" else "")}
+    if pl["tail_tiles"]:
+        out["launches"] = 2
+        where = (f"rows [{pl['main_rows']}, {prob.M})" if wl.kind == "contiguous"
+                 else f"columns [{pl['main_cols']}, {wl.N})")
+        out["tail"] = f"tile {pl['tail_tile_m']}x{pl['tail_tile_n']}, {pl['tail_tiles']} tiles, {where}"
+    return out
+
+
 def gemm_record(prob, fast, stream, sha, key, reps=20):
     """GEMM-only timing of one workload on one path, with its roofline."""
     import torch
@@ -531,6 +551,8 @@ def gemm_record(prob, fast, stream, sha, key, reps=20):
          "TFLOPS": flops / (each["mean"] / 1e6) / 1e12, "GB/s": nbytes / (each["mean"] / 1e6) / 1e9}
     r.update(roofline(flops, nbytes, each["mean"] / 1e6, peak_key, compute_bound, counters))
     r["algorithmic_flop"], r["algorithmic_bytes"] = flops, nbytes
+    if not prob.mx:
+        r["launch_plan"] = launch_plan(prob, fast)
     if counters:
         r["kernel_trace_avg_us"] = counters.get("avg_us_kernel_trace")
     return r
@@ -689,6 +711,9 @@ def main():
                     load_counters(f"gemm_{variant}_{tkey}", sha))
     roof["kernel"] = "gemm"
     roof["avg_launch_us"] = per_kernel["gemm"]["mean"]
+    if not mx:
+        # avg_launch_us spans the GEMM call: every launch of this plan
+        roof["launch_plan"] = launch_plan(prob, fast)
     roof["algorithmic_flop"] = flops
     roof["algorithmic_bytes"] = nbytes
     roof["flushed_avg_launch_us"] = flushed_gemm["mean"]
