@@ -136,8 +136,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
     const uint32_t qstep = uniform((int)(8 * NWAVES * K));
     // fragment addresses within a stage: row r of a subtile, logical chunk
     // 4h + pr at slot (4h + pr) ^ lds_swz(r); subtile and stage offsets are
-    // ds_read immediates (the swizzle depends on r mod 16 only).  Masked
-    // layout: set again per tile from the wave's first row and column there.
+    // ds_read immediates (the swizzle depends on r mod 16 only)
     uint32_t xa[NP], wa[NP];
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
