@@ -199,6 +199,46 @@ __device__ __forceinline__ bool decode_tile(int t, const GemmParams& p, const in
     return true;
 }
 
+// Masked layout, largest expert first: logical tile t -> (expert, m tile,
+// n tile) with the experts walked in decreasing order of their valid rows
+// (ties by index), each expert's tiles m-fastest as in decode_tile.  With one
+// workgroup per tile and tile costs that follow the counts, the hardware
+// dispatcher then starts the longest tiles first and fills the end of the
+// launch with the short ones (longest-processing-time-first list
+// scheduling).  Lane l < E takes expert l: its rank and its first m tile of
+// the walk come from one pass over the other experts' counts (broadcast from
+// their lanes), and the expert whose m-tile range holds t is found by a
+// ballot.  E <= 64.  Returns false for t past the walk.
+template <int BM, int BN>
+__device__ __forceinline__ bool decode_tile_masked_by_count(int t, const GemmParams& p, const int32_t* masked_m,
+                                                            TileCoord& tc) {
+    const int lane = threadIdx.x & 63;
+    int v = lane < p.E ? masked_m[lane] : 0;
+    v = v < 0 ? 0 : (v > p.max_m ? (int)p.max_m : v);
+    const int nmt = (v + BM - 1) / BM;
+    int base = 0;                       // m tiles of the experts walked before this one
+    for (int e = 0; e < p.E; ++e) {
+        const int ve = __builtin_amdgcn_readlane(v, e);
+        const int ne = __builtin_amdgcn_readlane(nmt, e);
+        if (ve > v || (ve == v && e < lane)) base += ne;
+    }
+    const int mt_t = t / p.n_tiles;
+    const uint64_t hit = __ballot(lane < p.E && nmt > 0 && mt_t >= base && mt_t < base + nmt);
+    if (hit == 0) return false;
+    const int e = (int)__builtin_ctzll(hit);
+    const int valid = __builtin_amdgcn_readlane(v, e);
+    const int nmt_e = __builtin_amdgcn_readlane(nmt, e);
+    const int base_e = __builtin_amdgcn_readlane(base, e);
+    const int local = t - base_e * p.n_tiles;
+    const int nt = local / nmt_e;
+    const int mt = local - nt * nmt_e;
+    tc.expert = e;
+    tc.row0 = (int64_t)e * p.max_m + (int64_t)mt * BM;
+    tc.row_end = (int64_t)e * p.max_m + valid;
+    tc.n0 = (int64_t)nt * BN;
+    return true;
+}
+
 // Calls f(integral_constant<int, 0>) ... f(integral_constant<int, S-1>) in order.
 template <int S, typename F>
 __device__ __forceinline__ void static_for(F&& f) {

@@ -55,9 +55,10 @@
 //     balances tiles of unequal cost), and each wave multiplies only its
 //     32-row subtiles that hold valid rows (DeepGEMM page, "分组 GEMM 的两种
 //     布局": the masked layout computes the valid positions only), so a
-//     tile's cost follows its expert's count in steps of 32 rows.  The tile
-//     body (kernels_exact_tile.inc) is instantiated once per number of valid
-//     subtiles.
+//     tile's cost follows its expert's count in steps of 32 rows; the tiles
+//     are walked largest expert first (gemm_common.h), so the dispatcher
+//     starts the longest ones first.  The tile body (kernels_exact_tile.inc)
+//     is instantiated once per number of valid subtiles.
 #pragma once
 
 #include "gemm_common.h"
@@ -164,7 +165,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
         if (t >= total_tiles) continue;
 
         TileCoord tc;
-        if (!decode_tile<MODE, BM, BN>(t, p, m_indices_, masked_m_, tc)) continue;
+        if constexpr (MODE == kMasked) {
+            // up to 64 experts: the largest first (the tiles' costs follow the counts)
+            if (p.E <= 64) {
+                if (!decode_tile_masked_by_count<BM, BN>(t, p, masked_m_, tc)) continue;
+            } else if (!decode_tile<MODE, BM, BN>(t, p, m_indices_, masked_m_, tc)) {
+                continue;
+            }
+        } else if (!decode_tile<MODE, BM, BN>(t, p, m_indices_, masked_m_, tc)) {
+            continue;
+        }
         const int64_t row0 = tc.row0, n0 = tc.n0;
         const int expert = tc.expert;
         const uint8_t* wq = wq_;
