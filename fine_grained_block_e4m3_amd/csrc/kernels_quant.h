@@ -61,16 +61,22 @@ __device__ __forceinline__ void quant_1x128_unit(const float* __restrict__ x, ui
         if (!PARTIAL || kb0 + 2 * q + half < KB) v[q] = load_stream(x + off + 256 * q);
         else v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    float sg[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int64_t kb = kb0 + 2 * q + half;
         const float amax = halfwave_max(abs_max4(v[q]));
         const float s = group_scale(amax, POW2);
-        if (!PARTIAL || kb < KB) {
+        sg[q] = s;
+        if (!PARTIAL || kb < KB)
             store_codes(xq + off + 256 * q, cvt_e4m3x4(v[q][0] / s, v[q][1] / s, v[q][2] / s, v[q][3] / s));
-            if ((lane & 31) == 0) sa[kb * M + m] = s;
-        }
     }
+    // the unit's 8 scales from lanes 0..7 in one store: lane i < 8 takes the
+    // scale of group kb0 + i, held by every lane of half i % 2 as sg[i / 2]
+    const int i8 = lane & 7;
+    const float mine = i8 < 2 ? sg[0] : i8 < 4 ? sg[1] : i8 < 6 ? sg[2] : sg[3];
+    const float sc = __shfl(mine, ((lane & 1) << 5) | i8);
+    if (lane < 8 && (!PARTIAL || kb0 + lane < KB)) sa[(kb0 + lane) * M + m] = sc;
 }
 
 template <bool POW2>
