@@ -171,6 +171,28 @@ def test_masked_tile_order(ue8m0, fast):
 
 
 @pytest.mark.parametrize("fast", PATHS)
+@pytest.mark.parametrize("E", [63, 64, 65, 90])
+def test_masked_many_experts(E, fast):
+    """Expert counts around 64 (the default path walks up to 64 experts
+    largest first, more in expert order), with equal counts among them (ties
+    walk in expert order) and empty experts: every valid row of every
+    expert is written once, with the right expert's weights, and nothing
+    else."""
+    rng = np.random.default_rng(E)
+    mm = rng.integers(0, 70, E).astype(np.int32)
+    mm[::7] = 33                                    # ties
+    mm[3::11] = 0                                   # empty experts
+    max_m, N, K = 64, 256, 256
+    wl = workloads.masked(E, max_m, N, K, seed=E, ue8m0=False, masked_m=mm)
+    xq, sa, wq, sb, flags = quant(wl)
+    ref, written = oracle.grouped_masked(xq, sa, wq, sb, mm, E, max_m, flags)
+    y = run_masked(xq, sa, wq, sb, mm, E, max_m, flags, fast)
+    row_expert = np.where(written, np.arange(E * max_m) // max_m, -1)
+    bound = grouped_bound(xq, sa, wq, sb, ref, row_expert, E, False) if fast else None
+    check_rows(y, ref, written, f"masked E={E}", bound)
+
+
+@pytest.mark.parametrize("fast", PATHS)
 def test_masked_rows_past_count_never_read(fast):
     """Rows past the count may hold NaN codes and NaN scales: the output must
     not change."""
