@@ -328,7 +328,13 @@ Plan plan_exact(int mode, int64_t M, int64_t N, int64_t K, bool qout, int cus, s
             // unsplit).
             const int64_t sx = decode_splits(M, N, K, cus, ws_bytes, 32 * kExactDecodeNW, 1);
             const bool fits = cdiv(K / 128, sx) <= exact_decode_kbmax(M);
-            if (fits && (sx > 1 || M <= 32)) {
+            if (sx == 1 && M <= 32 && cdiv(N, 32 * kExactDecodeNW) >= cus) {
+                // a whole round of column tiles, unsplit: X in chunks beats X
+                // resident (N 24576: M 1-32, K 1536 12.4-12.9 vs 13.1-13.6 us,
+                // M 32, K 3072 20.2 vs 21.4; with fewer tiles the resident X
+                // wins: 16x7168x2048 11.8 vs 12.7)
+                pl.main = kExactDecode;
+            } else if (fits && (sx > 1 || M <= 32)) {
                 pl.main = kExactDecodeX;
                 pl.k_splits = sx;
             } else if (sx == 1 && M > 32) {

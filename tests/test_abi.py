@@ -191,11 +191,14 @@ def test_plan_fills_whole_waves_on_the_prefill_shape(L):
     assert (e.exact, e.tile_m, e.tile_n, e.tiles, e.waves, e.grid) == (1, 256, 256, 256, 8, 256)
     assert (e.main_cols, e.tail_tile_m, e.tail_tile_n, e.tail_tiles) == (4096, 256, 192, 256)
     assert e.main_cols + 192 * (e.tail_tiles // 16) == 7168          # the two launches tile [0, N) once
-    d = _plan(0, 32, 24576, 1536)                   # exact decode kernel, X resident: 96 columns per workgroup
-    assert (d.exact, d.kernel, d.tile_n, d.tiles, d.grid) == (1, 4, 96, 256, 256)
+    d = _plan(0, 32, 24576, 1536)                   # exact decode kernel, X in chunks: 96 columns per workgroup
+    assert (d.exact, d.kernel, d.tile_n, d.tiles, d.grid, d.k_splits) == (1, 3, 96, 256, 256, 1)
+    d = _plan(0, 16, 7168, 2048)                    # fewer column tiles than CUs: X resident
+    assert (d.kernel, d.tiles, d.k_splits) == (4, 75, 1)
     d = _plan(0, 64, 24576, 1536)                   # unsplit, M > 32: the 64x96 tile
     assert (d.kernel, d.tile_m, d.tile_n) == (0, 64, 96)
-    assert _plan(0, 32, 24576, 3072).kernel == 4 and _plan(0, 32, 24576, 3200).kernel == 3   # 25 blocks: chunks
+    assert _plan(0, 32, 4096, 3072).kernel == 4 and _plan(0, 32, 4096, 3200).kernel == 3     # 25 blocks: chunks
+    assert _plan(0, 32, 24576, 3072).kernel == 3
     assert _plan(0, 65, 24576, 1536).kernel == 0
     assert _plan(0, 16, 24576, 1536, fp8.FLAG_FAST_ACCUM).kernel == 1
     assert _plan(0, 40, 24576, 1536, fp8.FLAG_FAST_ACCUM).kernel == 2
