@@ -120,8 +120,9 @@ fp8_status launch_tiles(Kernel kern, int threads, fp8k::GemmParams p, int group_
 template <int BM, int BN, int WM, int WN, int MODE, int PATH, int STAGES = 2, int GROUP_M = 4,
           bool QOUT = false>
 fp8_status launch_gemm(const fp8k::GemmParams& p, int cus, hipStream_t stream, int64_t m_hi = -1) {
+    // masked: one workgroup per possible tile (tile costs follow the counts)
     return launch_tiles<BM, BN, MODE>(fp8k::gemm_kernel<BM, BN, WM, WN, MODE, PATH, STAGES, QOUT>, 64 * WM * WN,
-                                      p, GROUP_M, cus, stream, m_hi);
+                                      p, GROUP_M, cus, stream, m_hi, MODE != fp8k::kMasked);
 }
 
 // The exact-partial kernel (the default path).
@@ -280,10 +281,12 @@ Plan plan_fast(int mode, int64_t M, int64_t N, int64_t K, bool mx, bool qout, in
             pl.tail = kFast128x64;
         }
     } else {
-        // Masked: 128-row tiles pad each expert's rows less than 256-row ones,
-        // and 256 columns per tile halve the re-reads of the expert's X rows
-        // (measured 94 -> 82 us on 16 experts x 256 rows, N 7168, K 2048).
-        pl.main = kFast128x256;
+        // Masked: 256-row tiles of 2x4 waves, one workgroup per possible tile,
+        // the waves skipping the 16-row subtiles past the expert's count and
+        // the tiles walked largest expert first (as on the default path);
+        // before: persistent 128x256 tiles (128-row tiles padded each
+        // expert's rows less than 256-row ones without the skip).
+        pl.main = kFast256x256;
     }
     return pl;
 }
@@ -457,7 +460,12 @@ fp8_status launch_fast(Inst i, const fp8k::GemmParams& p, int64_t splits, void* 
         }
     } else if constexpr (kBlock) {
         switch (i) {
-            case kFast128x256: return launch_gemm<128, 256, 2, 4, MODE, PATH, 3>(p, cus, stream, m_hi);
+            case kFast128x256:
+                if constexpr (MODE == fp8k::kContiguous) return launch_gemm<128, 256, 2, 4, MODE, PATH, 3>(p, cus, stream, m_hi);
+                else return FP8_ERR_UNSUPPORTED;
+            case kFast256x256:
+                if constexpr (MODE == fp8k::kMasked) return launch_gemm<256, 256, 2, 4, MODE, PATH, 2>(p, cus, stream, m_hi);
+                else return FP8_ERR_UNSUPPORTED;
             case kFast128x64:
                 if constexpr (MODE == fp8k::kContiguous) return launch_gemm<128, 64, 4, 2, MODE, PATH, 4>(p, cus, stream, m_hi);
                 else return FP8_ERR_UNSUPPORTED;
@@ -829,8 +837,8 @@ fp8_status fp8_gemm_plan(int32_t layout, int64_t M, int64_t N, int64_t K, uint32
         const int64_t rows = layout == 1 ? pl.main_rows : M;
         const int64_t cols = layout == 0 && pl.main_cols > 0 ? pl.main_cols : N;
         plan->tiles = cdiv(rows, a.bm) * cdiv(cols, a.bn);
-        // the exact masked launch has one workgroup per possible tile
-        const bool per_tile = layout == 2 && a.exact;
+        // the masked launches have one workgroup per possible tile
+        const bool per_tile = layout == 2;
         plan->grid = (int32_t)(plan->tiles < compute_units || per_tile ? plan->tiles : compute_units);
     }
     if (layout == 1 && pl.main_rows < M) {

@@ -148,6 +148,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     using ScaleT = std::conditional_t<kMx, int, float>;
     constexpr bool kSplitSb = kStreamW && TN <= 128 && !kScaledMfma;
     constexpr bool kPow2 = PATH == kPathFp8Pow2;
+    static_assert(MODE != kMasked || (!kStreamW && !kSplitSb), "masked: X rows streamed (the skip is per X subtile)");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole 16x16 subtiles");
     static_assert(BM % 64 == 0 && NSA < NWAVES, "activation scales: 64 rows per wave, one wave left for sB");
     static_assert(BN / 128 + 2 <= 64, "one scale load covers the tile's weight blocks");
@@ -170,7 +171,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
-    const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+    // Masked layout: wave w takes row w / WAVES_N and column w % WAVES_N, so
+    // that with WAVES_N = 4 the two waves sharing a SIMD (w mod 4) own
+    // different rows (the waves skip the subtiles past an expert's count).
+    const int wm = MODE == kMasked ? wave / WAVES_N : wave % WAVES_M;
+    const int wn = MODE == kMasked ? wave % WAVES_N : wave / WAVES_M;
     const int64_t K = p.K;
     const int KB = (int)(K / 128);
     const int64_t N = p.N;
@@ -274,7 +279,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     // G/8 consecutive logical tiles (a compact raster patch sharing operand
     // rows in that XCD's L2).
     const int G = gridDim.x;
-    const bool remap = (G & 7) == 0;
+    // (masked layout: one workgroup per possible tile, no remap)
+    const bool remap = MODE != kMasked && (G & 7) == 0;
     const int rounds = (total_tiles + G - 1) / G;
 
     for (int round = 0; round < rounds; ++round) {
@@ -285,7 +291,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 
         // ---------------- tile decode ----------------
         TileCoord tc;
-        if (!decode_tile<MODE, BM, BN>(t, p, m_indices_, masked_m_, tc)) continue;
+        if constexpr (MODE == kMasked) {
+            // up to 64 experts: the largest first (the tiles' costs follow the counts)
+            if (p.E <= 64) {
+                if (!decode_tile_masked_by_count<BM, BN>(t, p, masked_m_, tc)) continue;
+            } else if (!decode_tile<MODE, BM, BN>(t, p, m_indices_, masked_m_, tc)) {
+                continue;
+            }
+        } else if (!decode_tile<MODE, BM, BN>(t, p, m_indices_, masked_m_, tc)) {
+            continue;
+        }
         const int64_t row0 = tc.row0, row_end = tc.row_end, n0 = tc.n0;
         const int expert = tc.expert;
         const uint8_t* wq = wq_;
@@ -483,8 +498,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
 
         // The K loop, specialised on JB: with split scales, the streamed rows
         // 0 .. JB-1 take the first weight block's products (JB = 0 otherwise).
-        auto kloop = [&](auto jbc) {
+        // FV: the streamed rows (16-row X subtiles) of this wave that hold
+        // valid rows; the masked layout skips the multiplies of the others.
+        auto kloop = [&](auto jbc, auto fvc) {
         constexpr int JB = decltype(jbc)::value;
+        constexpr int FV = decltype(fvc)::value;
         // Prologue: blocks 0 .. STAGES-2 in full, all in flight together; once
         // block 0 has landed (for every wave), the first two window positions
         // of block STAGES-1; then the reads of block 0 that the pipeline
@@ -610,7 +628,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                         // operand A is the W fragment, B the X fragment
                         // operand format of A (W): 0 E4M3, 4 E2M1; B (X) is E4M3
                         constexpr int kFmtA = kW4 ? 4 : 0;
-                        if constexpr (kStreamW)
+                        if constexpr (r >= FV) {
+                            // a subtile past the valid rows (masked): nothing to multiply
+                        } else if constexpr (kStreamW)
                             accr(r, c) = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 fc, res[c], accr(r, c), kFmtA, 0, 0, ste, 0, rse[c]);
                         else
@@ -622,7 +642,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                     f32x4 cur[C];
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
-                        if constexpr (kStreamW)
+                        if constexpr (r >= FV) {
+                            // past the valid rows (masked): nothing to multiply
+                        } else if constexpr (kStreamW)
                             cur[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 fc, res[c], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
                         else
@@ -645,20 +667,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
                         if constexpr (r == 0) promote_p(R - 1, plast);
                         else promote_p(r - 1, pr[r - 1 < JB ? 0 : 1]);
                     } else {
-                        if constexpr (r == 0) promote(R - 1, rs_prev);
-                        else promote(r - 1, rs_cur);
+                        // (rows past the valid ones, masked: no partials to promote)
+                        if constexpr (r == 0) {
+                            if constexpr (R - 1 < FV) promote(R - 1, rs_prev);
+                        } else if constexpr (r - 1 < FV) {
+                            promote(r - 1, rs_cur);
+                        }
                     }
+                    if constexpr (r < FV) {
 #pragma unroll
-                    for (int c = 0; c < C; ++c) prev[c] = cur[c];
-                    st_prev = st_c;
+                        for (int c = 0; c < C; ++c) prev[c] = cur[c];
+                        st_prev = st_c;
+                    }
                     // each MFMA of this row preceded by the promotion FMAs of
                     // the subtile whose partials its result replaces (and the
                     // scale products)
-                    static_for<C>([&](auto qc) {
-                        constexpr int n = kSplitSb ? 4 : (decltype(qc)::value == 0 || kStreamW ? 5 : 4);
-                        __builtin_amdgcn_sched_group_barrier(0x002, n, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    });
+                    if constexpr (r < FV) {
+                        static_for<C>([&](auto qc) {
+                            constexpr int n = kSplitSb ? 4 : (decltype(qc)::value == 0 || kStreamW ? 5 : 4);
+                            __builtin_amdgcn_sched_group_barrier(0x002, n, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        });
+                    }
                 }
             });
             __builtin_amdgcn_sched_barrier(0);
@@ -683,15 +713,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
         });
         // drain: the last row's partials
         if constexpr (kSplitSb) promote_p(R - 1, plast);
-        else if constexpr (!kScaledMfma) promote(R - 1, rs_prev);
+        else if constexpr (!kScaledMfma && R - 1 < FV) promote(R - 1, rs_prev);
         };
         if constexpr (kSplitSb) {
             // one copy of the loop per boundary position (wave-uniform)
             static_for<FJ>([&](auto jc) {
-                if (jb == decltype(jc)::value + 1) kloop(std::integral_constant<int, decltype(jc)::value + 1>{});
+                if (jb == decltype(jc)::value + 1)
+                    kloop(std::integral_constant<int, decltype(jc)::value + 1>{}, std::integral_constant<int, R>{});
             });
         } else {
-            kloop(std::integral_constant<int, 0>{});
+            if constexpr (MODE == kMasked) {
+                const int fv = uniform(min(max(rows_valid - wm * TM + 15, 0) / 16, R));
+                static_for<R + 1>([&](auto fc) {
+                    if (fv == decltype(fc)::value) kloop(std::integral_constant<int, 0>{}, fc);
+                });
+            } else {
+                kloop(std::integral_constant<int, 0>{}, std::integral_constant<int, R>{});
+            }
         }
         // (the loads issued past the last block were discarded; they retire in
         // order before the next tile's loads, and the kernel's end waits for them)

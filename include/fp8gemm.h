@@ -305,9 +305,9 @@ fp8_status fp8_gemm_nt_mx_w4(const uint8_t* xq, const uint32_t* ea,
  *            fp8_gemm_nt_mx_w4) or FP8_PLAN_QOUT (fp8_gemm_nt_qout), dense only
  *   workspace_bytes  what an fp8_gemm_nt_ws call would pass
  * Masked plans count every expert's max_m rows (the kernel counts the valid
- * ones on the device), per expert.  The default path's masked launch has one
- * workgroup per possible tile (grid = tiles per expert, times E at the call);
- * every other tile-kernel launch is persistent (grid = min(tiles, CUs)).
+ * ones on the device), per expert.  A masked launch has one workgroup per
+ * possible tile (grid = tiles per expert, times E at the call); every other
+ * tile-kernel launch is persistent (grid = min(tiles, CUs)).
  */
 #define FP8_PLAN_MX 0x100u
 #define FP8_PLAN_QOUT 0x200u

@@ -233,16 +233,15 @@ def test_plan_exact_column_split_rule(L):
 
 
 def test_plan_masked_default_path_launches_one_workgroup_per_tile(L):
-    """Masked layout, default path: 256-row tiles of 8 waves, one workgroup
-    per possible tile of an expert (the kernel skips the subtiles past the
-    expert's count and the hardware dispatcher balances the unequal tiles);
-    the FP8-instruction path stays persistent."""
+    """Masked layout, both paths: 256-row tiles of 8 waves, one workgroup
+    per possible tile of an expert (the kernels skip the subtiles past the
+    expert's count and the hardware dispatcher balances the unequal tiles)."""
     e = _plan(2, 256, 7168, 2048)
     assert (e.exact, e.kernel, e.tile_m, e.tile_n, e.waves, e.tiles, e.grid) == (1, 0, 256, 256, 8, 28, 28)
     e = _plan(2, 512, 7168, 2048, cus=16)
     assert (e.tiles, e.grid) == (56, 56)
     f = _plan(2, 256, 7168, 2048, fp8.FLAG_FAST_ACCUM, cus=16)
-    assert f.exact == 0 and f.grid == min(f.tiles, 16)
+    assert (f.exact, f.tile_m, f.tile_n, f.tiles, f.grid) == (0, 256, 256, 28, 28)
 
 
 @pytest.mark.parametrize("fast", [0, fp8.FLAG_FAST_ACCUM])
