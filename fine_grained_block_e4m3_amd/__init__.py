@@ -65,7 +65,9 @@ class GemmPlan(ctypes.Structure):
                 ("tile_n", ctypes.c_int32), ("waves", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("tiles", ctypes.c_int64), ("main_rows", ctypes.c_int64), ("tail_tile_m", ctypes.c_int32),
                 ("tail_tile_n", ctypes.c_int32), ("tail_tiles", ctypes.c_int64), ("k_splits", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t), ("main_cols", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_size_t), ("main_cols", ctypes.c_int64),
+                ("paired", ctypes.c_int32), ("mid_tile_m", ctypes.c_int32), ("mid_tile_n", ctypes.c_int32),
+                ("mid_tiles", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -212,12 +212,15 @@ struct Plan {
                             // dense: the launch over columns [main_cols, N), if main_cols > 0
     int64_t k_splits;       // decode kernel
     int64_t main_cols = 0;  // dense, > 0: the main launch covers columns [0, main_cols)
+    bool paired = false;    // contiguous: main over pairs of 128-row blocks, then mid
+    Inst mid = kFast128x128; // and tail over the blocks left (gemm_common.h: pair schedule)
 };
 
 // The FP8-instruction paths.  Compute-bound shapes use 8 waves (2 per SIMD)
 // so that one wave's promotion FMAs run while the other wave's MFMAs occupy
 // the matrix core.
-Plan plan_fast(int mode, int64_t M, int64_t N, int64_t K, bool mx, bool qout, int cus, size_t ws_bytes) {
+Plan plan_fast(int mode, int64_t M, int64_t N, int64_t K, bool mx, bool qout, int cus, size_t ws_bytes,
+               bool pair) {
     Plan pl{kFast128x128, M, kFast128x128, 1};
     if (mode == fp8k::kDense) {
         if (qout) {
@@ -264,6 +267,13 @@ Plan plan_fast(int mode, int64_t M, int64_t N, int64_t K, bool mx, bool qout, in
         } else {
             pl.main = kFast128x128;
         }
+    } else if (mode == fp8k::kContiguous && pair && cdiv(M, 128) <= fp8k::kPairMaxBlocks &&
+               cdiv(M, 256) * cdiv(N, 256) >= cus) {
+        // the pair schedule, as on the exact path
+        pl.main = kFast256x256;
+        pl.mid = kFast128x256;
+        pl.tail = kFast128x64;
+        pl.paired = true;
     } else if (mode == fp8k::kContiguous) {
         // The M tile must equal the layout alignment (128): one expert per
         // tile.  When the last round of 128x256 tiles would leave over half of
@@ -314,7 +324,7 @@ int64_t exact_split_cols(int64_t M, int64_t N, int cus) {
     return cols;
 }
 
-Plan plan_exact(int mode, int64_t M, int64_t N, int64_t K, bool qout, int cus, size_t ws_bytes) {
+Plan plan_exact(int mode, int64_t M, int64_t N, int64_t K, bool qout, int cus, size_t ws_bytes, bool pair) {
     Plan pl{kExact128x128, M, kExact128x128, 1};
     if (mode == fp8k::kDense) {
         if (qout) {
@@ -355,6 +365,17 @@ Plan plan_exact(int mode, int64_t M, int64_t N, int64_t K, bool qout, int cus, s
         } else {
             pl.main = kExact128x128;
         }
+    } else if (mode == fp8k::kContiguous && pair && cdiv(M, 128) <= fp8k::kPairMaxBlocks &&
+               cdiv(M, 256) * cdiv(N, 256) >= cus) {
+        // 256-row tiles over pairs of one expert's 128-row blocks, then
+        // 128x256 and 128x64 tiles over the blocks left, the split found on
+        // the device (gemm_common.h).  8 experts x 8192 tokens, N 4096: 32
+        // pairs + 4 single blocks = 2 rounds of 256x256 tiles and one of
+        // 128x64 tiles, against 4 rounds of 128x256 tiles and one of 128x64.
+        pl.main = kExact256x256;
+        pl.mid = kExact128x256;
+        pl.tail = kExact128x64;
+        pl.paired = true;
     } else if (mode == fp8k::kContiguous) {
         // 128-row tiles (the layout alignment); the blocks past the last full
         // round of 128x256 tiles run as 128x64 tiles of 8 waves (32x32 each)
@@ -380,10 +401,11 @@ Plan plan_exact(int mode, int64_t M, int64_t N, int64_t K, bool qout, int cus, s
     return pl;
 }
 
+// pair: the contiguous pair schedule may be used (E <= kPairMaxExperts).
 Plan make_plan(int mode, int64_t M, int64_t N, int64_t K, uint32_t flags, bool mx, bool qout, int cus,
-               size_t ws_bytes) {
-    return (mx || (flags & FP8_FLAG_FAST_ACCUM)) ? plan_fast(mode, M, N, K, mx, qout, cus, ws_bytes)
-                                                 : plan_exact(mode, M, N, K, qout, cus, ws_bytes);
+               size_t ws_bytes, bool pair = true) {
+    return (mx || (flags & FP8_FLAG_FAST_ACCUM)) ? plan_fast(mode, M, N, K, mx, qout, cus, ws_bytes, pair)
+                                                 : plan_exact(mode, M, N, K, qout, cus, ws_bytes, pair);
 }
 
 // ---------------------------------------------------------------------------
@@ -463,9 +485,7 @@ fp8_status launch_fast(Inst i, const fp8k::GemmParams& p, int64_t splits, void* 
             case kFast128x256:
                 if constexpr (MODE == fp8k::kContiguous) return launch_gemm<128, 256, 2, 4, MODE, PATH, 3>(p, cus, stream, m_hi);
                 else return FP8_ERR_UNSUPPORTED;
-            case kFast256x256:
-                if constexpr (MODE == fp8k::kMasked) return launch_gemm<256, 256, 2, 4, MODE, PATH, 2>(p, cus, stream, m_hi);
-                else return FP8_ERR_UNSUPPORTED;
+            case kFast256x256: return launch_gemm<256, 256, 2, 4, MODE, PATH, 2>(p, cus, stream, m_hi);
             case kFast128x64:
                 if constexpr (MODE == fp8k::kContiguous) return launch_gemm<128, 64, 4, 2, MODE, PATH, 4>(p, cus, stream, m_hi);
                 else return FP8_ERR_UNSUPPORTED;
@@ -558,7 +578,7 @@ fp8_status launch_exact_inst(Inst i, const fp8k::GemmParams& p, int64_t splits, 
                 else return FP8_ERR_UNSUPPORTED;
             case kExact256x256:
                 if constexpr (MODE == fp8k::kMasked) return launch_exact<256, 256, 2, 4, MODE, POW2, 2>(p, cus, stream, m_hi);
-                else return FP8_ERR_UNSUPPORTED;
+                else return launch_exact<256, 256, 4, 2, MODE, POW2, 2>(p, cus, stream, m_hi);
             case kExact128x64:
                 if constexpr (MODE == fp8k::kContiguous) return launch_exact<128, 64, 4, 2, MODE, POW2, 4>(p, cus, stream, m_hi);
                 else return FP8_ERR_UNSUPPORTED;
@@ -584,6 +604,17 @@ fp8_status run_plan(const Plan& pl, bool exact, const fp8k::GemmParams& p, void*
         t.n_lo = pl.main_cols;
         return one(pl.tail, t, -1);
     }
+    if (MODE == fp8k::kContiguous && pl.paired) {
+        // the three launches of the pair schedule, each finding its share on
+        // the device
+        fp8k::GemmParams q = p;
+        q.pair_cus = cus;
+        for (Inst i : {pl.main, pl.mid, pl.tail}) {
+            const fp8_status st = one(i, q, -1);
+            if (st != FP8_OK) return st;
+        }
+        return FP8_OK;
+    }
     if (MODE == fp8k::kContiguous && pl.main_rows < p.M) {
         fp8_status st = one(pl.main, p, pl.main_rows);
         if (st != FP8_OK) return st;
@@ -601,7 +632,7 @@ fp8_status run_gemm(const fp8k::GemmParams& p, uint32_t flags, void* ws, size_t 
     int cus = 0;
     fp8_status st = current_device_cus(&cus);
     if (st != FP8_OK) return st;
-    const Plan pl = make_plan(MODE, p.M, p.N, p.K, flags, false, qout, cus, ws_bytes);
+    const Plan pl = make_plan(MODE, p.M, p.N, p.K, flags, false, qout, cus, ws_bytes, p.E <= fp8k::kPairMaxExperts);
     const bool exact = !(flags & FP8_FLAG_FAST_ACCUM);
     return (flags & FP8_FLAG_UE8M0) ? run_plan<MODE, fp8k::kPathFp8Pow2>(pl, exact, p, ws, cus, stream, qout)
                                     : run_plan<MODE, fp8k::kPathFp8>(pl, exact, p, ws, cus, stream, qout);
@@ -841,7 +872,17 @@ fp8_status fp8_gemm_plan(int32_t layout, int64_t M, int64_t N, int64_t K, uint32
         const bool per_tile = layout == 2;
         plan->grid = (int32_t)(plan->tiles < compute_units || per_tile ? plan->tiles : compute_units);
     }
-    if (layout == 1 && pl.main_rows < M) {
+    if (layout == 1 && pl.paired) {
+        // the shares of the three launches are found on the device: upper bounds
+        const InstInfo m = inst_info(pl.mid), t = inst_info(pl.tail);
+        plan->paired = 1;
+        plan->mid_tile_m = m.bm;
+        plan->mid_tile_n = m.bn;
+        plan->mid_tiles = cdiv(M, m.bm) * cdiv(N, m.bn);
+        plan->tail_tile_m = t.bm;
+        plan->tail_tile_n = t.bn;
+        plan->tail_tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
+    } else if (layout == 1 && pl.main_rows < M) {
         const InstInfo t = inst_info(pl.tail);
         plan->tail_tile_m = t.bm;
         plan->tail_tile_n = t.bn;

@@ -40,6 +40,9 @@ struct GemmParams {
     int32_t n_tiles;            // ceil(N/BN)
     int32_t group_m;            // raster group height in tiles
     float* part;                // decode split-K: FP32 partial sums [splits][M][N] (else null)
+    int32_t pair_cus;           // contiguous: > 0 when the tiles follow the pair schedule
+                                // built on the device (build_pair_sched), with this many
+                                // compute units in its full-round rule; 0: rows [m_lo, ...)
 };
 
 // Workgroup barrier without a memory fence.  Each wave has already waited on
@@ -237,6 +240,144 @@ __device__ __forceinline__ bool decode_tile_masked_by_count(int t, const GemmPar
     tc.row_end = (int64_t)e * p.max_m + valid;
     tc.n0 = (int64_t)nt * BN;
     return true;
+}
+
+// ---------------------------------------------------------------------------
+// Contiguous layout, 256-row tiles over pairs of 128-row blocks.  Each
+// 128-row aligned block belongs to one expert (DeepGEMM page, "分组 GEMM 的两
+// 种布局"), so two consecutive blocks of one expert share their weight tile and
+// can run as one 256-row tile.  Within each run of consecutive blocks of one
+// expert the blocks pair up in order; a run of odd length leaves its last
+// block single.  Three launches share the work, each taking whole rounds of
+// its tiles where a last partial round would leave over half of the compute
+// units idle and passing the rest on:
+//   1. 256x256 tiles over the pairs;
+//   2. 128x256 tiles over the blocks left (the singles, then the blocks of
+//      the pairs launch 1 passed on);
+//   3. 128x64 tiles over the blocks launch 2 passed on.
+// Nothing of this is known to the host: every workgroup builds the schedule
+// from the row indices into LDS when it starts.
+// ---------------------------------------------------------------------------
+constexpr int kPairMaxBlocks = 1024;        // 128-row blocks a paired schedule covers (M <= 131072)
+constexpr int kPairMaxExperts = 1 << 20;    // experts an entry can name
+constexpr int kPairEntries = kPairMaxBlocks + 2;
+
+// Expert of 128-row block b of mt: the first index in [0, E) among its rows,
+// in row order (the rule decode_tile follows); -1 for a block with none or
+// past the end.
+__device__ __forceinline__ int contig_block_expert(const GemmParams& p, const int32_t* m_indices, int b, int mt) {
+    if (b >= mt) return -1;
+    const int64_t r0 = (int64_t)b * 128, r1 = min(r0 + 128, p.M);
+    for (int64_t r = r0; r < r1; ++r) {
+        const int v = m_indices[r];
+        if (v >= 0 && v < p.E) return v;
+    }
+    return -1;
+}
+
+// Builds the pair schedule into ent (LDS, kPairEntries int32): entries
+// b | e << 11 (block b, expert e); the pairs' first blocks, in block order,
+// at ent[0 .. P), the singles, in block order, at ent[kPairMaxBlocks - 1],
+// ent[kPairMaxBlocks - 2], ...; P and S at ent[kPairMaxBlocks] and
+// ent[kPairMaxBlocks + 1].  One wave, all lanes active; the caller checks
+// that the blocks fit (mt <= kPairMaxBlocks, so P + S <= kPairMaxBlocks) and
+// that E <= kPairMaxExperts.  Lane l takes block 64c + l of chunk c: a block
+// starts a run when its expert differs from the one before; it starts a pair
+// when it lies an even number of blocks past its run's start and the next
+// block has its expert.
+__device__ __forceinline__ void build_pair_sched(const GemmParams& p, const int32_t* m_indices, int32_t* ent) {
+    const int lane = threadIdx.x & 63;
+    const int mt = (int)((p.M + 127) / 128);
+    const uint64_t below = (1ull << lane) - 1;
+    int np = 0, ns = 0, carry_e = -1, carry_rs = 0;
+    for (int c0 = 0; c0 < mt; c0 += 64) {
+        const int b = c0 + lane;
+        const int e = contig_block_expert(p, m_indices, b, mt);
+        const int en = contig_block_expert(p, m_indices, b + 1, mt);
+        int ep = __shfl_up(e, 1);
+        if (lane == 0) ep = carry_e;
+        // run starts at or below this lane (2 << 63 wraps to 0: all lanes)
+        const uint64_t starts = __ballot(e >= 0 && e != ep) & ((2ull << lane) - 1);
+        const int rs = starts ? c0 + 63 - __clzll((long long)starts) : carry_rs;
+        const bool even = ((b - rs) & 1) == 0;
+        const bool is_pair = e >= 0 && even && en == e;
+        const bool is_single = e >= 0 && even && en != e;
+        const uint64_t pm = __ballot(is_pair), sm = __ballot(is_single);
+        const int32_t v = b | (e << 11);
+        if (is_pair) ent[np + __popcll(pm & below)] = v;
+        if (is_single) ent[kPairMaxBlocks - 1 - (ns + __popcll(sm & below))] = v;
+        np += __popcll(pm);
+        ns += __popcll(sm);
+        carry_e = __shfl(e, 63);
+        carry_rs = __shfl(rs, 63);
+    }
+    if (lane == 0) {
+        ent[kPairMaxBlocks] = np;
+        ent[kPairMaxBlocks + 1] = ns;
+    }
+}
+
+// Of `units` (pairs or blocks) with nt column tiles each, the ones a launch
+// on cus compute units keeps: its whole rounds only, when the last partial
+// round would leave over half of the units idle; else all.
+__device__ __forceinline__ int units_kept(int units, int nt, int cus) {
+    const int tiles = units * nt, full = tiles / cus, last = tiles - full * cus;
+    return 2 * last < cus ? full * cus / nt : units;
+}
+
+// The share of one launch of the paired schedule (BM x BN: 256x256 launch 1,
+// 128x256 launch 2, 128x64 launch 3): its units (pairs or blocks), the first
+// of them in the list of blocks left after launch 1 (launch 3), and the
+// pairs launch 1 keeps.
+struct PairShare {
+    int units, first, pm, ns;
+};
+template <int BM, int BN>
+__device__ __forceinline__ PairShare pair_share(const GemmParams& p, const int32_t* ent) {
+    static_assert((BM == 256 && BN == 256) || (BM == 128 && (BN == 256 || BN == 64)), "paired launches");
+    const int np = uniform(ent[kPairMaxBlocks]), ns = uniform(ent[kPairMaxBlocks + 1]);
+    const int nt256 = (int)((p.N + 255) / 256);
+    PairShare sh{0, 0, units_kept(np, nt256, p.pair_cus), ns};
+    if constexpr (BM == 256) {
+        sh.units = sh.pm;
+    } else {
+        const int left = ns + 2 * (np - sh.pm);
+        const int mid = units_kept(left, nt256, p.pair_cus);
+        if constexpr (BN == 256) {
+            sh.units = mid;
+        } else {
+            sh.first = mid;
+            sh.units = left - mid;
+        }
+    }
+    return sh;
+}
+
+// Logical tile t of a paired launch -> its rows, columns and expert.  Block
+// u of the list of blocks left: the singles first, then the pairs' blocks.
+template <int BM, int BN>
+__device__ __forceinline__ void decode_tile_paired(int t, const GemmParams& p, const int32_t* ent,
+                                                   const PairShare& sh, TileCoord& tc) {
+    int u, nt;
+    raster(t, sh.units, p.n_tiles, p.group_m, u, nt);
+    int v, b;
+    if (BM == 256) {
+        v = uniform(ent[u]);
+        b = v & 2047;
+    } else {
+        u += sh.first;
+        if (u < sh.ns) {
+            v = uniform(ent[kPairMaxBlocks - 1 - u]);
+            b = v & 2047;
+        } else {
+            v = uniform(ent[sh.pm + ((u - sh.ns) >> 1)]);
+            b = (v & 2047) + ((u - sh.ns) & 1);
+        }
+    }
+    tc.expert = v >> 11;
+    tc.row0 = (int64_t)b * 128;
+    tc.row_end = p.M;
+    tc.n0 = (int64_t)nt * BN;
 }
 
 // Calls f(integral_constant<int, 0>) ... f(integral_constant<int, S-1>) in order.

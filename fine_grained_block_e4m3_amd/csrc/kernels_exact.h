@@ -122,7 +122,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
     const int h = lane >> 5;            // K half of the block this lane covers
     const int r32 = lane & 31;          // row of a 32-row subtile
 
-    const int total_tiles = count_tiles<MODE, BM>(p, masked_m_);
+    int total_tiles = count_tiles<MODE, BM>(p, masked_m_);
+    // Contiguous layout on the pair schedule: wave 0 builds it in LDS before
+    // the first tile (the planner keeps the blocks within its capacity).
+    __shared__ int32_t pair_ent[MODE == kContiguous ? kPairEntries : 1];
+    PairShare pair_sh{};
+    if constexpr (MODE == kContiguous) {
+        if (p.pair_cus > 0) {
+            if ((p.M + 127) / 128 > kPairMaxBlocks || p.E > kPairMaxExperts) return;
+            if (wave == 0) build_pair_sched(p, m_indices_, pair_ent);
+            __syncthreads();
+            pair_sh = pair_share<BM, BN>(p, pair_ent);
+            total_tiles = pair_sh.units * p.n_tiles;
+        }
+    }
 
     // ---- per-lane constants ----
     // DMA piece of 8-row group f: lane l writes slot l%8 of row 8f + l/8,
@@ -172,6 +185,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_exact_kernel(
             } else if (!decode_tile<MODE, BM, BN>(t, p, m_indices_, masked_m_, tc)) {
                 continue;
             }
+        } else if (MODE == kContiguous && p.pair_cus > 0) {
+            decode_tile_paired<BM, BN>(t, p, pair_ent, pair_sh, tc);
         } else if (!decode_tile<MODE, BM, BN>(t, p, m_indices_, masked_m_, tc)) {
             continue;
         }

@@ -181,7 +181,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
     const int64_t N = p.N;
     const int g = lane >> 4;             // K group of this lane: bytes [32g, 32g+32)
 
-    const int total_tiles = count_tiles<MODE, BM>(p, masked_m_);
+    int total_tiles = count_tiles<MODE, BM>(p, masked_m_);
+    // Contiguous layout on the pair schedule: wave 0 builds it in LDS before
+    // the first tile (the planner keeps the blocks within its capacity).
+    __shared__ int32_t pair_ent[MODE == kContiguous ? kPairEntries : 1];
+    PairShare pair_sh{};
+    if constexpr (MODE == kContiguous) {
+        if (p.pair_cus > 0) {
+            if ((p.M + 127) / 128 > kPairMaxBlocks || p.E > kPairMaxExperts) return;
+            if (wave == 0) build_pair_sched(p, m_indices_, pair_ent);
+            __syncthreads();
+            pair_sh = pair_share<BM, BN>(p, pair_ent);
+            total_tiles = pair_sh.units * p.n_tiles;
+        }
+    }
 
     // ---- per-lane constants, shared by every tile ----
     // DMA: a wave load fills 1 KB = 8 rows R0..R0+7 of 8-row group grp = R0/8;
@@ -298,6 +311,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(
             } else if (!decode_tile<MODE, BM, BN>(t, p, m_indices_, masked_m_, tc)) {
                 continue;
             }
+        } else if (MODE == kContiguous && p.pair_cus > 0) {
+            decode_tile_paired<BM, BN>(t, p, pair_ent, pair_sh, tc);
         } else if (!decode_tile<MODE, BM, BN>(t, p, m_indices_, masked_m_, tc)) {
             continue;
         }

@@ -327,6 +327,15 @@ typedef struct {
     int32_t k_splits;       /* decode kernel: workgroups along K per tile */
     size_t workspace_bytes; /* workspace the split uses */
     int64_t main_cols;      /* columns [0, main_cols) in the main launch (dense); else N */
+    int32_t paired;         /* contiguous, 1: three launches share the 128-row blocks, split on
+                               the device from m_indices: the main launch takes 256-row tiles
+                               over pairs of consecutive blocks of one expert, the middle launch
+                               (mid_tile_m x mid_tile_n) and the tail launch the blocks left,
+                               each in whole rounds of its tiles where a last partial round
+                               would leave over half of the compute units idle; tiles,
+                               mid_tiles and tail_tiles are then upper bounds, and main_rows M */
+    int32_t mid_tile_m, mid_tile_n;
+    int64_t mid_tiles;
 } fp8_gemm_plan_t;
 fp8_status fp8_gemm_plan(int32_t layout, int64_t M, int64_t N, int64_t K,
                          uint32_t flags, int32_t compute_units,

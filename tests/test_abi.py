@@ -253,6 +253,10 @@ def test_plan_contiguous_launches_cover_every_row_once(L, M, fast):
     exactly once, at whole 128-row blocks, and the first holds whole rounds."""
     N, cus = 4096, 256
     p = _plan(1, M, N, 7168, fast)
+    if p.paired:
+        # the pair schedule (test_plan_contiguous_pair_schedule)
+        assert M > 128
+        return
     assert p.tile_m == 128 and p.tile_n == 256
     assert p.main_rows % 128 == 0 and 0 < p.main_rows <= M
     assert p.tiles == ((p.main_rows + 127) // 128) * (N // 256)
@@ -264,6 +268,31 @@ def test_plan_contiguous_launches_cover_every_row_once(L, M, fast):
         assert 2 * (blocks % cus) < cus
     else:
         assert p.tail_tile_m == 0
+
+
+@pytest.mark.parametrize("fast", [0, fp8.FLAG_FAST_ACCUM])
+@pytest.mark.parametrize("M", [8704, 33 * 128, 1024 * 128])
+def test_plan_contiguous_pair_schedule(L, M, fast):
+    """Contiguous layout, at least a round of 256x256 tiles if every 128-row
+    block were paired: three launches, 256x256 tiles over the pairs of one
+    expert's blocks, then 128x256 and 128x64 tiles over the blocks left,
+    their shares found on the device (upper bounds here)."""
+    N, cus = 4096, 256
+    p = _plan(1, M, N, 7168, fast)
+    assert p.paired == 1 and p.exact == (0 if fast else 1)
+    assert (p.tile_m, p.tile_n, p.waves, p.main_rows) == (256, 256, 8, M)
+    assert p.tiles == (M + 255) // 256 * (N // 256) and p.grid == min(p.tiles, cus)
+    assert (p.mid_tile_m, p.mid_tile_n, p.mid_tiles) == (128, 256, (M + 127) // 128 * (N // 256))
+    assert (p.tail_tile_m, p.tail_tile_n, p.tail_tiles) == (128, 64, (M + 127) // 128 * (N // 64))
+
+
+@pytest.mark.parametrize("M,N,flags", [(1024 * 128 + 1, 4096, 0), (4096 - 256, 4096, 0), (8704, 256, 0),
+                                       (1024 * 128 + 1, 4096, fp8.FLAG_FAST_ACCUM)])
+def test_plan_contiguous_unpaired(L, M, N, flags):
+    """No pair schedule past 1024 blocks of 128 rows (its LDS table) or
+    below a round of 256x256 tiles."""
+    p = _plan(1, M, N, 7168, flags)
+    assert p.paired == 0 and p.tile_m == 128 and (p.mid_tile_m, p.mid_tiles) == (0, 0)
 
 
 def test_plan_decode_split_and_workspace(L):

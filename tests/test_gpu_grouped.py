@@ -122,6 +122,57 @@ def test_contiguous_dirichlet_and_bad_indices(fast):
     check_rows(y, ref, written, "contiguous dirichlet", bound)
 
 
+def block_layout(block_experts, seed):
+    """Row indices of 128-row blocks: block i belongs to expert
+    block_experts[i] (-1: a block of padding rows only); the last block of
+    each run of one expert keeps a random number of its rows (at least one)
+    and pads the rest with -1, as the layout pads an expert's rows up to the
+    alignment."""
+    rng = np.random.default_rng(seed)
+    be = np.asarray(block_experts)
+    idx = np.repeat(be, 128).astype(np.int32)
+    for i, e in enumerate(be):
+        if e >= 0 and (i + 1 == len(be) or be[i + 1] != e):
+            idx[i * 128 + int(rng.integers(1, 129)):(i + 1) * 128] = -1
+    return idx
+
+
+# Block layouts for the pair schedule (256x256 tiles over pairs of one
+# expert's consecutive blocks, then 128x256 and 128x64 tiles over the blocks
+# left; N = 4096, 256 CUs: 16 pairs or blocks per round).
+PAIR_LAYOUTS = {
+    # 17 pairs = 272 tiles of 256x256: the first launch keeps one round and
+    # passes the 17th pair on; 16 singles + its 2 blocks = 288 tiles of
+    # 128x256: the second keeps one round, the third takes 2 blocks
+    "passed_on": [0] * 34 + list(range(1, 17)),
+    # runs across the 64-block chunks in which the schedule is built: block
+    # 64 is the second block of a pair
+    "chunk_carry": [0] + [1] * 70 + [2] * 29,
+    # runs broken by padding blocks, one expert in two runs, runs of odd length
+    "breaks": [0] * 3 + [-1] + [0] * 2 + [1] * 5 + [2] + [1] * 9 + [-1, -1] + [3] * 11 + [4],
+    # no two consecutive blocks of one expert: every block single
+    "all_single": [0, 1] * 20,
+}
+
+
+@pytest.mark.parametrize("fast", PATHS)
+@pytest.mark.parametrize("layout", list(PAIR_LAYOUTS))
+def test_contiguous_pair_schedule(layout, fast):
+    blocks = PAIR_LAYOUTS[layout]
+    idx = block_layout(blocks, seed=len(blocks))
+    E, N, K = max(blocks) + 1, 4096, 128
+    plan = fp8.gemm_plan("contiguous", len(idx), N, K, fast_accum=fast)
+    assert plan["paired"] == 1
+    wl = workloads.dense(len(idx), N * E, K, seed=23)
+    xq, sa = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, idx, E)
+    assert np.array_equal(written, idx >= 0)
+    y = run_contiguous(xq, sa, wq, sb, idx, E, 0, fast)
+    bound = None if not fast else grouped_bound(xq, sa, wq, sb, ref, idx, E, False)
+    check_rows(y, ref, written, f"contiguous pairs {layout}", bound)
+
+
 @pytest.mark.parametrize("fast", PATHS)
 def test_contiguous_ue8m0(fast):
     wl = workloads.contiguous(E=3, tokens=400, N=256, K=256, seed=42)
