@@ -522,7 +522,15 @@ def launch_plan(prob, fast):
     kind = {0: "tile", 1: "decode", 2: "decode_x", 3: "exact_decode", 4: "exact_decode_x"}[pl["kernel"]]
     out = {"launches": 1, "main": f"{kind} {pl['tile_m']}x{pl['tile_n']}, {pl['tiles']} tiles, grid {pl['grid']}"
                                    + (" per expert" if wl.kind == "masked" else "")}
-    if pl["tail_tiles"]:
+    if pl["paired"]:
+        # contiguous pair schedule: the launches split the blocks on the device
+        out["launches"] = 3
+        out["main"] = (f"tile {pl['tile_m']}x{pl['tile_n']} over pairs of one expert's 128-row blocks, "
+                       f"at most {pl['tiles']} tiles, grid {pl['grid']}")
+        out["mid"] = f"tile {pl['mid_tile_m']}x{pl['mid_tile_n']} over the blocks left, at most {pl['mid_tiles']} tiles"
+        out["tail"] = (f"tile {pl['tail_tile_m']}x{pl['tail_tile_n']} over the blocks the middle launch leaves, "
+                       f"at most {pl['tail_tiles']} tiles")
+    elif pl["tail_tiles"]:
         out["launches"] = 2
         where = (f"rows [{pl['main_rows']}, {prob.M})" if wl.kind == "contiguous"
                  else f"columns [{pl['main_cols']}, {wl.N})")
