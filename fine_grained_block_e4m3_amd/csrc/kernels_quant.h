@@ -9,7 +9,9 @@
 // (1 B/element) plus one FP32 scale per group.  Loads are 16 B per lane and
 // fully coalesced; the group maximum is reduced with cross-lane shuffles.
 // The codes are the E4M3 rounding of the correctly rounded FP32 quotient
-// x / s (IEEE division, not a multiply by a rounded reciprocal).
+// x / s, obtained from the product with the rounded reciprocal where that
+// provably gives the same code and from an IEEE division elsewhere
+// (cvt_e4m3x4_quot).
 #pragma once
 
 #include "device_common.h"
@@ -41,6 +43,35 @@ __device__ __forceinline__ float abs_max4(f32x4 v) {
     return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 }
 
+// E4M3 codes of the correctly rounded quotients v[i] / s, with r the
+// correctly rounded 1 / s.  The product v[i] * r carries two roundings of
+// relative error at most 2^-24 each, so it lies within 2 units in the last
+// place of the exact quotient and within 2.5 of the correctly rounded one
+// (5 units of the lower binade where the two straddle a power of two).  The
+// conversion to E4M3 (round to nearest even, saturating) is monotone in the
+// magnitude: when the magnitudes 8 units below and 8 above the product take
+// the same code, every value between them does, the correctly rounded
+// quotient included, and the product's code (its sign is the quotient's) is
+// the answer.  Otherwise -- a product within 8 units of a rounding boundary,
+// about 2e-5 of random inputs -- the four quotients are divided.  With a
+// power-of-two scale the product is the quotient itself.
+template <bool POW2>
+__device__ __forceinline__ uint32_t cvt_e4m3x4_quot(f32x4 v, float s, float r) {
+    const float q0 = v[0] * r, q1 = v[1] * r, q2 = v[2] * r, q3 = v[3] * r;
+    if constexpr (POW2) {
+        return cvt_e4m3x4(q0, q1, q2, q3);
+    } else {
+        const uint32_t a0 = __float_as_uint(q0) & 0x7FFFFFFFu, a1 = __float_as_uint(q1) & 0x7FFFFFFFu;
+        const uint32_t a2 = __float_as_uint(q2) & 0x7FFFFFFFu, a3 = __float_as_uint(q3) & 0x7FFFFFFFu;
+        auto below = [](uint32_t a) { return __uint_as_float(a > 8u ? a - 8u : 0u); };
+        auto above = [](uint32_t a) { return __uint_as_float(a + 8u); };
+        const uint32_t lo = cvt_e4m3x4(below(a0), below(a1), below(a2), below(a3));
+        const uint32_t hi = cvt_e4m3x4(above(a0), above(a1), above(a2), above(a3));
+        if (lo == hi) return cvt_e4m3x4(q0, q1, q2, q3);
+        return cvt_e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+    }
+}
+
 // 1x128 activation quantizer.  A wave takes one row and up to 8 consecutive
 // groups of it (4 KB of FP32): lane l loads 16 bytes of each of 4 row
 // segments of 256 values, so each wave load covers 1 KB contiguous and holds
@@ -68,8 +99,7 @@ __device__ __forceinline__ void quant_1x128_unit(const float* __restrict__ x, ui
         const float amax = halfwave_max(abs_max4(v[q]));
         const float s = group_scale(amax, POW2);
         sg[q] = s;
-        if (!PARTIAL || kb < KB)
-            store_codes(xq + off + 256 * q, cvt_e4m3x4(v[q][0] / s, v[q][1] / s, v[q][2] / s, v[q][3] / s));
+        if (!PARTIAL || kb < KB) store_codes(xq + off + 256 * q, cvt_e4m3x4_quot<POW2>(v[q], s, 1.0f / s));
     }
     // the unit's 8 scales from lanes 0..7 in one store: lane i < 8 takes the
     // scale of group kb0 + i, held by every lane of half i % 2 as sg[i / 2]
@@ -127,10 +157,10 @@ __device__ __forceinline__ void quant_128x128_block(const float* __restrict__ w,
     __syncthreads();
     amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
     const float s = group_scale(amax, POW2);
+    const float r = 1.0f / s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        if (!PARTIAL || n0 + r0 + 8 * i < N)
-            store_codes(wq + off + rstep * i, cvt_e4m3x4(v[i][0] / s, v[i][1] / s, v[i][2] / s, v[i][3] / s));
+        if (!PARTIAL || n0 + r0 + 8 * i < N) store_codes(wq + off + rstep * i, cvt_e4m3x4_quot<POW2>(v[i], s, r));
     }
     if (threadIdx.x == 0) sb[nb * KB + kb] = s;
 }

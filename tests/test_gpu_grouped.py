@@ -156,21 +156,25 @@ PAIR_LAYOUTS = {
 
 
 @pytest.mark.parametrize("fast", PATHS)
-@pytest.mark.parametrize("layout", list(PAIR_LAYOUTS))
-def test_contiguous_pair_schedule(layout, fast):
+@pytest.mark.parametrize("layout,flags", [(name, 0) for name in PAIR_LAYOUTS]
+                         + [("passed_on", oracle.FLAG_UE8M0), ("breaks", oracle.FLAG_UE8M0)])
+def test_contiguous_pair_schedule(layout, flags, fast):
+    """The pair schedule on layouts that exercise each of its branches, with
+    FP32 scales and, on two layouts, power-of-two scales (the UE8M0 kernel
+    instances)."""
     blocks = PAIR_LAYOUTS[layout]
     idx = block_layout(blocks, seed=len(blocks))
-    E, N, K = max(blocks) + 1, 4096, 128
-    plan = fp8.gemm_plan("contiguous", len(idx), N, K, fast_accum=fast)
+    E, N, K = max(blocks) + 1, 4096, 256 if flags else 128
+    plan = fp8.gemm_plan("contiguous", len(idx), N, K, ue8m0=bool(flags), fast_accum=fast)
     assert plan["paired"] == 1
     wl = workloads.dense(len(idx), N * E, K, seed=23)
-    xq, sa = oracle.quant_1x128(wl.x)
-    wq, sb = oracle.quant_128x128(wl.w)
-    ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, idx, E)
+    xq, sa = oracle.quant_1x128(wl.x, flags)
+    wq, sb = oracle.quant_128x128(wl.w, flags)
+    ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, idx, E, flags)
     assert np.array_equal(written, idx >= 0)
-    y = run_contiguous(xq, sa, wq, sb, idx, E, 0, fast)
-    bound = None if not fast else grouped_bound(xq, sa, wq, sb, ref, idx, E, False)
-    check_rows(y, ref, written, f"contiguous pairs {layout}", bound)
+    y = run_contiguous(xq, sa, wq, sb, idx, E, flags, fast)
+    bound = None if not fast else grouped_bound(xq, sa, wq, sb, ref, idx, E, bool(flags))
+    check_rows(y, ref, written, f"contiguous pairs {layout} flags={flags}", bound)
 
 
 @pytest.mark.parametrize("fast", PATHS)

@@ -85,6 +85,56 @@ def test_hardware_encoder_matches_oracle():
     assert len(bad) == 0, [(x[tuple(b)], xq[tuple(b)], xq_ref[tuple(b)]) for b in bad[:8]]
 
 
+def _near_boundaries(c):
+    """(values, group maximum) for a scale factor c in [1, 2): the group's
+    maximum is c*448, so its scale s = fl32(max/448) is not a power of two,
+    and the values put the quotient x / s on every E4M3 rounding boundary
+    (the midpoint between two neighbouring codes) below 440 and within 10
+    FP32 units either side of it, both signs."""
+    amax = np.float32(448 * c)
+    s = np.float32(amax / np.float32(448))
+    dec = oracle.e4m3_decode(np.arange(0x7F)).astype(np.float64)
+    mid = (dec[:-1] + dec[1:]) / 2
+    base = (mid[mid < 440] * np.float64(s)).astype(np.float32).view(np.int32)
+    v = np.concatenate([(base + k).view(np.float32) for k in range(-10, 11)])
+    return np.concatenate([v, -v]), amax, s
+
+
+def test_quotients_on_rounding_boundaries():
+    """Codes where x / s lies on or next to an E4M3 rounding boundary, with
+    scales that are not powers of two: the quantizers take the product with
+    the reciprocal only where it provably rounds like the correctly rounded
+    quotient, and divide elsewhere; both must match the oracle's division
+    bit for bit."""
+    rng = np.random.default_rng(9)
+    rows, blocks = [], []
+    for c in rng.uniform(1.0, 2.0, 8):
+        v, amax, s = _near_boundaries(c)
+        rng.shuffle(v)
+        per = 127
+        n = (v.size + per - 1) // per
+        r = np.empty((n, 128), np.float32)
+        r[:, 0] = amax
+        r[:, 1:] = np.resize(v, n * per).reshape(n, per)
+        rows.append(r)
+        b = np.resize(v, 128 * 128).reshape(128, 128).astype(np.float32)
+        b[0, 0] = amax
+        blocks.append(b)
+    x = np.concatenate(rows)
+    xq_ref, sa_ref = oracle.quant_1x128(x)
+    xq, sa = _q1(x, 0)
+    assert np.array_equal(sa.view(np.uint32), sa_ref.view(np.uint32))
+    bad = np.argwhere(xq != xq_ref)
+    assert len(bad) == 0, [(x[tuple(b)], xq[tuple(b)], xq_ref[tuple(b)]) for b in bad[:8]]
+    w = np.concatenate(blocks)                     # (8*128, 128): one block per factor
+    wq_ref, sb_ref = oracle.quant_128x128(w)
+    assert len(np.unique(sb_ref)) == len(blocks)
+    wq, sb = _q2(w, 0)
+    assert np.array_equal(sb.view(np.uint32), sb_ref.view(np.uint32))
+    bad = np.argwhere(wq != wq_ref)
+    assert len(bad) == 0, [(w[tuple(b)], wq[tuple(b)], wq_ref[tuple(b)]) for b in bad[:8]]
+
+
 def test_zero_and_negative_zero_groups():
     x = np.zeros((4, 256), np.float32)
     x[1] = -0.0
