@@ -152,7 +152,10 @@ PAIR_LAYOUTS = {
     "breaks": [0] * 3 + [-1] + [0] * 2 + [1] * 5 + [2] + [1] * 9 + [-1, -1] + [3] * 11 + [4],
     # no two consecutive blocks of one expert: every block single
     "all_single": [0, 1] * 20,
+    # M not a multiple of 128: the last pair's second block holds 50 rows
+    "ragged_end": [0] * 33 + [1] * 4,
 }
+PAIR_ROWS = {"ragged_end": 36 * 128 + 50}
 
 
 @pytest.mark.parametrize("fast", PATHS)
@@ -163,7 +166,7 @@ def test_contiguous_pair_schedule(layout, flags, fast):
     FP32 scales and, on two layouts, power-of-two scales (the UE8M0 kernel
     instances)."""
     blocks = PAIR_LAYOUTS[layout]
-    idx = block_layout(blocks, seed=len(blocks))
+    idx = block_layout(blocks, seed=len(blocks))[:PAIR_ROWS.get(layout)]
     E, N, K = max(blocks) + 1, 4096, 256 if flags else 128
     plan = fp8.gemm_plan("contiguous", len(idx), N, K, ue8m0=bool(flags), fast_accum=fast)
     assert plan["paired"] == 1
