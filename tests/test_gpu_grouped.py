@@ -154,6 +154,10 @@ PAIR_LAYOUTS = {
     "all_single": [0, 1] * 20,
     # M not a multiple of 128: the last pair's second block holds 50 rows
     "ragged_end": [0] * 33 + [1] * 4,
+    # 3 pairs = 48 tiles: the first launch keeps none; 11 singles + 6 pair
+    # blocks = 272 tiles of 128x256: the second keeps 16 blocks, the third
+    # takes the last pair block; padding-only blocks in no launch
+    "mid_and_tail": [0, 0, 1, 1, 2, 2] + list(range(3, 14)) + [-1] * 14,
 }
 PAIR_ROWS = {"ragged_end": 36 * 128 + 50}
 
