@@ -185,6 +185,51 @@ def test_contiguous_pair_schedule(layout, flags, fast):
 
 
 @pytest.mark.parametrize("fast", PATHS)
+def test_contiguous_pair_schedule_graph_replays(fast):
+    """The three launches of the pair schedule captured in a graph: every
+    replay, with eager work and synchronizations between replays, equals the
+    eager result bit for bit; and since every workgroup rebuilds the schedule
+    from the row indices, a replay after new indices are written into the
+    same buffer follows them."""
+    blocks = PAIR_LAYOUTS["passed_on"]
+    idx = block_layout(blocks, seed=5)
+    E, N, K = max(blocks) + 1, 4096, 128
+    wl = workloads.dense(len(idx), N * E, K, seed=29)
+    xq, sa = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    ops = (dev(xq), dev(sa), dev(wq.reshape(E, N, K)), dev(sb.reshape(E, N // 128, K // 128)))
+    d_idx = dev(idx)
+    y = sentinel_like((len(idx), N))
+    s = torch.cuda.Stream()
+    run = lambda: fp8.grouped_gemm_contiguous(*ops, d_idx, fast_accum=fast, out=y)
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.synchronize()
+    eager = bf16_bits(y)
+    g = torch.cuda.CUDAGraph()
+    say(f"contiguous pairs: capture fast_accum={fast}")
+    with torch.cuda.graph(g, stream=s):
+        run()
+    for i in range(3):
+        y.view(torch.int16).fill_(SENTINEL)
+        torch.cuda.synchronize()
+        g.replay()
+        fp8.grouped_gemm_contiguous(*ops, d_idx, fast_accum=not fast)   # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(y), eager), f"replay {i}"
+    # other row indices in the same buffer (runs broken by padding blocks)
+    idx2 = np.resize(block_layout(PAIR_LAYOUTS["breaks"], seed=6), len(idx)).astype(np.int32)
+    d_idx.copy_(dev(idx2))
+    y.view(torch.int16).fill_(SENTINEL)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, idx2, E)
+    bound = None if not fast else grouped_bound(xq, sa, wq, sb, ref, np.where(written, idx2, -1), E, False)
+    check_rows(bf16_bits(y), ref, written, "contiguous pairs, replay with new indices", bound)
+
+
+@pytest.mark.parametrize("fast", PATHS)
 def test_contiguous_ue8m0(fast):
     wl = workloads.contiguous(E=3, tokens=400, N=256, K=256, seed=42)
     xq, sa = oracle.quant_1x128(wl.x, oracle.FLAG_UE8M0)
