@@ -184,6 +184,40 @@ def test_contiguous_pair_schedule(layout, flags, fast):
     check_rows(y, ref, written, f"contiguous pairs {layout} flags={flags}", bound)
 
 
+def random_block_experts(rng, E):
+    """A random block layout of 32 to 120 blocks: runs of 1 to 9 blocks of a
+    random expert (an expert may recur, a neighbour may repeat it, so runs
+    merge), with padding-only blocks (-1) between some runs."""
+    out = []
+    while len(out) < 32 or (len(out) < 120 and rng.random() < 0.9):
+        if out and rng.random() < 0.15:
+            out += [-1] * int(rng.integers(1, 3))
+        out += [int(rng.integers(0, E))] * int(rng.integers(1, 10))
+    return out[:120]
+
+
+@pytest.mark.parametrize("fast", PATHS)
+def test_contiguous_pair_schedule_random_layouts(fast):
+    """Twelve random block layouts through the pair schedule (each paired
+    by the planner, N = 4096), every row against the oracle."""
+    rng = np.random.default_rng(2024)
+    N, K, E = 4096, 128, 6
+    wl = workloads.dense(120 * 128, N * E, K, seed=31)
+    xq_all, sa_all = oracle.quant_1x128(wl.x)
+    wq, sb = oracle.quant_128x128(wl.w)
+    for case in range(12):
+        blocks = random_block_experts(rng, E)
+        idx = block_layout(blocks, seed=case)
+        M = len(idx)
+        assert fp8.gemm_plan("contiguous", M, N, K, fast_accum=fast)["paired"] == 1
+        xq, sa = xq_all[:M], np.ascontiguousarray(sa_all[:, :M])
+        say(f"case {case}: {len(blocks)} blocks {blocks}")
+        ref, written = oracle.grouped_contiguous(xq, sa, wq, sb, idx, E)
+        y = run_contiguous(xq, sa, wq, sb, idx, E, 0, fast)
+        bound = None if not fast else grouped_bound(xq, sa, wq, sb, ref, np.where(written, idx, -1), E, False)
+        check_rows(y, ref, written, f"contiguous pairs, random layout {case}", bound)
+
+
 @pytest.mark.parametrize("fast", PATHS)
 def test_contiguous_pair_schedule_graph_replays(fast):
     """The three launches of the pair schedule captured in a graph: every
